@@ -1,0 +1,39 @@
+"""CPU oracle for paged KV-cache attention.  TEST INFRASTRUCTURE ONLY.
+
+Plain, slow, obviously-correct numpy float64 implementations of what the HIP
+library computes.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package; the product path
+(``paged_kv_cache_79_amd``) never does, and this package imports nothing from
+it.  Every function cites the passage of the pages it follows; pages are named
+by title:
+
+  * "2.1 PagedAttention" (the vLLM tutorial chapter; Vietnamese and Chinese
+    editions carry the same sections) -- the block table, translation,
+    sharing and copy-on-write;
+  * "Inside vLLM, part 2" (gpuhub) -- chunked prefill;
+  * "vAttention 完全拆解" (pinghaoyang) -- the KV size model and the rule that
+    the valid length bounds what a kernel may see.
+
+Parity status of each function is listed in ``PINS`` below.
+"""
+from .paged import (  # noqa: F401
+    BF16, F32, widen, translate, slot_of, gather_kv, kv_head_of, attend, decode,
+    prefill_chunk, kv_write, copy_blocks, partition_partials, lse_merge, kv_size_bytes,
+    blocks_needed, tail_waste,
+)
+
+# function -> what pins it (see tests/test_oracle_pins.py)
+PINS = {
+    "translate/slot_of": "worked example of the 2.1 PagedAttention chapter, section 3 "
+                         "(tests/golden/worked_example_bs4.txt)",
+    "gather_kv": "worked example + round trip against kv_write + physical-id permutation",
+    "attend/decode": "torch scaled_dot_product_attention (fp64, CPU, enable_gqa) on identity "
+                     "tables; closed forms (ctx=1, q=0, equal keys); one-hot probe",
+    "prefill_chunk": "SDPA with is_causal on a chunk covering the whole context; "
+                     "every row equals decode on the truncated context",
+    "kv_write": "worked example slots; whole-pool bit comparison; negative slots skipped",
+    "copy_blocks": "snapshot semantics on hand-built pairs; CoW divergence scenario",
+    "partition_partials/lse_merge": "merge over any partition equals the unsplit result",
+    "kv_size_bytes": "Yi-34B TP=2 sizing printed on the vAttention page",
+    "blocks_needed/tail_waste": "waste bound of the 2.1 chapter, section 4",
+}
