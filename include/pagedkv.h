@@ -1,0 +1,175 @@
+/*
+ * pagedkv.h -- C ABI of libpagedkv: PagedAttention over a block-table-indexed
+ * KV cache on AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow the "2.1 PagedAttention" chapter (vLLM tutorial):
+ * a request's KV cache is cut into blocks of block_size tokens, its logical
+ * blocks are mapped to physical blocks by a block table (section 3), and the
+ * attention kernel reads every logical position at physical block number x
+ * block stride + offset inside the block (section 5).  Blocks can be shared
+ * by several tables and copied before a write (copy-on-write, section 6).
+ * Chunked prefill follows "Inside vLLM, part 2" (chunked prefill section).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer argument is a DEVICE pointer owned by the caller; the
+ *    library never allocates, frees, or synchronises.  Work is enqueued on
+ *    the given stream in call order; the caller orders a cache write before
+ *    the attention that reads it (stream order), and keeps context_lens
+ *    consistent with what has been written.
+ *  - KV pools: k_pool and v_pool are each
+ *        [num_blocks][num_kv_heads][block_size][head_dim]
+ *    contiguous, so kv_head_stride = block_size*head_dim elements and
+ *    kv_block_stride = num_kv_heads*block_size*head_dim elements.
+ *  - q, k/v pools, new K/V and outputs share one element type (pkv_dtype).
+ *    bf16 is stored as the upper 16 bits of an IEEE float32.
+ *  - Query head hq reads KV head hq / (num_q_heads / num_kv_heads).
+ *  - block_tables is int32 [rows][max_blocks_per_seq], row-major; entries
+ *    beyond ceil(context_len / block_size) are never read.
+ *  - A context length counts every token visible to the step's queries,
+ *    including the ones written in this step.
+ *  - Supported: head_dim in {64, 128}; block_size in {4, 8, 16, 32} with
+ *    block_size * head_dim * element size >= 1024 bytes;
+ *    num_q_heads / num_kv_heads in 1..8.
+ *  - Host-checkable arguments are validated before anything is enqueued; a
+ *    non-zero status means nothing was launched.  Device-resident contents
+ *    (block ids, slots, lengths) are not validated; out-of-range block ids
+ *    and slots are skipped by the kernels (never dereferenced), which keeps
+ *    a bad table from faulting the GPU but yields unspecified output.
+ *  - No entry point blocks or aborts; errors are status codes.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pkv_dtype {
+    PKV_F32 = 0,
+    PKV_BF16 = 1
+} pkv_dtype;
+
+typedef enum pkv_status {
+    PKV_OK = 0,
+    PKV_ERR_NULL = 1,          /* a required pointer is NULL */
+    PKV_ERR_SHAPE = 2,         /* a size is negative/zero where it must be positive, or inconsistent */
+    PKV_ERR_DTYPE = 3,         /* unknown pkv_dtype */
+    PKV_ERR_UNSUPPORTED = 4,   /* valid but not implemented (head_dim, block_size, group size, dtype) */
+    PKV_ERR_WORKSPACE = 5,     /* workspace missing or smaller than required */
+    PKV_ERR_LAUNCH = 6         /* the HIP runtime refused a launch */
+} pkv_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* pkv_status_string(pkv_status status);
+
+/*
+ * paged_kv_write -- slot-mapped write of the current step's new K/V.
+ * ("2.1 PagedAttention", section 3: each new token fills the next free slot of
+ * its request's current block, the scheduler naming the slot.)
+ *
+ *   k_new, v_new   [num_tokens][num_kv_heads][head_dim]
+ *   slot_mapping   int64 [num_tokens]; slot = physical_block*block_size + offset.
+ *                  slot < 0 marks padding and writes nothing.  Slots of one call
+ *                  must be distinct (two tokens on one slot: unspecified winner).
+ * For every token i with a valid slot, K_pool[slot/bs][h][slot%bs][:] = k_new[i][h][:]
+ * for all heads h (bit copy), and likewise for V.  num_tokens == 0 is a no-op.
+ */
+pkv_status paged_kv_write(pkv_dtype dtype, void* k_pool, void* v_pool, int32_t num_blocks,
+                          int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
+                          const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                          int32_t num_tokens, hipStream_t stream);
+
+/*
+ * copy_blocks -- block copies for copy-on-write ("2.1 PagedAttention", section 6:
+ * before writing into a shared block, the block is copied to a private block and
+ * the writer's table is re-pointed to the copy; re-pointing is the caller's).
+ *
+ *   block_mapping  int64 [num_pairs][2] = (src, dst) physical block ids.
+ * Each pair copies the whole block (every KV head and slot) of K and of V.  All
+ * destinations must be distinct and none may be a source of the same call.
+ * num_pairs == 0 is a no-op.
+ */
+pkv_status copy_blocks(pkv_dtype dtype, void* k_pool, void* v_pool, int32_t num_blocks,
+                       int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
+                       const int64_t* block_mapping, int32_t num_pairs, hipStream_t stream);
+
+/*
+ * Decode attention.  Each query head of sequence s attends to the
+ * context_lens[s] tokens of the sequence, read through its block table row
+ * ("2.1 PagedAttention", sections 3 and 5):
+ *     out[s][hq][:] = sum_t softmax_t(scale * q[s][hq] . K_t) * V_t
+ * with K_t, V_t at (block_tables[s][t / bs], kv head, t % bs).  The context is
+ * cut into partitions of partition_tokens tokens whose partial softmax states
+ * are merged by log-sum-exp; the result does not depend on the partition size
+ * beyond float rounding.  context_len 0 gives a zero row.
+ *
+ * paged_attention_decode_partition_tokens: partition size the library picks
+ * when partition_tokens == 0 (a multiple of 64).
+ * paged_attention_decode_workspace_bytes: bytes of device workspace the call
+ * needs for that partition size (0 when every sequence fits one partition).
+ */
+int32_t paged_attention_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
+                                                int32_t max_context_len);
+
+size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                              int32_t num_kv_heads, int32_t head_dim,
+                                              int32_t max_context_len, int32_t partition_tokens);
+
+/*
+ *   out           [num_seqs][num_q_heads][head_dim]   (written)
+ *   q             [num_seqs][num_q_heads][head_dim]
+ *   block_tables  int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens  int32 [num_seqs], each in [0, max_blocks_per_seq*block_size]
+ *   max_context_len  host-known upper bound of context_lens (sizes the grid;
+ *                    a larger context is truncated to it)
+ *   partition_tokens 0 = library choice, else a positive multiple of 64
+ *   workspace     device scratch of at least paged_attention_decode_workspace_bytes
+ *                 (may be NULL when that is 0); its contents need no initialisation
+ *                 and are garbage afterwards; calls sharing a workspace must not
+ *                 overlap in time.
+ */
+pkv_status paged_attention_decode(pkv_dtype dtype, void* out, const void* q,
+                                  const void* k_pool, const void* v_pool, int32_t num_blocks,
+                                  int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t num_seqs,
+                                  int32_t max_context_len, int32_t num_q_heads, float scale,
+                                  int32_t partition_tokens, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * paged_attention_prefill_chunk -- causal attention of prefill query chunks over
+ * their paged contexts ("Inside vLLM, part 2", chunked prefill: a long prompt is
+ * processed a bounded number of tokens per step, each chunk attending to the
+ * already-cached prefix and to itself).
+ *
+ *   out, q        [total_q][num_q_heads][head_dim], total_q = cu_q_lens[num_chunks]
+ *   cu_q_lens     int32 [num_chunks + 1], cu_q_lens[0] = 0, non-decreasing
+ *   max_q_len     host-known max of cu_q_lens[c+1] - cu_q_lens[c]
+ *   block_tables  int32 [num_chunks][max_blocks_per_seq]
+ *   context_lens  int32 [num_chunks], including the chunk; chunk c's queries are the
+ *                 last n_q positions, query i at p = ctx - n_q + i, seeing keys t <= p.
+ *                 n_q must not exceed ctx.
+ * The chunk's own K/V must already be in the cache (paged_kv_write earlier on the
+ * stream).  bf16 only (PKV_ERR_UNSUPPORTED for fp32); runs on the matrix cores.
+ */
+pkv_status paged_attention_prefill_chunk(pkv_dtype dtype, void* out, const void* q,
+                                         const int32_t* cu_q_lens, int32_t num_chunks,
+                                         int32_t max_q_len, const void* k_pool,
+                                         const void* v_pool, int32_t num_blocks,
+                                         int32_t num_kv_heads, int32_t block_size,
+                                         int32_t head_dim, const int32_t* block_tables,
+                                         int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                         int32_t max_context_len, int32_t num_q_heads, float scale,
+                                         hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,227 @@
+// C ABI of libpagedkv: argument validation, geometry, partition choice, launches.
+// Every entry point validates what the host can see before enqueuing anything,
+// never allocates, and never synchronises.
+#include <math.h>
+
+#include "pagedkv.h"
+#include "pkv_internal.h"
+
+using namespace pkv;
+
+namespace {
+
+int elem_bytes(pkv_dtype dt) { return dt == PKV_BF16 ? 2 : 4; }
+
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int ilog2(int x) {
+    int r = 0;
+    while ((1 << r) < x) ++r;
+    return r;
+}
+
+// Shared checks of the pool geometry.  A (block, kv head) run must span at least
+// one wave-wide 16-byte load (64 lanes x 16 B = 1 KiB) so that every such load
+// stays inside one block.
+pkv_status check_geom(pkv_dtype dt, int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
+                      int32_t head_dim, PoolGeom* g) {
+    if (dt != PKV_F32 && dt != PKV_BF16) return PKV_ERR_DTYPE;
+    if (num_blocks <= 0 || num_kv_heads <= 0 || block_size <= 0 || head_dim <= 0)
+        return PKV_ERR_SHAPE;
+    if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
+    if (!pow2(block_size) || block_size < 4 || block_size > 32) return PKV_ERR_UNSUPPORTED;
+    const int eb = elem_bytes(dt);
+    if (block_size * head_dim * eb < 1024) return PKV_ERR_UNSUPPORTED;
+    // slots are int64, block offsets int64; a single (block, head) run is < 2^31 bytes
+    g->row_bytes = head_dim * eb;
+    g->head_stride_bytes = block_size * head_dim * eb;
+    g->block_stride_bytes = (int64_t)num_kv_heads * g->head_stride_bytes;
+    g->num_blocks = num_blocks;
+    g->num_kv_heads = num_kv_heads;
+    g->block_size = block_size;
+    g->log2_bs = ilog2(block_size);
+    return PKV_OK;
+}
+
+pkv_status launch_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH; }
+
+int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Partition size: aim for about 8K (sequence, kv head, partition) work items so
+// that 256 CUs stay busy through the ragged end, with at least 256 tokens per
+// partition so the merge traffic stays a few percent of the KV bytes.
+int32_t pick_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len) {
+    const int64_t work = (int64_t)num_seqs * num_kv_heads * (int64_t)max_context_len;
+    const int64_t per = work / 8192;
+    int32_t pt = 256;
+    while (pt < per && pt < 8192) pt *= 2;
+    return pt;
+}
+
+int32_t num_partitions(int32_t max_context_len, int32_t pt) {
+    return max_context_len <= 0 ? 1 : (int32_t)cdiv64(max_context_len, pt);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_string(pkv_status s) {
+    switch (s) {
+        case PKV_OK: return "PKV_OK";
+        case PKV_ERR_NULL: return "PKV_ERR_NULL: a required pointer is NULL";
+        case PKV_ERR_SHAPE: return "PKV_ERR_SHAPE: invalid or inconsistent size";
+        case PKV_ERR_DTYPE: return "PKV_ERR_DTYPE: unknown element type";
+        case PKV_ERR_UNSUPPORTED: return "PKV_ERR_UNSUPPORTED: configuration not implemented";
+        case PKV_ERR_WORKSPACE: return "PKV_ERR_WORKSPACE: workspace missing or too small";
+        case PKV_ERR_LAUNCH: return "PKV_ERR_LAUNCH: kernel launch failed";
+    }
+    return "PKV_ERR_UNKNOWN";
+}
+
+pkv_status paged_kv_write(pkv_dtype dtype, void* k_pool, void* v_pool, int32_t num_blocks,
+                          int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
+                          const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                          int32_t num_tokens, hipStream_t stream) {
+    PoolGeom g;
+    const pkv_status st = check_geom(dtype, num_blocks, num_kv_heads, block_size, head_dim, &g);
+    if (st != PKV_OK) return st;
+    if (num_tokens < 0) return PKV_ERR_SHAPE;
+    if (num_tokens == 0) return PKV_OK;
+    if (!k_pool || !v_pool || !k_new || !v_new || !slot_mapping) return PKV_ERR_NULL;
+    WriteArgs a;
+    a.k_pool = static_cast<char*>(k_pool);
+    a.v_pool = static_cast<char*>(v_pool);
+    a.k_new = static_cast<const char*>(k_new);
+    a.v_new = static_cast<const char*>(v_new);
+    a.slot_mapping = slot_mapping;
+    a.num_tokens = num_tokens;
+    a.g = g;
+    return launch_status(launch_kv_write(a, stream));
+}
+
+pkv_status copy_blocks(pkv_dtype dtype, void* k_pool, void* v_pool, int32_t num_blocks,
+                       int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
+                       const int64_t* block_mapping, int32_t num_pairs, hipStream_t stream) {
+    PoolGeom g;
+    const pkv_status st = check_geom(dtype, num_blocks, num_kv_heads, block_size, head_dim, &g);
+    if (st != PKV_OK) return st;
+    if (num_pairs < 0) return PKV_ERR_SHAPE;
+    if (num_pairs == 0) return PKV_OK;
+    if (!k_pool || !v_pool || !block_mapping) return PKV_ERR_NULL;
+    CopyArgs a;
+    a.k_pool = static_cast<char*>(k_pool);
+    a.v_pool = static_cast<char*>(v_pool);
+    a.block_mapping = block_mapping;
+    a.num_pairs = num_pairs;
+    a.g = g;
+    return launch_status(launch_copy_blocks(a, stream));
+}
+
+int32_t paged_attention_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
+                                                int32_t max_context_len) {
+    return pick_partition(num_seqs, num_kv_heads, max_context_len);
+}
+
+size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                              int32_t num_kv_heads, int32_t head_dim,
+                                              int32_t max_context_len, int32_t partition_tokens) {
+    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0) return 0;
+    const int32_t pt = partition_tokens > 0 ? partition_tokens
+                                            : pick_partition(num_seqs, num_kv_heads, max_context_len);
+    const int32_t np = num_partitions(max_context_len, pt);
+    if (np <= 1) return 0;
+    return (size_t)num_seqs * num_q_heads * np * (size_t)(head_dim + 2) * sizeof(float);
+}
+
+pkv_status paged_attention_decode(pkv_dtype dtype, void* out, const void* q, const void* k_pool,
+                                  const void* v_pool, int32_t num_blocks, int32_t num_kv_heads,
+                                  int32_t block_size, int32_t head_dim,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t num_seqs,
+                                  int32_t max_context_len, int32_t num_q_heads, float scale,
+                                  int32_t partition_tokens, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+    PoolGeom g;
+    const pkv_status st = check_geom(dtype, num_blocks, num_kv_heads, block_size, head_dim, &g);
+    if (st != PKV_OK) return st;
+    if (num_seqs < 0 || max_context_len < 0 || max_blocks_per_seq <= 0 || num_q_heads <= 0)
+        return PKV_ERR_SHAPE;
+    if (num_q_heads % num_kv_heads) return PKV_ERR_SHAPE;
+    const int group = num_q_heads / num_kv_heads;
+    if (group > 8) return PKV_ERR_UNSUPPORTED;
+    if (partition_tokens < 0 || (partition_tokens % 64) != 0) return PKV_ERR_SHAPE;
+    if (!isfinite(scale)) return PKV_ERR_SHAPE;
+    if (num_seqs == 0) return PKV_OK;
+    if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PKV_ERR_NULL;
+    if ((int64_t)num_seqs * num_kv_heads > 65535) return PKV_ERR_UNSUPPORTED;  // grid.y
+
+    const int32_t pt = partition_tokens > 0 ? partition_tokens
+                                            : pick_partition(num_seqs, num_kv_heads, max_context_len);
+    const int32_t np = num_partitions(max_context_len, pt);
+    const size_t need = paged_attention_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads,
+                                                               head_dim, max_context_len, pt);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
+
+    DecodeArgs a;
+    a.out = out;
+    a.q = q;
+    a.k_pool = static_cast<const char*>(k_pool);
+    a.v_pool = static_cast<const char*>(v_pool);
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.part_o = static_cast<float*>(workspace);
+    a.part_ml = need > 0 ? static_cast<float*>(workspace) +
+                               (size_t)num_seqs * num_q_heads * np * head_dim
+                         : nullptr;
+    a.g = g;
+    a.num_q_heads = num_q_heads;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.max_context_len = max_context_len;
+    a.part_tokens = pt;
+    a.num_parts = np;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    return launch_status(launch_decode(a, dtype == PKV_BF16, head_dim, group, num_seqs, stream));
+}
+
+pkv_status paged_attention_prefill_chunk(pkv_dtype dtype, void* out, const void* q,
+                                         const int32_t* cu_q_lens, int32_t num_chunks,
+                                         int32_t max_q_len, const void* k_pool, const void* v_pool,
+                                         int32_t num_blocks, int32_t num_kv_heads,
+                                         int32_t block_size, int32_t head_dim,
+                                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                         const int32_t* context_lens, int32_t max_context_len,
+                                         int32_t num_q_heads, float scale, hipStream_t stream) {
+    PoolGeom g;
+    const pkv_status st = check_geom(dtype, num_blocks, num_kv_heads, block_size, head_dim, &g);
+    if (st != PKV_OK) return st;
+    if (dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+    if (num_chunks < 0 || max_q_len < 0 || max_context_len < 0 || max_blocks_per_seq <= 0 ||
+        num_q_heads <= 0)
+        return PKV_ERR_SHAPE;
+    if (num_q_heads % num_kv_heads) return PKV_ERR_SHAPE;
+    const int group = num_q_heads / num_kv_heads;
+    if (group > 8) return PKV_ERR_UNSUPPORTED;
+    if (!isfinite(scale)) return PKV_ERR_SHAPE;
+    if (num_chunks == 0 || max_q_len == 0) return PKV_OK;
+    if (!out || !q || !cu_q_lens || !k_pool || !v_pool || !block_tables || !context_lens)
+        return PKV_ERR_NULL;
+    if (num_chunks > 65535) return PKV_ERR_UNSUPPORTED;  // grid.z
+
+    PrefillArgs a;
+    a.out = out;
+    a.q = q;
+    a.cu_q_lens = cu_q_lens;
+    a.k_pool = static_cast<const char*>(k_pool);
+    a.v_pool = static_cast<const char*>(v_pool);
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.g = g;
+    a.num_q_heads = num_q_heads;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.max_context_len = max_context_len;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    return launch_status(launch_prefill(a, head_dim, group, num_chunks, max_q_len, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,78 @@
+// Internal launch interface between the C ABI (pkv_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+struct PoolGeom {
+    int64_t block_stride_bytes;  // num_kv_heads * block_size * head_dim * elem
+    int32_t head_stride_bytes;   // block_size * head_dim * elem
+    int32_t row_bytes;           // head_dim * elem
+    int32_t num_blocks;
+    int32_t num_kv_heads;
+    int32_t block_size;
+    int32_t log2_bs;
+};
+
+struct WriteArgs {
+    char* k_pool;
+    char* v_pool;
+    const char* k_new;
+    const char* v_new;
+    const int64_t* slot_mapping;
+    int32_t num_tokens;
+    PoolGeom g;
+};
+
+struct CopyArgs {
+    char* k_pool;
+    char* v_pool;
+    const int64_t* block_mapping;
+    int32_t num_pairs;
+    PoolGeom g;
+};
+
+struct DecodeArgs {
+    void* out;
+    const void* q;
+    const char* k_pool;
+    const char* v_pool;
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    float* part_o;       // [S][Hq][num_parts][D]   unnormalised partial outputs
+    float* part_ml;      // [S][Hq][num_parts][2]   (running max in log2 units, sum)
+    PoolGeom g;
+    int32_t num_q_heads;
+    int32_t max_blocks_per_seq;
+    int32_t max_context_len;
+    int32_t part_tokens;
+    int32_t num_parts;
+    float scale_log2;    // scale * log2(e)
+};
+
+struct PrefillArgs {
+    void* out;
+    const void* q;
+    const int32_t* cu_q_lens;
+    const char* k_pool;
+    const char* v_pool;
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    PoolGeom g;
+    int32_t num_q_heads;
+    int32_t max_blocks_per_seq;
+    int32_t max_context_len;
+    float scale_log2;
+};
+
+hipError_t launch_kv_write(const WriteArgs& a, hipStream_t st);
+hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t st);
+// is_bf16 selects the element type; group = num_q_heads / num_kv_heads (1..8).
+hipError_t launch_decode(const DecodeArgs& a, bool is_bf16, int head_dim, int group,
+                         int num_seqs, hipStream_t st);
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int group, int num_chunks,
+                          int max_q_len, hipStream_t st);
+
+}  // namespace pkv

@@ -1,0 +1,195 @@
+"""Decode attention on the GPU against the oracle, plus paging invariants that must
+hold bit for bit on the device."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_79_amd as pkv
+import workloads as W
+from oracle import paged as O
+from tests.gpu_helpers import TOL, DecodeRun, dev, host, oracle_after_write, oracle_decode, rownorm_err
+
+pytestmark = pytest.mark.gpu
+
+
+def check(b, partition_tokens=0, label=""):
+    print(f"decode {b.name} S={b.num_seqs} Hq={b.num_q_heads} Hkv={b.num_kv_heads} D={b.head_dim} "
+          f"bs={b.block_size} max_ctx={b.max_context_len} part={partition_tokens} {label}", flush=True)
+    r = DecodeRun(b)
+    r.write()
+    got = O.widen(r.decode(partition_tokens), b.dtype)
+    k, v = oracle_after_write(b)
+    want = oracle_decode(b, k, v)
+    err = rownorm_err(got, want)
+    assert err <= TOL[b.dtype], f"row-normalised error {err:.3e}"
+    return got
+
+
+def batch(dtype, d, bs, hq, hkv, ctx, seed=7):
+    return W.build_decode_batch(name=f"{dtype}_d{d}_bs{bs}_g{hq // hkv}", dtype=dtype,
+                                context_lens=ctx, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                                block_size=bs, seed=seed)
+
+
+def test_tiny_fp32_worked_example():
+    check(W.tiny())
+    check(W.tiny(), partition_tokens=64)
+
+
+@pytest.mark.parametrize("part", [0, 64, 128, 512, 8192])
+def test_gqa_small_partitions(part):
+    check(W.gqa(num_seqs=8), partition_tokens=part)
+
+
+@pytest.mark.parametrize("g", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_group_sizes(g):
+    rng = np.random.Generator(np.random.PCG64(100 + g))
+    ctx = rng.integers(1, 700, size=4, endpoint=True)
+    check(batch("bf16", 128, 16, 2 * g, 2, ctx, seed=g), partition_tokens=256)
+
+
+@pytest.mark.parametrize("dtype,d,bs", [("bf16", 64, 16), ("bf16", 64, 32), ("bf16", 64, 8),
+                                        ("bf16", 128, 4), ("bf16", 128, 8), ("bf16", 128, 32),
+                                        ("f32", 64, 4), ("f32", 128, 4), ("f32", 128, 16),
+                                        ("f32", 64, 32)])
+def test_shapes(dtype, d, bs):
+    ctx = [1, 63, 64, 65, 130, 257, 600]
+    check(batch(dtype, d, bs, 8, 2, ctx), partition_tokens=128)
+    check(batch(dtype, d, bs, 8, 2, ctx), partition_tokens=0)
+
+
+def test_edge_lengths():
+    # 0 (empty -> zero rows), 1, exact tile and block multiples, ragged tails
+    ctx = [0, 1, 2, 15, 16, 17, 63, 64, 65, 127, 128, 129, 1023, 1024, 1025]
+    b = W.build_decode_batch(name="edges", dtype="bf16", context_lens=ctx, num_q_heads=8,
+                             num_kv_heads=2, head_dim=128, block_size=16, seed=3)
+    for part in (0, 64, 256):
+        r = DecodeRun(b)
+        slots = b.slot_mapping.copy()
+        r.write(slot_mapping=slots)
+        got = O.widen(r.decode(part), "bf16")
+        k, v = O.kv_write(b.k_pool, b.k_new, slots), O.kv_write(b.v_pool, b.v_new, slots)
+        want = oracle_decode(b, k, v)
+        assert np.array_equal(got[0], np.zeros_like(got[0]))           # empty context
+        assert rownorm_err(got[1:], want[1:]) <= TOL["bf16"]
+
+
+def test_long_small():
+    check(W.long_context(num_seqs=2, ctx_range=(3000, 9000)), partition_tokens=0)
+    check(W.long_context(num_seqs=2, ctx_range=(3000, 9000)), partition_tokens=1024)
+
+
+def test_prefix_cow_flow():
+    """Copy-on-write then write then decode; the copied (re-pointed) tables give the same
+    bits as the shared ones, since the copies hold the same data."""
+    p = W.prefix_cow(num_seqs=24)
+    b = p.batch
+    r = DecodeRun(b)
+    pkv.copy_blocks(r.k, r.v, dev(p.block_mapping))
+    r.write()
+    got_private = r.decode(0)
+    k, v = O.kv_write(O.copy_blocks(b.k_pool, p.block_mapping), b.k_new, b.slot_mapping), \
+        O.kv_write(O.copy_blocks(b.v_pool, p.block_mapping), b.v_new, b.slot_mapping)
+    want = oracle_decode(b, k, v)
+    assert rownorm_err(O.widen(got_private, "bf16"), want) <= TOL["bf16"]
+    got_shared = r.decode(0, tables=dev(p.shared_tables))
+    assert np.array_equal(got_private, got_shared)
+
+
+def test_permutation_of_physical_ids_is_bit_identical():
+    b = W.gqa(num_seqs=6)
+    r = DecodeRun(b)
+    r.write()
+    base = r.decode(256)
+    k, v = host(r.k), host(r.v)
+    perm = np.random.Generator(np.random.PCG64(5)).permutation(b.num_blocks)
+    k2, v2 = np.empty_like(k), np.empty_like(v)
+    k2[perm], v2[perm] = k, v
+    t2 = np.where(b.block_tables >= 0, perm[np.maximum(b.block_tables, 0)], -1).astype(np.int32)
+    r2 = DecodeRun(b, tables=t2)
+    r2.k, r2.v = dev(k2), dev(v2)
+    assert np.array_equal(r2.decode(256), base)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_one_hot_probe_exact(dtype):
+    """q = 64 e0; the target token's K[0] = +64, every other valid token's -64.  The
+    other weights underflow to exactly 0, so the output is the target's V row, bit for bit,
+    for every target position (exact block-table translation through the kernel)."""
+    d, bs, n = 128, 16, 100
+    b = W.build_decode_batch(name="probe", dtype=dtype, context_lens=[n], num_q_heads=1,
+                             num_kv_heads=1, head_dim=d, block_size=bs, seed=9)
+    k_new = O.kv_write(b.k_pool, b.k_new, b.slot_mapping)
+    v_all = O.kv_write(b.v_pool, b.v_new, b.slot_mapping)
+    q = np.zeros((1, 1, d), dtype=np.float32)
+    q[0, 0, 0] = 64.0
+    enc = (lambda x: W.f32_to_bf16_bits(x)) if dtype == "bf16" else (lambda x: x.astype(np.float32))
+    r = DecodeRun(b)
+    r.v = dev(v_all)
+    for part in (0, 64):
+        for target in list(range(0, n, 7)) + [n - 1]:
+            k = np.array(k_new, copy=True)
+            kv = O.widen(k, dtype)
+            for t in range(n):
+                _, pb, off = O.translate(b.block_tables[0], t, bs)
+                kv[pb, 0, off, :] = 0.0
+                kv[pb, 0, off, 0] = 64.0 if t == target else -64.0
+            r.k = dev(enc(kv.astype(np.float32)))
+            got = r.decode(part, q=dev(enc(q)))
+            _, pb, off = O.translate(b.block_tables[0], target, bs)
+            want = v_all[pb, 0, off]
+            assert np.array_equal(got[0, 0].view(want.dtype), want), (part, target)
+
+
+def test_max_context_len_bound_respected():
+    """A host bound larger than every context changes nothing; the grid just has idle
+    partitions."""
+    b = W.gqa(num_seqs=4)
+    r = DecodeRun(b)
+    r.write()
+    a = r.decode(256)
+    c = r.decode(256, max_ctx=b.max_context_len * 3)
+    assert np.array_equal(a, c)
+
+
+# --------------------------------------------------------------------------
+# full-size workloads, launched as the benchmark launches them
+# --------------------------------------------------------------------------
+def test_full_gqa():
+    check(W.gqa(), partition_tokens=0, label="full")
+
+
+def test_full_long_context():
+    check(W.long_context(), partition_tokens=0, label="full")
+
+
+def test_full_prefix_cow():
+    p = W.prefix_cow()
+    b = p.batch
+    print(f"decode prefix_cow full S={b.num_seqs}", flush=True)
+    r = DecodeRun(b)
+    pkv.copy_blocks(r.k, r.v, dev(p.block_mapping))
+    r.write()
+    got = O.widen(r.decode(0), "bf16")
+    rng = np.random.Generator(np.random.PCG64(1))
+    seqs = sorted(rng.choice(b.num_seqs, 24, replace=False).tolist())
+    k = O.kv_write(O.copy_blocks(b.k_pool, p.block_mapping), b.k_new, b.slot_mapping)
+    v = O.kv_write(O.copy_blocks(b.v_pool, p.block_mapping), b.v_new, b.slot_mapping)
+    want = oracle_decode(b, k, v, seqs=seqs)
+    assert rownorm_err(got, want) <= TOL["bf16"]
+
+
+def test_full_mixed_decode_part():
+    m = W.mixed()
+    b = m.decode
+    print(f"decode mixed full S={b.num_seqs}", flush=True)
+    r = DecodeRun(b)
+    r.write()
+    got = O.widen(r.decode(0), "bf16")
+    k, v = oracle_after_write(b)
+    rng = np.random.Generator(np.random.PCG64(2))
+    seqs = sorted(rng.choice(b.num_seqs, 24, replace=False).tolist())
+    want = oracle_decode(b, k, v, seqs=seqs)
+    assert rownorm_err(got, want) <= TOL["bf16"]
