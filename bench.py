@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged KV-cache hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gqa|long|prefix_cow|mixed]
+
+One step is one pass of the path over one synthetic batch: the step's cache
+write (paged_kv_write) followed by paged decode attention (split-context
+partitions + log-sum-exp merge); the prefix workload adds its copy-on-write
+block copies and the mixed workload its chunked-prefill attention.  Inputs are
+resident in HBM before timing starts.  Several device copies of the pools are
+rotated step by step so that repeated steps cannot be served from the 256 MB
+Infinity Cache.
+
+Prints ONE JSON line: metric/value = decode KV GB/s of the whole step
+(algorithmic KV bytes: K and V of every valid token, read once per
+(sequence, kv head)), plus seqs/s, a roofline object for the decode kernels
+(HIP events on the launch stream) and the CPU oracle timed on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
+METRIC = "paged decode attention KV GB/s (% of HBM peak) + seqs/s, 1xMI355X"
+
+
+def kv_bytes(context_lens, num_kv_heads, head_dim, elem) -> int:
+    """Algorithmic bytes of one decode call: K and V of every valid token, each read
+    once per (sequence, kv head) -- 2*N*L*H*D*P of the vAttention page with N = 1."""
+    return int(2 * np.asarray(context_lens, dtype=np.int64).sum() * num_kv_heads * head_dim * elem)
+
+
+def prefill_flops(pre) -> int:
+    """Algorithmic flops of causal chunk attention: 4*D per visible (query, key) pair
+    per query head (QK^T and PV)."""
+    tot = 0
+    for c in range(pre.num_chunks):
+        nq = int(pre.cu_q_lens[c + 1] - pre.cu_q_lens[c])
+        n = int(pre.context_lens[c])
+        visible = nq * (n - nq) + nq * (nq + 1) // 2
+        tot += visible
+    return int(4 * pre.head_dim * pre.num_q_heads * tot)
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------
+# CPU oracle baseline (bounded sample, on this host's cores)
+# ----------------------------------------------------------------------------
+_ORACLE_BATCH = None
+
+
+def _oracle_unit(s):
+    from threadpoolctl import threadpool_limits
+    from oracle import paged as O
+    b, k, v = _ORACLE_BATCH
+    with threadpool_limits(1):
+        O.decode(b.q, k, v, b.block_tables, b.context_lens, b.scale, b.dtype, b.num_kv_heads,
+                 seqs=[s])
+    return s
+
+
+def cpu_baseline(b, target_s=12.0):
+    """Time the oracle's decode of the batch (after the step's write) on this host's cores,
+    one process per core, one sequence per task; repeat passes until about target_s of CPU."""
+    import multiprocessing as mp
+    from oracle import paged as O
+    global _ORACLE_BATCH
+    k = O.kv_write(b.k_pool, b.k_new, b.slot_mapping)
+    v = O.kv_write(b.v_pool, b.v_new, b.slot_mapping)
+    _ORACLE_BATCH = (b, k, v)
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    # one single-process pass over a few sequences estimates the per-sequence cost
+    t0 = time.perf_counter()
+    probe = list(range(min(4, b.num_seqs)))
+    for s in probe:
+        _oracle_unit(s)
+    per_seq = (time.perf_counter() - t0) / len(probe)
+    passes = max(1, int(math.ceil(target_s / max(per_seq * b.num_seqs, 1e-3))))
+    passes = min(passes, 8)
+    ctx = mp.get_context("fork")
+    with ctx.Pool(cores) as pool:
+        t0 = time.perf_counter()
+        for _ in range(passes):
+            pool.map(_oracle_unit, range(b.num_seqs), chunksize=1)
+        wall = time.perf_counter() - t0
+    _ORACLE_BATCH = None
+    byts = passes * kv_bytes(b.context_lens, b.num_kv_heads, b.head_dim, 2 if b.dtype == "bf16" else 4)
+    return {"value": round(byts / wall / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "seqs_per_s": round(passes * b.num_seqs / wall, 2), "wall_s": round(wall, 2),
+            "sample": f"{passes} pass(es) of fp64 numpy decode over all {b.num_seqs} sequences of "
+                      f"the {b.name} batch, one process per core"}
+
+
+# ----------------------------------------------------------------------------
+# GPU
+# ----------------------------------------------------------------------------
+def _dev(a):
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a).cuda()
+
+
+def make_workload(name):
+    import workloads as W
+    if name == "gqa":
+        b = W.gqa(poison=False)
+        return dict(batch=b, extra=None, prefill=None)
+    if name == "long":
+        return dict(batch=W.long_context(poison=False), extra=None, prefill=None)
+    if name == "prefix_cow":
+        p = W.prefix_cow(poison=False)
+        return dict(batch=p.batch, extra=p, prefill=None)
+    if name == "mixed":
+        m = W.mixed(poison=False)
+        return dict(batch=m.decode, extra=m, prefill=m.prefill)
+    raise SystemExit(f"unknown workload {name}")
+
+
+def run(args):
+    import torch
+    import paged_kv_cache_79_amd as pkv
+
+    log(f"building workload {args.workload}")
+    wl = make_workload(args.workload)
+    b = wl["batch"]
+    log(f"workload ready: {b.num_seqs} sequences, max context {b.max_context_len}")
+    elem = 2 if b.dtype == "bf16" else 4
+    pool_bytes = 2 * b.k_pool.nbytes
+    # enough pool copies that a rotation cycle spans well over 4x the 256 MB MALL
+    copies = max(2, min(8, int(math.ceil(2.4e9 / max(pool_bytes, 1)))))
+    k0, v0 = _dev(b.k_pool), _dev(b.v_pool)
+    pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(copies - 1)]
+    q = _dev(b.q)
+    tables = _dev(b.block_tables)
+    ctx = _dev(b.context_lens)
+    k_new, v_new, slots = _dev(b.k_new), _dev(b.v_new), _dev(b.slot_mapping)
+    out = torch.empty_like(q)
+    pt = args.partition_tokens            # 0: balanced split over the resident waves
+    ws_bytes = pkv.paged_attention_decode_workspace_bytes(b.num_seqs, b.num_q_heads, b.num_kv_heads,
+                                                          b.head_dim, b.max_context_len, pt)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    extra = wl["extra"]
+    cow_map = _dev(extra.block_mapping) if args.workload == "prefix_cow" else None
+    pre = wl["prefill"]
+    if pre is not None:
+        pq, pcu = _dev(pre.q), _dev(pre.cu_q_lens)
+        ptab, pctx = _dev(pre.block_tables), _dev(pre.context_lens)
+        pout = torch.empty_like(pq)
+
+    stream = torch.cuda.current_stream()
+
+    def decode(i):
+        kp, vp = pools[i % copies]
+        pkv.paged_attention_decode(out, q, kp, vp, tables, ctx, b.max_context_len, b.scale,
+                                   partition_tokens=pt, workspace=ws)
+
+    def step(i):
+        kp, vp = pools[i % copies]
+        if cow_map is not None:
+            pkv.copy_blocks(kp, vp, cow_map)
+        pkv.paged_kv_write(kp, vp, k_new, v_new, slots)
+        if pre is not None:
+            pkv.paged_attention_prefill_chunk(pout, pq, pcu, kp, vp, ptab, pctx, pre.max_q_len,
+                                              pre.max_context_len, pre.scale)
+        decode(i)
+
+    def timed(fn, n):
+        """HIP events on the launch stream around n back-to-back calls; mean ms per call."""
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for i in range(n):
+            fn(i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / n
+
+    log(f"{copies} pool copies on device; warmup {args.warmup}, timing {args.steps} steps")
+    for i in range(args.warmup):
+        step(i)
+    ms_step = timed(step, args.steps)
+    # the decode kernels alone, same inputs and pool rotation, for the roofline
+    dec_runs = [timed(decode, args.steps) for _ in range(3)]
+    dec_avg = sorted(dec_runs)[1]
+    byts = kv_bytes(b.context_lens, b.num_kv_heads, b.head_dim, elem)
+    value = byts / (ms_step * 1e-3) / 1e9
+    achieved = byts / (dec_avg * 1e-3) / 1e9
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": b.dtype,
+        "data": "synthetic",
+        "config": {"workload": b.name, "num_seqs": b.num_seqs, "num_q_heads": b.num_q_heads,
+                   "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim,
+                   "block_size": b.block_size, "max_context_len": b.max_context_len,
+                   "mean_context_len": round(float(np.mean(b.context_lens)), 1),
+                   "split": "balanced" if pt == 0 else f"partitions of {pt}",
+                   "pool_copies_rotated": copies},
+        "seqs_per_s": round(b.num_seqs / (ms_step * 1e-3), 1),
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "kv_bytes_per_step": byts,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "paged_attention_decode (attention kernel + merge kernel)",
+                     "avg_us": round(dec_avg * 1e3, 2),
+                     "runs_us": [round(x * 1e3, 2) for x in dec_runs]},
+    }
+    if pre is not None:
+        # prefill alone, same inputs and pool rotation
+        def prefill(i):
+            kp, vp = pools[i % copies]
+            pkv.paged_attention_prefill_chunk(pout, pq, pcu, kp, vp, ptab, pctx, pre.max_q_len,
+                                              pre.max_context_len, pre.scale)
+        p_ms = timed(prefill, max(5, args.steps // 4))
+        fl = prefill_flops(pre)
+        rec["prefill"] = {"avg_us": round(p_ms * 1e3, 2), "flops": fl,
+                          "tflops": round(fl / (p_ms * 1e-3) / 1e12, 2),
+                          "mfma_frac": round(fl / (p_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    log(f"GPU: {ms_step * 1e3:.1f} us/step, decode {dec_avg * 1e3:.1f} us")
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        rec["cpu_baseline"] = cpu_baseline(b)
+    else:
+        rec["cpu_baseline"] = None
+    return rec
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gqa", choices=["gqa", "long", "prefix_cow", "mixed"])
+    ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    rec = run(args)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

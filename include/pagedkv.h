@@ -103,19 +103,21 @@ pkv_status copy_blocks(pkv_dtype dtype, void* k_pool, void* v_pool, int32_t num_
  * context_lens[s] tokens of the sequence, read through its block table row
  * ("2.1 PagedAttention", sections 3 and 5):
  *     out[s][hq][:] = sum_t softmax_t(scale * q[s][hq] . K_t) * V_t
- * with K_t, V_t at (block_tables[s][t / bs], kv head, t % bs).  The context is
- * cut into partitions of partition_tokens tokens whose partial softmax states
- * are merged by log-sum-exp; the result does not depend on the partition size
- * beyond float rounding.  context_len 0 gives a zero row.
+ * with K_t, V_t at (block_tables[s][t / bs], kv head, t % bs).  Long contexts are
+ * split into pieces whose partial softmax states are merged by log-sum-exp; the
+ * result does not depend on the split beyond float rounding.  context_len 0
+ * gives a zero row.
  *
- * paged_attention_decode_partition_tokens: partition size the library picks
- * when partition_tokens == 0 (a multiple of 64).
+ * Split: partition_tokens == 0 (default) divides all 64-token tiles of the batch
+ * evenly over the waves the device keeps resident, whatever the mix of lengths
+ * (the split, hence the rounding, depends on the device's compute-unit count);
+ * partition_tokens > 0 cuts every context into pieces of that many positions
+ * instead (device independent).
+ *
  * paged_attention_decode_workspace_bytes: bytes of device workspace the call
- * needs for that partition size (0 when every sequence fits one partition).
+ * needs for that choice of split (for the default split it depends on the
+ * current device; for fixed partitions it is 0 when every context fits one).
  */
-int32_t paged_attention_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
-                                                int32_t max_context_len);
-
 size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                               int32_t num_kv_heads, int32_t head_dim,
                                               int32_t max_context_len, int32_t partition_tokens);
@@ -127,7 +129,7 @@ size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_he
  *   context_lens  int32 [num_seqs], each in [0, max_blocks_per_seq*block_size]
  *   max_context_len  host-known upper bound of context_lens (sizes the grid;
  *                    a larger context is truncated to it)
- *   partition_tokens 0 = library choice, else a positive multiple of 64
+ *   partition_tokens 0 = balanced split (default), else a positive multiple of 64
  *   workspace     device scratch of at least paged_attention_decode_workspace_bytes
  *                 (may be NULL when that is 0); its contents need no initialisation
  *                 and are garbage afterwards; calls sharing a workspace must not

@@ -20,7 +20,6 @@ EXPORTS = (
     "pkv_status_string",
     "paged_kv_write",
     "copy_blocks",
-    "paged_attention_decode_partition_tokens",
     "paged_attention_decode_workspace_bytes",
     "paged_attention_decode",
     "paged_attention_prefill_chunk",
@@ -55,8 +54,6 @@ def load_library(path: Optional[str] = None):
     lib.paged_kv_write.restype = ctypes.c_int
     lib.copy_blocks.argtypes = [ctypes.c_int, VP, VP, I32, I32, I32, I32, VP, I32, VP]
     lib.copy_blocks.restype = ctypes.c_int
-    lib.paged_attention_decode_partition_tokens.argtypes = [I32, I32, I32]
-    lib.paged_attention_decode_partition_tokens.restype = I32
     lib.paged_attention_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32]
     lib.paged_attention_decode_workspace_bytes.restype = SZ
     lib.paged_attention_decode.argtypes = [ctypes.c_int, VP, VP, VP, VP, I32, I32, I32, I32, VP, I32,
@@ -157,11 +154,6 @@ def copy_blocks(k_pool, v_pool, block_mapping, stream=None) -> None:
     _check("copy_blocks", lib.copy_blocks(
         _dtype_code(k_pool), _ptr(k_pool), _ptr(v_pool), nb, hkv, bs, d, _ptr(block_mapping), n,
         _stream(stream)))
-
-
-def paged_attention_decode_partition_tokens(num_seqs: int, num_kv_heads: int, max_context_len: int) -> int:
-    return int(load_library().paged_attention_decode_partition_tokens(num_seqs, num_kv_heads,
-                                                                      max_context_len))
 
 
 def paged_attention_decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int,

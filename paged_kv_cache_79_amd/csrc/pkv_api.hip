@@ -3,6 +3,8 @@
 // never allocates, and never synchronises.
 #include <math.h>
 
+#include <algorithm>
+
 #include "pagedkv.h"
 #include "pkv_internal.h"
 
@@ -47,19 +49,33 @@ pkv_status launch_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_E
 
 int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Partition size: aim for about 8K (sequence, kv head, partition) work items so
-// that 256 CUs stay busy through the ragged end, with at least 256 tokens per
-// partition so the merge traffic stays a few percent of the KV bytes.
-int32_t pick_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len) {
-    const int64_t work = (int64_t)num_seqs * num_kv_heads * (int64_t)max_context_len;
-    const int64_t per = work / 8192;
-    int32_t pt = 256;
-    while (pt < per && pt < 8192) pt *= 2;
-    return pt;
-}
-
 int32_t num_partitions(int32_t max_context_len, int32_t pt) {
     return max_context_len <= 0 ? 1 : (int32_t)cdiv64(max_context_len, pt);
+}
+
+// Upper bound of the persistent waves of the balanced split on the current device:
+// 8 single-wave workgroups per CU (the register and LDS budget of the bf16 kernels;
+// the fp32 ones keep fewer resident).
+int64_t balanced_wave_bound() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    return (int64_t)cus * 8;
+}
+
+size_t decode_workspace(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t max_context_len, int32_t partition_tokens) {
+    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        num_q_heads % num_kv_heads)
+        return 0;
+    if (partition_tokens > 0) {
+        const int32_t np = num_partitions(max_context_len, partition_tokens);
+        if (np <= 1) return 0;
+        return (size_t)num_seqs * num_q_heads * np * (size_t)(head_dim + 2) * sizeof(float);
+    }
+    const int64_t group = num_q_heads / num_kv_heads;
+    return (size_t)balanced_wave_bound() * 2 * group * (size_t)(head_dim + 2) * sizeof(float);
 }
 
 }  // namespace
@@ -118,20 +134,11 @@ pkv_status copy_blocks(pkv_dtype dtype, void* k_pool, void* v_pool, int32_t num_
     return launch_status(launch_copy_blocks(a, stream));
 }
 
-int32_t paged_attention_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
-                                                int32_t max_context_len) {
-    return pick_partition(num_seqs, num_kv_heads, max_context_len);
-}
-
 size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                               int32_t num_kv_heads, int32_t head_dim,
                                               int32_t max_context_len, int32_t partition_tokens) {
-    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0) return 0;
-    const int32_t pt = partition_tokens > 0 ? partition_tokens
-                                            : pick_partition(num_seqs, num_kv_heads, max_context_len);
-    const int32_t np = num_partitions(max_context_len, pt);
-    if (np <= 1) return 0;
-    return (size_t)num_seqs * num_q_heads * np * (size_t)(head_dim + 2) * sizeof(float);
+    return decode_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                            partition_tokens);
 }
 
 pkv_status paged_attention_decode(pkv_dtype dtype, void* out, const void* q, const void* k_pool,
@@ -156,11 +163,8 @@ pkv_status paged_attention_decode(pkv_dtype dtype, void* out, const void* q, con
     if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PKV_ERR_NULL;
     if ((int64_t)num_seqs * num_kv_heads > 65535) return PKV_ERR_UNSUPPORTED;  // grid.y
 
-    const int32_t pt = partition_tokens > 0 ? partition_tokens
-                                            : pick_partition(num_seqs, num_kv_heads, max_context_len);
-    const int32_t np = num_partitions(max_context_len, pt);
-    const size_t need = paged_attention_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads,
-                                                               head_dim, max_context_len, pt);
+    const size_t need = decode_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                         max_context_len, partition_tokens);
     if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
 
     DecodeArgs a;
@@ -170,17 +174,31 @@ pkv_status paged_attention_decode(pkv_dtype dtype, void* out, const void* q, con
     a.v_pool = static_cast<const char*>(v_pool);
     a.block_tables = block_tables;
     a.context_lens = context_lens;
-    a.part_o = static_cast<float*>(workspace);
-    a.part_ml = need > 0 ? static_cast<float*>(workspace) +
-                               (size_t)num_seqs * num_q_heads * np * head_dim
-                         : nullptr;
     a.g = g;
+    a.num_seqs = num_seqs;
     a.num_q_heads = num_q_heads;
     a.max_blocks_per_seq = max_blocks_per_seq;
     a.max_context_len = max_context_len;
-    a.part_tokens = pt;
-    a.num_parts = np;
     a.scale_log2 = scale * 1.4426950408889634f;
+    a.part_tokens = partition_tokens;
+    a.num_parts = 1;
+    a.num_waves = 0;
+    a.part_o = static_cast<float*>(workspace);
+    a.part_ml = nullptr;
+    if (partition_tokens > 0) {
+        a.num_parts = num_partitions(max_context_len, partition_tokens);
+        if (a.num_parts > 1)
+            a.part_ml = a.part_o + (size_t)num_seqs * num_q_heads * a.num_parts * head_dim;
+    } else {
+        // one wave per resident slot, but no more than there are tiles to share out
+        const int64_t tiles_bound = (int64_t)num_seqs * num_kv_heads * cdiv64(max_context_len, 64);
+        int64_t waves = decode_balanced_waves(dtype == PKV_BF16, head_dim, group);
+        if (waves <= 0) return PKV_ERR_LAUNCH;
+        waves = std::min(waves, balanced_wave_bound());
+        waves = std::max<int64_t>(1, std::min(waves, tiles_bound));
+        a.num_waves = (int32_t)waves;
+        a.part_ml = a.part_o + (size_t)waves * 2 * group * head_dim;
+    }
     return launch_status(launch_decode(a, dtype == PKV_BF16, head_dim, group, num_seqs, stream));
 }
 

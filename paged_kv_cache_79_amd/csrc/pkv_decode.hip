@@ -4,28 +4,35 @@
 // of a sequence attends to the sequence's whole context, each logical position
 // t being read at physical block block_table[t / block_size], slot
 // t % block_size of the pool.  The pages' kernel sketch walks the blocks of
-// one sequence with a 32-lane warp; here a 64-lane wave owns one
-// (sequence, kv head, context partition) work item and consumes the context
-// in tiles of 64 tokens:
+// one sequence with a 32-lane warp; here a 64-lane wave consumes contexts in
+// tiles of 64 tokens of one (sequence, kv head):
 //
-//   1. load    every lane issues 16-byte loads in the pool's natural order, so
-//              one wave instruction covers 1 KiB of contiguous K (or V) of one
-//              block; the block id comes from a scalar (uniform) table read and
-//              is folded into a scalar base address;
+//   1. load    every lane issues 16-byte nontemporal loads in the pool's natural
+//              order, so one wave instruction covers 1 KiB of contiguous K (or V)
+//              of one block; the tile's block ids arrive with one vector load
+//              (issued a tile ahead) and are taken with readlane into scalar bases;
 //   2. QK      K is restaged through LDS so that lane t owns token t of the
-//              tile; it forms the dot products of all G query heads of its
-//              group (grouped-query packing: one K read serves G heads) with
-//              q held in scalar registers -- no cross-lane reduction;
-//   3. softmax tile maximum by DPP row rotations + permlane swaps; running
-//              max per head, per-lane running sums (summed once at the end);
+//              tile and forms the dot products of all G query heads of its
+//              group (grouped-query packing: one K read serves G heads) with q
+//              broadcast from LDS -- no cross-lane reduction;
+//   3. softmax tile maximum by DPP row rotations + permlane swaps; running max
+//              per head, per-lane running sums (summed once per segment);
 //   4. PV      V stays in the load layout (lane = 8 elements of one token row);
-//              bf16 probabilities of two tokens are paired with the matching
-//              V halves (byte permute) and accumulated with v_dot2;
-//   5. output  partial (max, sum, unnormalised o) per partition, or the final
-//              row when a sequence fits one partition.
-// A second kernel merges partitions by log-sum-exp.  Tokens at or beyond the
-// valid length are removed by selection (score -inf, V row zero), never by
-// arithmetic, so stale or NaN slots cannot leak into the result.
+//              bf16 probabilities of two tokens are paired with the matching V
+//              halves (byte permute) and accumulated with v_dot2.
+// Tokens at or beyond the valid length are removed by selection (score -inf,
+// V row zero), never by arithmetic, so stale or NaN slots cannot leak in.
+//
+// Work split.  By default (balanced split) a persistent grid of exactly as many
+// waves as the device keeps resident divides all tiles of the batch -- ordered
+// by (sequence, kv head, tile) -- into equal contiguous ranges, so every wave
+// streams the same number of bytes whatever the mix of context lengths.  A
+// (sequence, kv head) that lies inside one wave's range is finished by that
+// wave; one that straddles waves leaves partial softmax states that a second
+// kernel merges by log-sum-exp.  With a fixed partition size (> 0) the split
+// is by sequence position instead and does not depend on the device.
+#include <mutex>
+
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -45,48 +52,57 @@ struct DecodeShape {
     static_assert(R >= 2 && R <= 8, "row groups");
 };
 
+template <bool BF16>
+struct DecodeLds {
+    static constexpr int PWORDS = BF16 ? kTile / 2 * 8 : kTile * 8;   // probabilities (dwords)
+};
+
+__device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int c) {
+    return max(0, min(c, min(a.max_context_len, a.max_blocks_per_seq * a.g.block_size)));
+}
+__device__ __forceinline__ int ntiles_of(int ctx) { return (ctx + kTile - 1) / kTile; }
+
+// Block-table entries of the 64-token tile starting at t0: lane j holds the physical
+// block of logical block t0/bs + j (clamped to the sequence's last block), so one
+// vector load fetches every entry a tile needs.
+__device__ __forceinline__ int load_tile_table(const int32_t* table, int t0, int log2_bs, int nblk,
+                                               int lane) {
+    return table[min((t0 >> log2_bs) + lane, nblk - 1)];
+}
+
+// Softmax state of one segment of one (sequence, kv head) for its G query heads,
+// after the per-lane pieces have been combined: m and l are uniform; lanes of row
+// group 0 hold o for their 16-byte chunk of the head dimension.
 template <bool BF16, int D, int G>
-__global__ __launch_bounds__(64) void decode_partial_kernel(DecodeArgs a) {
+struct SegState {
+    float m[G], l[G], o[G][DecodeShape<BF16, D>::EPC];
+};
+
+// Attend the G query heads of (s, h) to tokens [t_begin, t_end) of the sequence.
+template <bool BF16, int D, int G>
+__device__ __forceinline__ void attend_segment(const DecodeArgs& a, int s, int h, int ctx,
+                                               int t_begin, int t_end, char* lds_k,
+                                               uint32_t* lds_p, uint32_t* lds_q,
+                                               SegState<BF16, D, G>& st) {
     using S = DecodeShape<BF16, D>;
-    __shared__ __attribute__((aligned(16))) char lds_k[kTile * S::KPITCH];
-    __shared__ __attribute__((aligned(16))) uint32_t lds_p[kTile * 8];
-
-    const int part = blockIdx.x;
-    const int sh = blockIdx.y;
-    const int s = sh / a.g.num_kv_heads;
-    const int h = sh - s * a.g.num_kv_heads;
     const int lane = threadIdx.x;
-    const int Hq = a.num_q_heads;
     const int bs = a.g.block_size;
-    const int mb = a.max_blocks_per_seq;
-    const int hq0 = h * G;
-
-    int ctx = as_const(a.context_lens)[s];
-    ctx = max(0, min(ctx, min(a.max_context_len, mb * bs)));
-    const int t_begin = part * a.part_tokens;
-    const bool single = a.num_parts == 1;
-
-    if (t_begin >= ctx) {
-        if (single) {  // empty context: zero rows
-            if constexpr (BF16) {
-                uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)s * Hq + hq0) * D;
-                for (int e = lane; e < G * D; e += 64) o[e] = 0;
-            } else {
-                float* o = reinterpret_cast<float*>(a.out) + ((int64_t)s * Hq + hq0) * D;
-                for (int e = lane; e < G * D; e += 64) o[e] = 0.f;
-            }
-        }
-        return;
-    }
-    const int t_end = min(ctx, t_begin + a.part_tokens);
     const int nblk = (ctx + bs - 1) >> a.g.log2_bs;
     const int ra = lane / S::CPR;          // row inside a wave-wide load
     const int rc = lane - ra * S::CPR;     // 16-byte chunk inside the row
-    const_ptr<int32_t> table = as_const(a.block_tables) + (int64_t)s * mb;
-    const char* kb = a.k_pool + (int64_t)h * a.g.head_stride_bytes;
-    const char* vb = a.v_pool + (int64_t)h * a.g.head_stride_bytes;
-    const_ptr<uint32_t> qrow = as_const(reinterpret_cast<const uint32_t*>(
-        reinterpret_cast<const char*>(a.q) + ((int64_t)s * Hq + hq0) * S::RB));
+    const uint32_t lane_off = (uint32_t)(ra * S::RB + rc * 16);
+    const int32_t* table = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+    const char* kb = (const char*)pin_uniform(a.k_pool + (int64_t)h * a.g.head_stride_bytes);
+    const char* vb = (const char*)pin_uniform(a.v_pool + (int64_t)h * a.g.head_stride_bytes);
+
+    int tab_cur = load_tile_table(table, t_begin, a.g.log2_bs, nblk, lane);
+    __syncthreads();  // the previous segment is done with lds_q
+    {
+        const u32x4* qsrc = reinterpret_cast<const u32x4*>(
+            reinterpret_cast<const char*>(a.q) + ((int64_t)s * a.num_q_heads + h * G) * S::RB);
+        u32x4* qdst = reinterpret_cast<u32x4*>(lds_q);
+        for (int c = lane; c < G * S::RB / 16; c += 64) qdst[c] = qsrc[c];
+    }
 
     float m[G], l[G], o[G][S::EPC];
 #pragma unroll
@@ -98,57 +114,67 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeArgs a) {
     }
 
     for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
-        // ---- 1. load K and V of the tile (natural layout) -------------------
-        uint4 kreg[S::NL], vreg[S::NL];
+        // ---- 1. loads of this tile; the next tile's table entries go out after them
+        u32x4 kreg[S::NL], vreg[S::NL];
+        const int tab = tab_cur;
+        // refreshed in the loop so the 32-bit offset is not widened and hoisted: the
+        // loads then take the scalar base + 32-bit lane offset form
+        uint32_t loff = lane_off;
+        asm volatile("" : "+v"(loff));
 #pragma unroll
         for (int i = 0; i < S::NL; ++i) {
-            const int r0 = t0 + i * S::R;                  // uniform: first token of this load
-            const int lb = min(r0 >> a.g.log2_bs, nblk - 1);
-            int pb = table[lb];
-            pb = ((unsigned)pb < (unsigned)a.g.num_blocks) ? pb : 0;
-            const int64_t base = (int64_t)pb * a.g.block_stride_bytes;  // scalar
-            const uint32_t off = (uint32_t)(((r0 & (bs - 1)) + ra) * S::RB + rc * 16);
-            kreg[i] = *reinterpret_cast<const uint4*>((kb + base) + off);
-            vreg[i] = *reinterpret_cast<const uint4*>((vb + base) + off);
+            const int rel = (i * S::R) >> a.g.log2_bs;   // block of this load inside the tile
+            int pb = __builtin_amdgcn_readlane(tab, rel);
+            pb = ((unsigned)pb < (unsigned)a.g.num_blocks) ? pb : 0;   // never dereference a bad id
+            // scalar base: block, head and first row of this load; per-lane part is lane_off.
+            // The 64-bit product is spelled as two 32-bit halves so it stays on the scalar unit.
+            const uint32_t ub = (uint32_t)pb, us = (uint32_t)a.g.block_stride_bytes;
+            const uint64_t base = (((uint64_t)__umulhi(ub, us) << 32) | (uint64_t)(ub * us)) +
+                                  (uint64_t)(((i * S::R) & (bs - 1)) * S::RB);
+            // K and V are read exactly once: nontemporal loads keep them from
+            // displacing reusable lines (tables, q, partials) in the caches
+            kreg[i] = __builtin_nontemporal_load((global_ptr<u32x4>)(pin_uniform(kb + base) + loff));
+            vreg[i] = __builtin_nontemporal_load((global_ptr<u32x4>)(pin_uniform(vb + base) + loff));
         }
+        tab_cur = load_tile_table(table, t0 + kTile, a.g.log2_bs, nblk, lane);
 #pragma unroll
         for (int i = 0; i < S::NL; ++i)
-            *reinterpret_cast<uint4*>(lds_k + (i * S::R + ra) * S::KPITCH + rc * 16) = kreg[i];
-        if (t0 + kTile > t_end) {  // tail tile: rows past the valid length contribute nothing
-#pragma unroll
-            for (int i = 0; i < S::NL; ++i)
-                if (t0 + i * S::R + ra >= t_end) vreg[i] = make_uint4(0, 0, 0, 0);
-        }
+            *reinterpret_cast<u32x4*>(lds_k + (i * S::R + ra) * S::KPITCH + rc * 16) = kreg[i];
         __syncthreads();
 
-        // ---- 2. QK: lane = token ------------------------------------------
+        // ---- 2. QK: lane = token ------------------------------------------------
         float acc[G];
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) acc[hh] = 0.f;
-        const_ptr<uint32_t> qs = qrow;
-        asm volatile("" : "+s"(qs));   // re-read q each tile (keeps it in SGPRs, not hoisted)
         const char* krow = lds_k + lane * S::KPITCH;
+        // q is re-read from LDS every tile: an opaque zero offset stops the compiler from
+        // hoisting all G*D q values out of the loop into registers
+        uint32_t qoff = 0;
+        asm volatile("" : "+v"(qoff));
 #pragma unroll
         for (int j = 0; j < S::CPR; ++j) {
-            const uint4 kk = *reinterpret_cast<const uint4*>(krow + j * 16);
+            const u32x4 kk = *reinterpret_cast<const u32x4*>(krow + j * 16);
 #pragma unroll
             for (int hh = 0; hh < G; ++hh) {
-                const_ptr<uint32_t> qh = qs + hh * (S::RB / 4) + j * 4;
+                const u32x4 qq = *reinterpret_cast<const u32x4*>(
+                    reinterpret_cast<const char*>(lds_q) + qoff + (hh * (S::RB / 4) + j * 4) * 4);
                 if constexpr (BF16) {
-                    acc[hh] = dot2_bf16(kk.x, qh[0], acc[hh]);
-                    acc[hh] = dot2_bf16(kk.y, qh[1], acc[hh]);
-                    acc[hh] = dot2_bf16(kk.z, qh[2], acc[hh]);
-                    acc[hh] = dot2_bf16(kk.w, qh[3], acc[hh]);
+                    acc[hh] = dot2_bf16(kk.x, qq.x, acc[hh]);
+                    acc[hh] = dot2_bf16(kk.y, qq.y, acc[hh]);
+                    acc[hh] = dot2_bf16(kk.z, qq.z, acc[hh]);
+                    acc[hh] = dot2_bf16(kk.w, qq.w, acc[hh]);
                 } else {
-                    acc[hh] = fmaf(u2f(kk.x), u2f(qh[0]), acc[hh]);
-                    acc[hh] = fmaf(u2f(kk.y), u2f(qh[1]), acc[hh]);
-                    acc[hh] = fmaf(u2f(kk.z), u2f(qh[2]), acc[hh]);
-                    acc[hh] = fmaf(u2f(kk.w), u2f(qh[3]), acc[hh]);
+                    acc[hh] = fmaf(u2f(kk.x), u2f(qq.x), acc[hh]);
+                    acc[hh] = fmaf(u2f(kk.y), u2f(qq.y), acc[hh]);
+                    acc[hh] = fmaf(u2f(kk.z), u2f(qq.z), acc[hh]);
+                    acc[hh] = fmaf(u2f(kk.w), u2f(qq.w), acc[hh]);
                 }
             }
+            // keep the LDS reads of two chunks at a time in flight, not all of them
+            if (j & 1) __builtin_amdgcn_sched_barrier(0);
         }
 
-        // ---- 3. online softmax --------------------------------------------
+        // ---- 3. online softmax ------------------------------------------------------
         const bool valid = (t0 + lane) < t_end;
         float alpha[G];
 #pragma unroll
@@ -160,7 +186,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeArgs a) {
             m[hh] = mn;
             l[hh] = l[hh] * alpha[hh] + p;
             if constexpr (BF16) {
-                // pair slot of this token: rows i*R+a and (i^1)*R+a share one dword
+                // rows i*R+a and (i^1)*R+a share one dword: (even row lo, odd row hi)
                 const int i = lane / S::R, ar = lane - (lane / S::R) * S::R;
                 const int pidx = (i >> 1) * S::R + ar;
                 reinterpret_cast<uint16_t*>(lds_p)[(pidx * 8 + hh) * 2 + (i & 1)] = f32_to_bf16(p);
@@ -170,7 +196,12 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeArgs a) {
         }
         __syncthreads();
 
-        // ---- 4. PV --------------------------------------------------------
+        // ---- 4. PV ------------------------------------------------------------------
+        if (t0 + kTile > t_end) {  // tail tile: rows past the valid length contribute nothing
+#pragma unroll
+            for (int i = 0; i < S::NL; ++i)
+                if (t0 + i * S::R + ra >= t_end) vreg[i] = u32x4{0u, 0u, 0u, 0u};
+        }
 #pragma unroll
         for (int hh = 0; hh < G; ++hh)
 #pragma unroll
@@ -178,10 +209,10 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeArgs a) {
         if constexpr (BF16) {
 #pragma unroll
             for (int ii = 0; ii < S::NL / 2; ++ii) {
-                const uint4 v0 = vreg[2 * ii], v1 = vreg[2 * ii + 1];
+                const u32x4 v0 = vreg[2 * ii], v1 = vreg[2 * ii + 1];
                 const uint32_t* pp = lds_p + (ii * S::R + ra) * 8;
-                const uint4 pa = *reinterpret_cast<const uint4*>(pp);
-                const uint4 pz = *reinterpret_cast<const uint4*>(pp + 4);
+                const u32x4 pa = *reinterpret_cast<const u32x4*>(pp);
+                const u32x4 pz = *reinterpret_cast<const u32x4*>(pp + 4);
                 const uint32_t pk[8] = {pa.x, pa.y, pa.z, pa.w, pz.x, pz.y, pz.z, pz.w};
                 const uint32_t w0[4] = {v0.x, v0.y, v0.z, v0.w};
                 const uint32_t w1[4] = {v1.x, v1.y, v1.z, v1.w};
@@ -212,60 +243,293 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeArgs a) {
         }
     }
 
-    // ---- 5. combine lanes and write --------------------------------------
+    // ---- combine lanes: per-lane sums, then the row groups sharing a chunk -----------
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-        l[hh] = wave_sum(l[hh]);
+        st.m[hh] = m[hh];
+        st.l[hh] = wave_sum(l[hh]);
 #pragma unroll
-        for (int e = 0; e < S::EPC; ++e) o[hh][e] = group_sum<S::R>(o[hh][e]);
+        for (int e = 0; e < S::EPC; ++e) st.o[hh][e] = group_sum<S::R>(o[hh][e]);
     }
-    if (single) {
+}
+
+// Normalised output rows of the G heads of (s, h).
+template <bool BF16, int D, int G>
+__device__ __forceinline__ void write_rows(const DecodeArgs& a, int s, int h,
+                                           const SegState<BF16, D, G>& st) {
+    using S = DecodeShape<BF16, D>;
+    const int lane = threadIdx.x;
+    const int ra = lane / S::CPR, rc = lane - (lane / S::CPR) * S::CPR;
+    if (ra != 0) return;
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+        const float inv = st.l[hh] > 0.f ? 1.f / st.l[hh] : 0.f;
+        const int64_t row = ((int64_t)s * a.num_q_heads + h * G + hh) * D + rc * S::EPC;
+        if constexpr (BF16) {
+            uint4 w;
+            w.x = pack_bf16(st.o[hh][0] * inv, st.o[hh][1] * inv);
+            w.y = pack_bf16(st.o[hh][2] * inv, st.o[hh][3] * inv);
+            w.z = pack_bf16(st.o[hh][4] * inv, st.o[hh][5] * inv);
+            w.w = pack_bf16(st.o[hh][6] * inv, st.o[hh][7] * inv);
+            *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.out) + row) = w;
+        } else {
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + row) =
+                make_float4(st.o[hh][0] * inv, st.o[hh][1] * inv, st.o[hh][2] * inv,
+                            st.o[hh][3] * inv);
+        }
+    }
+}
+
+// Unnormalised partial state of head hh into row prow0 + hh * prow_step of the
+// workspace (o: D floats per row; (max, sum): 2 floats per row).
+template <bool BF16, int D, int G>
+__device__ __forceinline__ void write_partial(const DecodeArgs& a, int64_t prow0, int64_t prow_step,
+                                              const SegState<BF16, D, G>& st) {
+    using S = DecodeShape<BF16, D>;
+    const int lane = threadIdx.x;
+    const int ra = lane / S::CPR, rc = lane - (lane / S::CPR) * S::CPR;
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+        const int64_t prow = prow0 + hh * prow_step;
         if (ra == 0) {
+            float* dst = a.part_o + prow * D + rc * S::EPC;
 #pragma unroll
-            for (int hh = 0; hh < G; ++hh) {
-                const float inv = l[hh] > 0.f ? 1.f / l[hh] : 0.f;
-                const int64_t row = ((int64_t)s * Hq + hq0 + hh) * D + rc * S::EPC;
-                if constexpr (BF16) {
-                    uint4 w;
-                    w.x = pack_bf16(o[hh][0] * inv, o[hh][1] * inv);
-                    w.y = pack_bf16(o[hh][2] * inv, o[hh][3] * inv);
-                    w.z = pack_bf16(o[hh][4] * inv, o[hh][5] * inv);
-                    w.w = pack_bf16(o[hh][6] * inv, o[hh][7] * inv);
-                    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.out) + row) = w;
-                } else {
-                    *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + row) =
-                        make_float4(o[hh][0] * inv, o[hh][1] * inv, o[hh][2] * inv, o[hh][3] * inv);
-                }
-            }
+            for (int e = 0; e < S::EPC; e += 4)
+                *reinterpret_cast<float4*>(dst + e) =
+                    make_float4(st.o[hh][e], st.o[hh][e + 1], st.o[hh][e + 2], st.o[hh][e + 3]);
         }
+        if (lane == 0)
+            *reinterpret_cast<float2*>(a.part_ml + prow * 2) = make_float2(st.m[hh], st.l[hh]);
+    }
+}
+
+template <bool BF16, int D, int G>
+__device__ __forceinline__ void zero_rows(const DecodeArgs& a, int s, int h) {
+    const int lane = threadIdx.x;
+    const int64_t row0 = ((int64_t)s * a.num_q_heads + h * G) * D;
+    if constexpr (BF16) {
+        uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + row0;
+        for (int e = lane; e < G * D; e += 64) o[e] = 0;
     } else {
+        float* o = reinterpret_cast<float*>(a.out) + row0;
+        for (int e = lane; e < G * D; e += 64) o[e] = 0.f;
+    }
+}
+
+// --------------------------------------------------------------------------------------
+// balanced split
+// --------------------------------------------------------------------------------------
+__device__ __forceinline__ int wave_sum_int(int x) {
+    x += (int)__builtin_amdgcn_update_dpp(0u, (uint32_t)x, 0x128, 0xF, 0xF, false);
+    x += (int)__builtin_amdgcn_update_dpp(0u, (uint32_t)x, 0x124, 0xF, 0xF, false);
+    x += (int)__builtin_amdgcn_update_dpp(0u, (uint32_t)x, 0x122, 0xF, 0xF, false);
+    x += (int)__builtin_amdgcn_update_dpp(0u, (uint32_t)x, 0x121, 0xF, 0xF, false);
+    auto r = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+    x = (int)(r[0] + r[1]);
+    auto q = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+    // every lane holds the total; readfirstlane tells the compiler it is uniform
+    return __builtin_amdgcn_readfirstlane((int)(q[0] + q[1]));
+}
+
+// Tiles of the whole batch (all sequences, one kv head) and tiles before sequence `upto`.
+__device__ __forceinline__ void count_tiles(const DecodeArgs& a, int upto, int64_t& total,
+                                            int64_t& before) {
+    const int lane = threadIdx.x;
+    total = 0;
+    before = 0;
+    for (int c0 = 0; c0 < a.num_seqs; c0 += 64) {
+        const int sl = c0 + lane;
+        const int nt = sl < a.num_seqs ? ntiles_of(clamp_ctx(a, a.context_lens[sl])) : 0;
+        total += wave_sum_int(nt);
+        before += wave_sum_int(sl < upto ? nt : 0);
+    }
+}
+
+// Wave owning unit u when T units are split into W ranges [floor(wT/W), floor((w+1)T/W)).
+__device__ __forceinline__ int64_t unit_owner(int64_t u, int64_t T, int64_t W) {
+    return ((u + 1) * W - 1) / T;
+}
+
+template <bool BF16, int D, int G>
+__global__ __launch_bounds__(64, (BF16 ? 2 : 1)) void decode_balanced_kernel(DecodeArgs a) {
+    using S = DecodeShape<BF16, D>;
+    __shared__ __attribute__((aligned(16))) char lds_k[kTile * S::KPITCH];
+    __shared__ __attribute__((aligned(16))) uint32_t lds_p[DecodeLds<BF16>::PWORDS];
+    __shared__ __attribute__((aligned(16))) uint32_t lds_q[G * S::RB / 4];
+
+    const int lane = threadIdx.x;
+    const int64_t w = blockIdx.x;
+    const int Hkv = a.g.num_kv_heads;
+
+    // units = 64-token tiles, ordered by (sequence, kv head, tile); with W <= T every
+    // wave's range [wT/W, (w+1)T/W) is non-empty
+    int64_t tiles_all, unused;
+    count_tiles(a, 0, tiles_all, unused);
+    const int64_t T = tiles_all * Hkv;
+    const int64_t W = min((int64_t)a.num_waves, T);
+    if (w >= W) return;
+    const int64_t b = w * T / W, e = (w + 1) * T / W;
+
+    // locate the sequence holding unit b: first s with Hkv * (tiles up to s) > b
+    int s = 0;
+    int64_t before = 0;
+    {
+        int64_t carry = 0;
+        for (int c0 = 0; c0 < a.num_seqs; c0 += 64) {
+            const int sl = c0 + lane;
+            const int nt = sl < a.num_seqs ? ntiles_of(clamp_ctx(a, a.context_lens[sl])) : 0;
+            int incl = nt;
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-            const int64_t prow = ((int64_t)s * Hq + hq0 + hh) * a.num_parts + part;
-            if (ra == 0) {
-                float* dst = a.part_o + prow * D + rc * S::EPC;
-#pragma unroll
-                for (int e = 0; e < S::EPC; e += 4)
-                    *reinterpret_cast<float4*>(dst + e) =
-                        make_float4(o[hh][e], o[hh][e + 1], o[hh][e + 2], o[hh][e + 3]);
+            for (int d = 1; d < 64; d <<= 1) {
+                const int y = __shfl_up(incl, d);
+                if (lane >= d) incl += y;
             }
-            if (lane == 0)
-                *reinterpret_cast<float2*>(a.part_ml + prow * 2) = make_float2(m[hh], l[hh]);
+            const uint64_t hit = __ballot((carry + incl) * Hkv > b);
+            if (hit) {
+                const int ln = __ffsll((unsigned long long)hit) - 1;
+                s = c0 + ln;
+                // readlane with a uniform lane: the compiler then knows the value is uniform
+                before = carry + __builtin_amdgcn_readlane(incl - nt, ln);
+                break;
+            }
+            carry += __builtin_amdgcn_readlane(incl, 63);
         }
     }
+    int nt_s = ntiles_of(clamp_ctx(a, a.context_lens[s]));
+    const int64_t rel = b - before * Hkv;
+    int h = (int)(rel / nt_s);
+    int tile = (int)(rel - (int64_t)h * nt_s);
+    int64_t remaining = e - b;
+    bool first = true;
+    SegState<BF16, D, G> st;
+    while (remaining > 0) {
+        const int seg = (int)min((int64_t)(nt_s - tile), remaining);
+        const bool last = seg == remaining;
+        const int ctx = clamp_ctx(a, a.context_lens[s]);
+        attend_segment<BF16, D, G>(a, s, h, ctx, tile * kTile, min(ctx, (tile + seg) * kTile),
+                                   lds_k, lds_p, lds_q, st);
+        if (tile == 0 && seg == nt_s) {
+            write_rows<BF16, D, G>(a, s, h, st);
+        } else {
+            if (first) write_partial<BF16, D, G>(a, (w * 2 + 0) * G, 1, st);
+            if (last) write_partial<BF16, D, G>(a, (w * 2 + 1) * G, 1, st);
+        }
+        remaining -= seg;
+        first = false;
+        if (remaining > 0) {
+            tile = 0;
+            if (++h == Hkv) {
+                h = 0;
+                do {
+                    ++s;
+                    nt_s = ntiles_of(clamp_ctx(a, a.context_lens[s]));
+                } while (nt_s == 0);
+            }
+        }
+    }
+}
+
+// Merge the pieces of each (sequence, kv head) that straddles waves, one wave per
+// query head; write zero rows for empty contexts.  The first covering wave holds
+// its piece in its last slot, every later covering wave in its first slot.
+template <bool BF16, int D, int G>
+__global__ __launch_bounds__(64) void decode_balanced_merge_kernel(DecodeArgs a) {
+    constexpr int PER = D / 64;
+    const int lane = threadIdx.x;
+    const int Hkv = a.g.num_kv_heads;
+    const int s = blockIdx.x / a.num_q_heads;
+    const int hq = blockIdx.x - s * a.num_q_heads;
+    const int h = hq / G, hh = hq - h * G;
+    int64_t tiles_all, before;
+    count_tiles(a, s, tiles_all, before);
+    const int nt = ntiles_of(clamp_ctx(a, a.context_lens[s]));
+    const int64_t o = ((int64_t)s * a.num_q_heads + hq) * D + lane * PER;
+    if (nt == 0) {
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            if constexpr (BF16)
+                reinterpret_cast<uint16_t*>(a.out)[o + k] = 0;
+            else
+                reinterpret_cast<float*>(a.out)[o + k] = 0.f;
+        }
+        return;
+    }
+    const int64_t T = tiles_all * Hkv, W = min((int64_t)a.num_waves, T);
+    const int64_t u0 = before * Hkv + (int64_t)h * nt;
+    const int64_t w0 = unit_owner(u0, T, W), w1 = unit_owner(u0 + nt - 1, T, W);
+    if (w0 == w1) return;  // finished by one wave
+    const int npieces = (int)(w1 - w0 + 1);
+    auto slot_row = [&](int p) -> int64_t { return ((w0 + p) * 2 + (p == 0 ? 1 : 0)) * G + hh; };
+    float M = kNoMax;
+    for (int p = lane; p < npieces; p += 64) M = fmaxf(M, a.part_ml[slot_row(p) * 2]);
+    M = wave_max(M);
+    float L = 0.f;
+    for (int p = lane; p < npieces; p += 64) {
+        const int64_t r = slot_row(p);
+        L += fast_exp2(a.part_ml[r * 2] - M) * a.part_ml[r * 2 + 1];
+    }
+    L = wave_sum(L);
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    float acc[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) acc[k] = 0.f;
+#pragma unroll 8
+    for (int p = 0; p < npieces; ++p) {
+        const int64_t r = slot_row(p);
+        const float wgt = fast_exp2(a.part_ml[r * 2] - M);
+#pragma unroll
+        for (int k = 0; k < PER; ++k) acc[k] = fmaf(wgt, a.part_o[r * D + lane * PER + k], acc[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        if constexpr (BF16)
+            reinterpret_cast<uint16_t*>(a.out)[o + k] = f32_to_bf16(acc[k] * inv);
+        else
+            reinterpret_cast<float*>(a.out)[o + k] = acc[k] * inv;
+    }
+}
+
+// --------------------------------------------------------------------------------------
+// fixed partitions of part_tokens positions
+// --------------------------------------------------------------------------------------
+template <bool BF16, int D, int G>
+__global__ __launch_bounds__(64, (BF16 ? 2 : 1)) void decode_partition_kernel(DecodeArgs a) {
+    using S = DecodeShape<BF16, D>;
+    __shared__ __attribute__((aligned(16))) char lds_k[kTile * S::KPITCH];
+    __shared__ __attribute__((aligned(16))) uint32_t lds_p[DecodeLds<BF16>::PWORDS];
+    __shared__ __attribute__((aligned(16))) uint32_t lds_q[G * S::RB / 4];
+
+    const int part = blockIdx.x;
+    const int sh = blockIdx.y;
+    const int s = sh / a.g.num_kv_heads;
+    const int h = sh - s * a.g.num_kv_heads;
+    const int ctx = clamp_ctx(a, a.context_lens[s]);
+    const int t_begin = part * a.part_tokens;
+    const bool single = a.num_parts == 1;
+    if (t_begin >= ctx) {
+        if (single) zero_rows<BF16, D, G>(a, s, h);
+        return;
+    }
+    SegState<BF16, D, G> st;
+    attend_segment<BF16, D, G>(a, s, h, ctx, t_begin, min(ctx, t_begin + a.part_tokens), lds_k,
+                               lds_p, lds_q, st);
+    if (single)
+        write_rows<BF16, D, G>(a, s, h, st);
+    else
+        write_partial<BF16, D, G>(a, ((int64_t)s * a.num_q_heads + h * G) * a.num_parts + part,
+                                  a.num_parts, st);
 }
 
 // Log-sum-exp merge of the partitions of one (sequence, q head):
 // with M the largest partition max, weight w_p = 2^(m_p - M);
 // out = sum_p w_p o_p / sum_p w_p l_p.  One wave per output row.
 template <bool BF16, int D>
-__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64) void decode_partition_merge_kernel(DecodeArgs a) {
     constexpr int PER = D / 64;
     const int row = blockIdx.x;
     const int s = row / a.num_q_heads;
     const int lane = threadIdx.x;
-    int ctx = a.context_lens[s];
-    ctx = max(0, min(ctx, min(a.max_context_len, a.max_blocks_per_seq * a.g.block_size)));
+    const int ctx = clamp_ctx(a, a.context_lens[s]);
     const int n = (ctx + a.part_tokens - 1) / a.part_tokens;
     const float* ml = a.part_ml + (int64_t)row * a.num_parts * 2;
     const float* po = a.part_o + (int64_t)row * a.num_parts * D;
@@ -279,6 +543,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
     float acc[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) acc[k] = 0.f;
+#pragma unroll 8
     for (int p = 0; p < n; ++p) {
         const float w = fast_exp2(ml[2 * p] - M);
 #pragma unroll
@@ -294,40 +559,92 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
     }
 }
 
+// --------------------------------------------------------------------------------------
+// host side
+// --------------------------------------------------------------------------------------
 template <bool BF16, int D, int G>
-static hipError_t launch_decode_t(const DecodeArgs& a, int num_seqs, hipStream_t st) {
-    const dim3 grid(a.num_parts, num_seqs * a.g.num_kv_heads);
-    hipLaunchKernelGGL((decode_partial_kernel<BF16, D, G>), grid, dim3(64), 0, st, a);
-    if (a.num_parts > 1)
-        hipLaunchKernelGGL((decode_merge_kernel<BF16, D>), dim3(num_seqs * a.num_q_heads), dim3(64),
-                           0, st, a);
+static int balanced_waves_t() {
+    // resident waves of the balanced kernel on the current device, cached per device
+    static std::mutex mu;
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cache[dev] == 0) {
+        int per_cu = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &per_cu, reinterpret_cast<const void*>(decode_balanced_kernel<BF16, D, G>), 64, 0) !=
+                hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        cache[dev] = max(1, per_cu) * max(1, cus);
+    }
+    return cache[dev];
+}
+
+template <bool BF16, int D, int G>
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
+    const int S = a.num_seqs;
+    if (a.part_tokens > 0) {
+        const dim3 grid(a.num_parts, S * a.g.num_kv_heads);
+        hipLaunchKernelGGL((decode_partition_kernel<BF16, D, G>), grid, dim3(64), 0, st, a);
+        if (a.num_parts > 1)
+            hipLaunchKernelGGL((decode_partition_merge_kernel<BF16, D>), dim3(S * a.num_q_heads),
+                               dim3(64), 0, st, a);
+    } else {
+        hipLaunchKernelGGL((decode_balanced_kernel<BF16, D, G>), dim3(a.num_waves), dim3(64), 0, st,
+                           a);
+        hipLaunchKernelGGL((decode_balanced_merge_kernel<BF16, D, G>), dim3(S * a.num_q_heads),
+                           dim3(64), 0, st, a);
+    }
     return hipGetLastError();
 }
 
-template <bool BF16, int D>
-static hipError_t launch_decode_g(const DecodeArgs& a, int group, int num_seqs, hipStream_t st) {
-    switch (group) {
-        case 1: return launch_decode_t<BF16, D, 1>(a, num_seqs, st);
-        case 2: return launch_decode_t<BF16, D, 2>(a, num_seqs, st);
-        case 3: return launch_decode_t<BF16, D, 3>(a, num_seqs, st);
-        case 4: return launch_decode_t<BF16, D, 4>(a, num_seqs, st);
-        case 5: return launch_decode_t<BF16, D, 5>(a, num_seqs, st);
-        case 6: return launch_decode_t<BF16, D, 6>(a, num_seqs, st);
-        case 7: return launch_decode_t<BF16, D, 7>(a, num_seqs, st);
-        case 8: return launch_decode_t<BF16, D, 8>(a, num_seqs, st);
-        default: return hipErrorInvalidValue;
+#define PKV_DISPATCH_G(FN, BF, DD, group, ...)     \
+    switch (group) {                               \
+        case 1: return FN<BF, DD, 1>(__VA_ARGS__); \
+        case 2: return FN<BF, DD, 2>(__VA_ARGS__); \
+        case 3: return FN<BF, DD, 3>(__VA_ARGS__); \
+        case 4: return FN<BF, DD, 4>(__VA_ARGS__); \
+        case 5: return FN<BF, DD, 5>(__VA_ARGS__); \
+        case 6: return FN<BF, DD, 6>(__VA_ARGS__); \
+        case 7: return FN<BF, DD, 7>(__VA_ARGS__); \
+        case 8: return FN<BF, DD, 8>(__VA_ARGS__); \
+        default: break;                            \
     }
+
+template <bool BF16, int D>
+static hipError_t launch_decode_g(const DecodeArgs& a, int group, hipStream_t st) {
+    PKV_DISPATCH_G(launch_decode_t, BF16, D, group, a, st)
+    return hipErrorInvalidValue;
+}
+
+template <bool BF16, int D>
+static int balanced_waves_g(int group) {
+    PKV_DISPATCH_G(balanced_waves_t, BF16, D, group)
+    return 0;
+}
+
+int decode_balanced_waves(bool is_bf16, int head_dim, int group) {
+    if (is_bf16) {
+        if (head_dim == 128) return balanced_waves_g<true, 128>(group);
+        if (head_dim == 64) return balanced_waves_g<true, 64>(group);
+    } else {
+        if (head_dim == 128) return balanced_waves_g<false, 128>(group);
+        if (head_dim == 64) return balanced_waves_g<false, 64>(group);
+    }
+    return 0;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, bool is_bf16, int head_dim, int group, int num_seqs,
                          hipStream_t st) {
     if (num_seqs == 0) return hipSuccess;
     if (is_bf16) {
-        if (head_dim == 128) return launch_decode_g<true, 128>(a, group, num_seqs, st);
-        if (head_dim == 64) return launch_decode_g<true, 64>(a, group, num_seqs, st);
+        if (head_dim == 128) return launch_decode_g<true, 128>(a, group, st);
+        if (head_dim == 64) return launch_decode_g<true, 64>(a, group, st);
     } else {
-        if (head_dim == 128) return launch_decode_g<false, 128>(a, group, num_seqs, st);
-        if (head_dim == 64) return launch_decode_g<false, 64>(a, group, num_seqs, st);
+        if (head_dim == 128) return launch_decode_g<false, 128>(a, group, st);
+        if (head_dim == 64) return launch_decode_g<false, 64>(a, group, st);
     }
     return hipErrorInvalidValue;
 }

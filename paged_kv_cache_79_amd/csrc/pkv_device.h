@@ -13,6 +13,9 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
+// Native vector types (first-class LLVM values, kept in registers even when loop-carried).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // A finite stand-in for "no score seen yet": exp2(x - kNoMax) never overflows for
 // real scores, and exp2(-inf - m) is 0 for every finite running max m.
@@ -85,6 +88,19 @@ using const_ptr = const __attribute__((address_space(4))) T*;
 template <typename T>
 __device__ __forceinline__ const_ptr<T> as_const(const T* p) {
     return (const_ptr<T>)p;
+}
+
+// A wave-uniform global pointer pinned to scalar registers.  Loads of
+// (pinned + 32-bit per-lane offset) then use the scalar-base addressing form
+// instead of a 64-bit per-lane address that the compiler would otherwise build by
+// re-associating the sum.
+template <typename T>
+using global_ptr = const __attribute__((address_space(1))) T*;
+__device__ __forceinline__ global_ptr<char> pin_uniform(const char* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (global_ptr<char>)(((uint64_t)hi << 32) | lo);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -41,16 +41,24 @@ struct DecodeArgs {
     const char* v_pool;
     const int32_t* block_tables;
     const int32_t* context_lens;
-    float* part_o;       // [S][Hq][num_parts][D]   unnormalised partial outputs
-    float* part_ml;      // [S][Hq][num_parts][2]   (running max in log2 units, sum)
+    // Partial softmax states.  Fixed partitions: [S][Hq][num_parts][D] and
+    // [S][Hq][num_parts][2].  Balanced split: [num_waves][2 slots][G][D] and
+    // [num_waves][2][G][2].  (max in log2 units, sum of exponentials)
+    float* part_o;
+    float* part_ml;
     PoolGeom g;
+    int32_t num_seqs;
     int32_t num_q_heads;
     int32_t max_blocks_per_seq;
     int32_t max_context_len;
-    int32_t part_tokens;
-    int32_t num_parts;
-    float scale_log2;    // scale * log2(e)
+    int32_t part_tokens;   // fixed partitions (> 0), or 0 for the balanced split
+    int32_t num_parts;     // fixed partitions per sequence (grid.x)
+    int32_t num_waves;     // balanced split: persistent waves (grid.x)
+    float scale_log2;      // scale * log2(e)
 };
+
+// Persistent waves the balanced decode launches on the current device.
+int decode_balanced_waves(bool is_bf16, int head_dim, int group);
 
 struct PrefillArgs {
     void* out;

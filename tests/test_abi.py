@@ -97,17 +97,21 @@ def test_decode_validation(lib):
     assert decode(lib, S=0, ptr=None) == OK
     # a context that needs several partitions requires a workspace
     need = lib.paged_attention_decode_workspace_bytes(2, 8, 2, 128, 4096, 256)
-    assert need == 2 * 8 * 16 * 130 * 4
     assert decode(lib, maxctx=4096, mb=256, pt=256) == WS
     assert decode(lib, maxctx=4096, mb=256, pt=256, ws=P, wsb=need - 1) == WS
-    assert lib.paged_attention_decode_workspace_bytes(2, 8, 2, 128, 200, 256) == 0
+    # the balanced split always needs one
+    assert decode(lib, maxctx=64, mb=4, pt=0) == WS
 
 
-def test_partition_choice(lib):
-    f = lib.paged_attention_decode_partition_tokens
-    for args in [(64, 8, 4096), (8, 4, 200000), (1, 1, 10), (256, 8, 2560)]:
-        pt = f(*args)
-        assert pt >= 256 and pt % 64 == 0
+def test_workspace_sizes(lib):
+    f = lib.paged_attention_decode_workspace_bytes
+    # fixed partitions: S * Hq * parts * (D + 2) floats, none when one partition suffices
+    assert f(2, 8, 2, 128, 4096, 256) == 2 * 8 * 16 * 130 * 4
+    assert f(2, 8, 2, 128, 200, 256) == 0
+    # balanced split: two partial slots of G heads per resident wave (8 per CU)
+    b = f(2, 8, 2, 128, 4096, 0)
+    assert b > 0 and b % (2 * 4 * 130 * 4) == 0
+    assert f(0, 8, 2, 128, 4096, 0) == 0
 
 
 @dummy_ptrs
