@@ -54,6 +54,20 @@ def prefill_flops(pre) -> int:
     return int(4 * pre.head_dim * pre.num_q_heads * tot)
 
 
+def recorded_traffic(workload_name):
+    """Counter-derived HBM bytes per decode call, as recorded under profiles/ with the
+    hash of the decode source they were measured on; None when absent or stale."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"decode_{workload_name.replace('_decode', '')}_traffic.json")
+    src = os.path.join(ROOT, "paged_kv_cache_79_amd", "csrc", "pkv_decode.hip")
+    try:
+        rec = json.load(open(path))
+        cur = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    return rec["traffic_bytes_per_call"] if rec.get("decode_source_sha256") == cur else None
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -226,7 +240,8 @@ def run(args):
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "kv_bytes_per_step": byts,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(b.name) if pt == 0 else None,
                      "kernel": "paged_attention_decode (attention kernel + merge kernel)",
                      "avg_us": round(dec_avg * 1e3, 2),
                      "runs_us": [round(x * 1e3, 2) for x in dec_runs]},
