@@ -29,8 +29,8 @@
  *  - A context length counts every token visible to the step's queries,
  *    including the ones written in this step.
  *  - Supported: head_dim in {64, 128}; block_size in {4, 8, 16, 32} with
- *    block_size * head_dim * element size >= 1024 bytes;
- *    num_q_heads / num_kv_heads in 1..8.
+ *    block_size * head_dim * element size >= 1024 bytes; one pool block
+ *    (all kv heads) smaller than 2 GiB; num_q_heads / num_kv_heads in 1..8.
  *  - Host-checkable arguments are validated before anything is enqueued; a
  *    non-zero status means nothing was launched.  Device-resident contents
  *    (block ids, slots, lengths) are not validated; out-of-range block ids

@@ -38,6 +38,8 @@ pkv_status check_geom(pkv_dtype dt, int32_t num_blocks, int32_t num_kv_heads, in
     g->row_bytes = head_dim * eb;
     g->head_stride_bytes = block_size * head_dim * eb;
     g->block_stride_bytes = (int64_t)num_kv_heads * g->head_stride_bytes;
+    // kernels form block offsets as 32 x 32 -> 64-bit products
+    if (g->block_stride_bytes >= ((int64_t)1 << 31)) return PKV_ERR_UNSUPPORTED;
     g->num_blocks = num_blocks;
     g->num_kv_heads = num_kv_heads;
     g->block_size = block_size;

@@ -11,6 +11,7 @@ namespace pkv {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 // Native vector types (first-class LLVM values, kept in registers even when loop-carried).
@@ -118,8 +119,9 @@ __device__ __forceinline__ float bf16hi(uint32_t w) { return u2f(w & 0xFFFF0000u
 __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
     return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
+// Two floats -> packed bf16 pair (lo in bits 0-15), one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t){lo, hi}, bf16x2_t));
 }
 
 // Byte permutes pairing the same half of two dwords: (a.lo, b.lo) and (a.hi, b.hi).

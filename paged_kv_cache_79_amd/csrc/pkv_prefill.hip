@@ -8,16 +8,23 @@
 // ("2.1 PagedAttention", sections 3 and 5).
 //
 // Mapping: one workgroup (4 waves) owns 128 packed query rows of one
-// (chunk, kv head): row r = (query r / G, head r % G) of the G query heads
-// that share the kv head, so every K/V tile is loaded once for all G heads.
-// Per 64-key tile:
+// (chunk, kv head): row r = (query r / G, head r % G) of the G query heads that
+// share the kv head, so every K/V tile is loaded once for all G heads.  Per
+// 64-key tile:
 //   S^T = K Q^T       v_mfma_f32_32x32x16_bf16, A = K rows from LDS, B = Q rows
 //                     held in registers; the C layout gives each lane one query
-//                     row (column) and 16 keys per 32-key block, so the
-//                     row-wise softmax is lane-local plus one permlane32 swap;
+//                     row (column) and 16 keys per 32-key block, so the row-wise
+//                     softmax is lane-local plus one permlane32 swap;
 //   O^T += V^T P^T    A = V^T from LDS (stored transposed, keys in the order in
 //                     which the C registers of S^T hold them), B = bf16 P^T
 //                     straight from those registers.
+// Software pipeline: while the matrix cores work on tile j from LDS, the K/V
+// global loads of tile j+1 are in flight (their block ids were fetched during
+// tile j-1) and the block ids of tile j+2 are being fetched; tile j+1 lands in
+// LDS after tile j's products.  V is written transposed with a 16-byte XOR
+// swizzle so that the transposing writes meet fewer LDS bank conflicts while the
+// operand reads stay conflict-free.  Workgroups are ordered so that all query
+// tiles of one (chunk, kv head) run on the same XCD and share its L2.
 // Keys past the context are zero in LDS and masked to -inf, so stale or NaN
 // slots never reach the matrix cores.
 #include "pkv_device.h"
@@ -27,15 +34,18 @@ namespace pkv {
 
 constexpr int kRowsPerWg = 128;   // packed (query, head) rows per workgroup
 constexpr int kKeyTile = 64;      // keys per tile
+constexpr int kXcds = 8;          // MI355X: workgroups are dealt round-robin to 8 XCDs
 
 template <int D>
 struct PrefillShape {
-    static constexpr int RB = D * 2;             // bytes of a K/V row (bf16)
-    static constexpr int CPR = RB / 16;          // 16-byte chunks per row
-    static constexpr int KPITCH = RB + 16;       // K tile row pitch in LDS (bytes)
-    static constexpr int VPITCH = kKeyTile * 2 + 16;  // V^T row pitch in LDS (bytes)
-    static constexpr int KSTEPS = D / 16;        // QK k-steps of 16
-    static constexpr int DT = D / 32;            // 32-row output tiles
+    static constexpr int RB = D * 2;                  // bytes of a K/V row (bf16)
+    static constexpr int CPR = RB / 16;               // 16-byte chunks per row
+    static constexpr int KPITCH = RB + 16;            // K tile row pitch in LDS (bytes)
+    static constexpr int VPITCH = kKeyTile * 2 + 16;  // V^T row pitch in LDS (bytes): 36 dwords
+    static constexpr int KSTEPS = D / 16;             // QK k-steps of 16
+    static constexpr int DT = D / 32;                 // 32-row output tiles
+    static constexpr int KLOADS = kKeyTile * CPR / 256;   // K chunks per thread per tile
+    static constexpr int VLOADS = CPR / 8;            // V chunk pairs per thread per tile
 };
 
 // Position of key k (0..63) inside the transposed V tile.  Within a group of 16
@@ -46,18 +56,129 @@ __device__ __forceinline__ int vt_slot(int k) {
     return (k & ~0xC) | ((k & 4) << 1) | ((k & 8) >> 1);
 }
 
+// Byte offset of 16-byte group g (8 key slots) of V^T row d: groups are XOR-swizzled
+// by d / 8 so that rows 8 apart never share banks.
+template <int D>
+__device__ __forceinline__ int vt_off(int d, int g) {
+    return d * PrefillShape<D>::VPITCH + ((g ^ ((d >> 3) & 7)) << 4);
+}
+
+// Thread t loads K rows t / CPR + (256 / CPR) i (whole rows per wave) and the V
+// rows of key pair t / 8, chunks t % 8 + 8 j (half rows per lane).
+template <int D>
+__device__ __forceinline__ int k_row(int i, int tid) {
+    using P = PrefillShape<D>;
+    return i * (256 / P::CPR) + tid / P::CPR;
+}
+
+template <int D>
+struct KvStage {
+    u32x4 k[PrefillShape<D>::KLOADS];
+    u32x4 v[2 * PrefillShape<D>::VLOADS];
+};
+
+// Physical block ids behind the rows one thread loads from a tile.
+template <int D>
+struct TileIds {
+    int k[PrefillShape<D>::KLOADS];
+    int v[2];
+};
+
+// Block ids for the tile starting at t0.  Rows past the context are clamped to its
+// last token (their data is replaced by zeros when loaded), so every table read
+// stays inside the sequence's used blocks.
+template <int D>
+__device__ __forceinline__ void load_ids(TileIds<D>& ids, const int32_t* table, int log2_bs,
+                                         int ctx, int t0, int tid) {
+    using P = PrefillShape<D>;
+#pragma unroll
+    for (int i = 0; i < P::KLOADS; ++i)
+        ids.k[i] = table[min(t0 + k_row<D>(i, tid), ctx - 1) >> log2_bs];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+        ids.v[r] = table[min(t0 + 2 * (tid >> 3) + r, ctx - 1) >> log2_bs];
+}
+
+template <int D>
+__device__ __forceinline__ const u32x4* row_chunk(const char* base, int pb, int tok, int chunk,
+                                                  const PrefillArgs& a) {
+    const uint32_t ub = ((unsigned)pb < (unsigned)a.g.num_blocks) ? pb : 0;   // never a bad id
+    return reinterpret_cast<const u32x4*>(
+        base + (uint64_t)ub * (uint32_t)a.g.block_stride_bytes +
+        (uint32_t)((tok & (a.g.block_size - 1)) * PrefillShape<D>::RB + chunk * 16));
+}
+
+// Global loads of the 64-key tile starting at t0; keys >= ctx read as zero.
+template <int D>
+__device__ __forceinline__ void load_tile(KvStage<D>& st, const TileIds<D>& ids,
+                                          const PrefillArgs& a, const char* kb, const char* vb,
+                                          int ctx, int t0, int tid) {
+    using P = PrefillShape<D>;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < P::KLOADS; ++i) {
+        const int tok = t0 + k_row<D>(i, tid);
+        const u32x4 x = __builtin_nontemporal_load(
+            row_chunk<D>(kb, ids.k[i], min(tok, ctx - 1), tid % P::CPR, a));
+        st.k[i] = tok < ctx ? x : zero;
+    }
+    const int kp = tid >> 3, c0 = tid & 7;
+#pragma unroll
+    for (int j = 0; j < P::VLOADS; ++j)
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int tok = t0 + 2 * kp + r;
+            const u32x4 x = __builtin_nontemporal_load(
+                row_chunk<D>(vb, ids.v[r], min(tok, ctx - 1), c0 + 8 * j, a));
+            st.v[2 * j + r] = tok < ctx ? x : zero;
+        }
+}
+
+// Staged tile -> LDS: K rows as they are, V transposed (pairs of keys per dword).
+template <int D>
+__device__ __forceinline__ void store_tile(const KvStage<D>& st, char* lds_k, char* lds_vt, int tid) {
+    using P = PrefillShape<D>;
+#pragma unroll
+    for (int i = 0; i < P::KLOADS; ++i)
+        *reinterpret_cast<u32x4*>(lds_k + k_row<D>(i, tid) * P::KPITCH + (tid % P::CPR) * 16) =
+            st.k[i];
+    const int kp = tid >> 3, c0 = tid & 7;
+    const int slot = vt_slot(2 * kp);           // even: keys 2kp, 2kp+1 share one dword
+    const int g = slot >> 3, within = (slot & 7) * 2;
+#pragma unroll
+    for (int j = 0; j < P::VLOADS; ++j) {
+        const u32x4 x0 = st.v[2 * j], x1 = st.v[2 * j + 1];
+        const uint32_t a0[4] = {x0.x, x0.y, x0.z, x0.w};
+        const uint32_t a1[4] = {x1.x, x1.y, x1.z, x1.w};
+        const int dbase = (c0 + 8 * j) * 8;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int d = dbase + 2 * q;
+            *reinterpret_cast<uint32_t*>(lds_vt + vt_off<D>(d, g) + within) = pair_lo(a0[q], a1[q]);
+            *reinterpret_cast<uint32_t*>(lds_vt + vt_off<D>(d + 1, g) + within) = pair_hi(a0[q], a1[q]);
+        }
+    }
+}
+
 template <int D, int G>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, int num_q_tiles,
+                                                         int num_items) {
     using P = PrefillShape<D>;
     constexpr int QP = kRowsPerWg / G;           // query positions per workgroup
     __shared__ __attribute__((aligned(16))) char lds_k[kKeyTile * P::KPITCH];
     __shared__ __attribute__((aligned(16))) char lds_vt[D * P::VPITCH];
 
-    const int qt = blockIdx.x;
-    const int h = blockIdx.y;
-    const int c = blockIdx.z;
+    // XCD-aware order: consecutive work items (the query tiles of one (chunk, kv head))
+    // get workgroup ids that are equal modulo the XCD count.
+    const int nwg = gridDim.x;
+    const int item = (blockIdx.x % kXcds) * (nwg / kXcds) + blockIdx.x / kXcds;
+    if (item >= num_items) return;
+    const int qt = item % num_q_tiles;
+    const int h = (item / num_q_tiles) % a.g.num_kv_heads;
+    const int c = item / (num_q_tiles * a.g.num_kv_heads);
+
     const int tid = threadIdx.x;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
     const int lane = tid & 63;
     const int n = lane & 31;
     const int half = lane >> 5;
@@ -70,7 +191,6 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     int ctx = as_const(a.context_lens)[c];
     ctx = max(0, min(ctx, min(a.max_context_len, mb * bs)));
     if (qt * QP >= nq || nq > ctx) return;
-    const int nblk = (ctx + bs - 1) >> a.g.log2_bs;
     const int32_t* table = a.block_tables + (int64_t)c * mb;
     const char* kb = a.k_pool + (int64_t)h * a.g.head_stride_bytes;
     const char* vb = a.v_pool + (int64_t)h * a.g.head_stride_bytes;
@@ -81,84 +201,49 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     const int hh = r - qi * G;
     const int qpos_local = qt * QP + qi;
     const bool row_valid = (r < QP * G) && (qpos_local < nq);
-    const int pos = ctx - nq + qpos_local;       // causal limit (inclusive)
     const int64_t qidx = (int64_t)q0 + qpos_local;
+    // last key the row sees (causal limit); -1 hides every key from rows past the chunk
+    const int last_key = row_valid ? ctx - nq + qpos_local : -1;
 
-    uint4 qreg[P::KSTEPS];
+    u32x4 qreg[P::KSTEPS];
     {
         const char* qp = reinterpret_cast<const char*>(a.q) +
                          (qidx * Hq + (int64_t)h * G + hh) * P::RB + half * 16;
 #pragma unroll
         for (int ks = 0; ks < P::KSTEPS; ++ks)
-            qreg[ks] = row_valid ? *reinterpret_cast<const uint4*>(qp + ks * 32)
-                                 : make_uint4(0, 0, 0, 0);
+            qreg[ks] = row_valid ? *reinterpret_cast<const u32x4*>(qp + ks * 32)
+                                 : u32x4{0u, 0u, 0u, 0u};
     }
+    // Every row of the wave sees all keys below full_end: the smallest position
+    // among its rows bounds them.  Rows past the chunk then compute on zero queries
+    // and are never stored; each output column depends on its own row only.
+    const int full_end = min(ctx - nq + qt * QP + (w * 32) / G + 1, ctx);
 
     floatx16_t oacc[P::DT];
 #pragma unroll
     for (int dt = 0; dt < P::DT; ++dt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[dt][e] = 0.f;
-    float m = kNoMax, l = 0.f;
+    float m = kNoMax, l = 0.f;           // running max (log2 units) and sum of the row
+    const float sl2 = a.scale_log2;
 
     // keys any row of this workgroup may see
     const int t_stop = ctx - nq + min(nq, (qt + 1) * QP);
 
+    KvStage<D> stage;
+    TileIds<D> ids;
+    load_ids<D>(ids, table, a.g.log2_bs, ctx, 0, tid);
+    load_tile<D>(stage, ids, a, kb, vb, ctx, 0, tid);
+    load_ids<D>(ids, table, a.g.log2_bs, ctx, kKeyTile, tid);
+    store_tile<D>(stage, lds_k, lds_vt, tid);
+    __syncthreads();
+
     for (int t0 = 0; t0 < t_stop; t0 += kKeyTile) {
-        // ---- K tile, natural row layout --------------------------------------
-        {
-            constexpr int RPI = 256 / P::CPR;    // rows per pass of the workgroup
-            const int cr = tid % P::CPR;
-#pragma unroll
-            for (int i = 0; i < kKeyTile / RPI; ++i) {
-                const int row = i * RPI + tid / P::CPR;
-                const int tok = t0 + row;
-                uint4 x = make_uint4(0, 0, 0, 0);
-                if (tok < ctx) {
-                    int pb = table[min(tok >> a.g.log2_bs, nblk - 1)];
-                    pb = ((unsigned)pb < (unsigned)a.g.num_blocks) ? pb : 0;
-                    x = *reinterpret_cast<const uint4*>(
-                        kb + (int64_t)pb * a.g.block_stride_bytes +
-                        (uint32_t)((tok & (bs - 1)) * P::RB + cr * 16));
-                }
-                *reinterpret_cast<uint4*>(lds_k + row * P::KPITCH + cr * 16) = x;
-            }
+        const bool more = t0 + kKeyTile < t_stop;
+        if (more) {
+            load_tile<D>(stage, ids, a, kb, vb, ctx, t0 + kKeyTile, tid);
+            load_ids<D>(ids, table, a.g.log2_bs, ctx, t0 + 2 * kKeyTile, tid);
         }
-        // ---- V tile, transposed: lds_vt[d][slot(key)] -------------------------
-        {
-            const int kp = tid & 31;             // key pair 2kp, 2kp+1
-            const int cg = tid >> 5;             // chunk group
-#pragma unroll
-            for (int j = 0; j < P::CPR / 8; ++j) {
-                const int ch = cg + 8 * j;
-                uint4 x0 = make_uint4(0, 0, 0, 0), x1 = make_uint4(0, 0, 0, 0);
-                const int tk = t0 + 2 * kp;
-                if (tk < ctx) {
-                    int pb = table[min(tk >> a.g.log2_bs, nblk - 1)];
-                    pb = ((unsigned)pb < (unsigned)a.g.num_blocks) ? pb : 0;
-                    x0 = *reinterpret_cast<const uint4*>(
-                        vb + (int64_t)pb * a.g.block_stride_bytes +
-                        (uint32_t)((tk & (bs - 1)) * P::RB + ch * 16));
-                }
-                if (tk + 1 < ctx) {
-                    int pb = table[min((tk + 1) >> a.g.log2_bs, nblk - 1)];
-                    pb = ((unsigned)pb < (unsigned)a.g.num_blocks) ? pb : 0;
-                    x1 = *reinterpret_cast<const uint4*>(
-                        vb + (int64_t)pb * a.g.block_stride_bytes +
-                        (uint32_t)(((tk + 1) & (bs - 1)) * P::RB + ch * 16));
-                }
-                const uint32_t a0[4] = {x0.x, x0.y, x0.z, x0.w};
-                const uint32_t a1[4] = {x1.x, x1.y, x1.z, x1.w};
-                const int col = vt_slot(2 * kp) * 2;   // byte offset in the row
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int d = ch * 8 + 2 * q;
-                    *reinterpret_cast<uint32_t*>(lds_vt + d * P::VPITCH + col) = pair_lo(a0[q], a1[q]);
-                    *reinterpret_cast<uint32_t*>(lds_vt + (d + 1) * P::VPITCH + col) = pair_hi(a0[q], a1[q]);
-                }
-            }
-        }
-        __syncthreads();
 
         // ---- S^T = K Q^T ----------------------------------------------------------
         floatx16_t sacc[2];
@@ -168,7 +253,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
             for (int e = 0; e < 16; ++e) sacc[mt][e] = 0.f;
 #pragma unroll
             for (int ks = 0; ks < P::KSTEPS; ++ks) {
-                const uint4 ka = *reinterpret_cast<const uint4*>(
+                const u32x4 ka = *reinterpret_cast<const u32x4*>(
                     lds_k + (mt * 32 + n) * P::KPITCH + ks * 32 + half * 16);
                 sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     __builtin_bit_cast(bf16x8_t, ka), __builtin_bit_cast(bf16x8_t, qreg[ks]),
@@ -176,56 +261,72 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
             }
         }
 
-        // ---- online softmax over this row's 32 keys per lane -------------------
-        float sc[2][16];
+        // ---- online softmax; lane holds keys t0 + 32mt + 8(e/4) + 4half + e%4 -----
+        // On unmasked tiles with a positive scale the max is taken on raw scores and
+        // the scale folds into the exponent's fma; otherwise scores are scaled first
+        // and hidden keys set to -inf.
+        const bool scaled = t0 + kKeyTile > full_end || !(sl2 > 0.f);   // wave-uniform
+        const float mul = scaled ? 1.f : sl2;
+        if (scaled) {
+            const int lim = last_key - t0 - 4 * half;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    sacc[mt][e] = (mt * 32 + 8 * (e >> 2) + (e & 3) <= lim) ? sacc[mt][e] * sl2
+                                                                            : -INFINITY;
+        }
         float mloc = -INFINITY;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int key = t0 + mt * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-                const bool vis = row_valid && key <= pos && key < ctx;
-                sc[mt][e] = vis ? sacc[mt][e] * a.scale_log2 : -INFINITY;
-                mloc = fmaxf(mloc, sc[mt][e]);
-            }
-        const float mn = fmaxf(m, swap32_max(mloc));
-        const float alpha = fast_exp2(m - mn);
+            for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, sacc[mt][e]);
+        const float mn = fmaxf(m, swap32_max(mloc) * mul);
+        // rescale the output only when some row of the wave raised its maximum
+        if (__builtin_amdgcn_ballot_w64(mn > m)) {
+            const float alpha = fast_exp2(m - mn);
+            l *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < P::DT; ++dt)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
+        }
         m = mn;
         float psum = 0.f;
-        uint4 pk[4];
+        u32x4 pk[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int mt = u >> 1, e0 = (u & 1) * 8;
             float p[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                p[j] = fast_exp2(sc[mt][e0 + j] - mn);
+                p[j] = fast_exp2(__builtin_fmaf(sacc[mt][e0 + j], mul, -mn));
                 psum += p[j];
             }
-            pk[u] = make_uint4(pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]),
-                               pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7]));
+            pk[u] = u32x4{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
+                          pack_bf16(p[6], p[7])};
         }
-        l = l * alpha + psum;
-#pragma unroll
-        for (int dt = 0; dt < P::DT; ++dt)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
+        l += psum;
 
         // ---- O^T += V^T P^T ---------------------------------------------------------
 #pragma unroll
         for (int dt = 0; dt < P::DT; ++dt)
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const uint4 va = *reinterpret_cast<const uint4*>(
-                    lds_vt + (dt * 32 + n) * P::VPITCH + (u * 16 + half * 8) * 2);
+                const u32x4 va = *reinterpret_cast<const u32x4*>(
+                    lds_vt + vt_off<D>(dt * 32 + n, 2 * u + half));
                 oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     __builtin_bit_cast(bf16x8_t, va), __builtin_bit_cast(bf16x8_t, pk[u]),
                     oacc[dt], 0, 0, 0);
             }
-        __syncthreads();
+        __syncthreads();                 // every wave is done with this tile's LDS
+        if (more) {
+            store_tile<D>(stage, lds_k, lds_vt, tid);
+            __syncthreads();
+        }
     }
 
-    // ---- normalise and store: lane holds d = 32dt + 8(e/4) + 4half + e%4 ----------
+    // ---- normalise and store: lane holds d = 32dt + 8(e/4) + 4half + e%4 ------------
     const float lt = swap32_sum(l);
     if (!row_valid) return;
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
@@ -246,8 +347,11 @@ template <int D, int G>
 static hipError_t launch_prefill_t(const PrefillArgs& a, int num_chunks, int max_q_len,
                                    hipStream_t st) {
     constexpr int QP = kRowsPerWg / G;
-    const dim3 grid((max_q_len + QP - 1) / QP, a.g.num_kv_heads, num_chunks);
-    hipLaunchKernelGGL((prefill_kernel<D, G>), grid, dim3(256), 0, st, a);
+    const int nqt = (max_q_len + QP - 1) / QP;
+    const int64_t items = (int64_t)nqt * a.g.num_kv_heads * num_chunks;
+    if (items > (int64_t)1 << 30) return hipErrorInvalidValue;
+    const int nwg = (int)((items + kXcds - 1) / kXcds * kXcds);   // a multiple of the XCD count
+    hipLaunchKernelGGL((prefill_kernel<D, G>), dim3(nwg), dim3(256), 0, st, a, nqt, (int)items);
     return hipGetLastError();
 }
 

@@ -75,6 +75,7 @@ def test_write_validation(lib):
     assert write(lib, bs=64) == UNSUP
     assert write(lib, bs=4, d=64) == UNSUP            # bf16 block run of 512 B < 1 KiB
     assert write(lib, nb=0) == SHAPE
+    assert write(lib, hkv=262144, bs=32) == UNSUP      # one pool block of 2 GiB (bf16)
     assert write(lib, T=-1) == SHAPE
     assert write(lib, ptr=None) == NULL
     assert write(lib, T=0, ptr=None) == OK             # nothing to do, nothing launched
