@@ -185,6 +185,7 @@ pkv_status paged_attention_decode(pkv_dtype dtype, void* out, const void* q, con
     a.part_tokens = partition_tokens;
     a.num_parts = 1;
     a.num_waves = 0;
+    a.lead_share_q10 = 512;
     a.part_o = static_cast<float*>(workspace);
     a.part_ml = nullptr;
     if (partition_tokens > 0) {
@@ -197,6 +198,8 @@ pkv_status paged_attention_decode(pkv_dtype dtype, void* out, const void* q, con
         int64_t waves = decode_balanced_waves(dtype == PKV_BF16, head_dim, group);
         if (waves <= 0) return PKV_ERR_LAUNCH;
         waves = std::min(waves, balanced_wave_bound());
+        // two waves per SIMD (the bf16 kernels fill every slot): lead waves get more tiles
+        if (waves == balanced_wave_bound()) a.lead_share_q10 = kLeadShareQ10;
         waves = std::max<int64_t>(1, std::min(waves, tiles_bound));
         a.num_waves = (int32_t)waves;
         a.part_ml = a.part_o + (size_t)waves * 2 * group * head_dim;

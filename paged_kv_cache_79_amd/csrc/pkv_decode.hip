@@ -25,8 +25,10 @@
 //
 // Work split.  By default (balanced split) a persistent grid of exactly as many
 // waves as the device keeps resident divides all tiles of the batch -- ordered
-// by (sequence, kv head, tile) -- into equal contiguous ranges, so every wave
-// streams the same number of bytes whatever the mix of context lengths.  A
+// by (sequence, kv head, tile) -- into contiguous ranges, so that the work per
+// wave does not depend on the mix of context lengths.  When two waves share each
+// SIMD, the first-dispatched half of the grid runs faster (it wins issue
+// arbitration), so that half gets a fixed larger share of the tiles.  A
 // (sequence, kv head) that lies inside one wave's range is finished by that
 // wave; one that straddles waves leaves partial softmax states that a second
 // kernel merges by log-sum-exp.  With a fixed partition size (> 0) the split
@@ -345,9 +347,30 @@ __device__ __forceinline__ void count_tiles(const DecodeArgs& a, int upto, int64
     }
 }
 
-// Wave owning unit u when T units are split into W ranges [floor(wT/W), floor((w+1)T/W)).
-__device__ __forceinline__ int64_t unit_owner(int64_t u, int64_t T, int64_t W) {
-    return ((u + 1) * W - 1) / T;
+// The split of T tiles over W waves: the first Wl waves share the first F tiles
+// evenly, the other W - Wl waves the remaining T - F (every range non-empty).
+struct Split {
+    int64_t T, W, F, Wl;
+};
+__device__ __forceinline__ Split make_split(const DecodeArgs& a, int64_t T, int64_t W) {
+    Split p{T, W, T, W};                       // even split: one class of waves
+    if (W == a.num_waves && W % 2 == 0) {
+        const int64_t F = T * a.lead_share_q10 / 1024, Wl = W / 2;
+        if (F >= Wl && T - F >= W - Wl) {
+            p.F = F;
+            p.Wl = Wl;
+        }
+    }
+    return p;
+}
+// First tile of wave w's range [begin(w), begin(w + 1)); begin(Wl) = F, begin(W) = T.
+__device__ __forceinline__ int64_t range_begin(const Split& p, int64_t w) {
+    return w <= p.Wl ? w * p.F / p.Wl : p.F + (w - p.Wl) * (p.T - p.F) / (p.W - p.Wl);
+}
+// Wave whose range holds tile u.
+__device__ __forceinline__ int64_t unit_owner(const Split& p, int64_t u) {
+    return u < p.F ? ((u + 1) * p.Wl - 1) / p.F
+                   : p.Wl + ((u - p.F + 1) * (p.W - p.Wl) - 1) / (p.T - p.F);
 }
 
 template <bool BF16, int D, int G>
@@ -368,7 +391,8 @@ __global__ __launch_bounds__(64, (BF16 ? 2 : 1)) void decode_balanced_kernel(Dec
     const int64_t T = tiles_all * Hkv;
     const int64_t W = min((int64_t)a.num_waves, T);
     if (w >= W) return;
-    const int64_t b = w * T / W, e = (w + 1) * T / W;
+    const Split sp = make_split(a, T, W);
+    const int64_t b = range_begin(sp, w), e = range_begin(sp, w + 1);
 
     // locate the sequence holding unit b: first s with Hkv * (tiles up to s) > b
     int s = 0;
@@ -456,30 +480,50 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(DecodeArgs a)
     }
     const int64_t T = tiles_all * Hkv, W = min((int64_t)a.num_waves, T);
     const int64_t u0 = before * Hkv + (int64_t)h * nt;
-    const int64_t w0 = unit_owner(u0, T, W), w1 = unit_owner(u0 + nt - 1, T, W);
+    const Split sp = make_split(a, T, W);
+    const int64_t w0 = unit_owner(sp, u0), w1 = unit_owner(sp, u0 + nt - 1);
     if (w0 == w1) return;  // finished by one wave
     const int npieces = (int)(w1 - w0 + 1);
     auto slot_row = [&](int p) -> int64_t { return ((w0 + p) * 2 + (p == 0 ? 1 : 0)) * G + hh; };
     float M = kNoMax;
     for (int p = lane; p < npieces; p += 64) M = fmaxf(M, a.part_ml[slot_row(p) * 2]);
     M = wave_max(M);
+    // pieces in chunks of 64: lane p holds the weight of piece c0 + p; the output rows
+    // of kBatch pieces are loaded together (unconditionally, clamped to the chunk, so
+    // that the whole batch is in flight at once), then weighted by readlane
+    constexpr int kBatch = 32;
     float L = 0.f;
-    for (int p = lane; p < npieces; p += 64) {
-        const int64_t r = slot_row(p);
-        L += fast_exp2(a.part_ml[r * 2] - M) * a.part_ml[r * 2 + 1];
-    }
-    L = wave_sum(L);
-    const float inv = L > 0.f ? 1.f / L : 0.f;
     float acc[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) acc[k] = 0.f;
-#pragma unroll 8
-    for (int p = 0; p < npieces; ++p) {
-        const int64_t r = slot_row(p);
-        const float wgt = fast_exp2(a.part_ml[r * 2] - M);
+    for (int c0 = 0; c0 < npieces; c0 += 64) {
+        const int cnt = min(64, npieces - c0);
+        float wgt = 0.f;
+        if (lane < cnt) {
+            const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + slot_row(c0 + lane) * 2);
+            wgt = fast_exp2(ml.x - M);
+            L = fmaf(wgt, ml.y, L);
+        }
+        for (int j0 = 0; j0 < cnt; j0 += kBatch) {
+            float v[kBatch][PER];
 #pragma unroll
-        for (int k = 0; k < PER; ++k) acc[k] = fmaf(wgt, a.part_o[r * D + lane * PER + k], acc[k]);
+            for (int j = 0; j < kBatch; ++j) {
+                const float* src = a.part_o + slot_row(c0 + min(j0 + j, cnt - 1)) * D + lane * PER;
+#pragma unroll
+                for (int k = 0; k < PER; ++k) v[j][k] = src[k];
+            }
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                if (j0 + j < cnt) {
+                    const float wj = u2f(__builtin_amdgcn_readlane(f2u(wgt), j0 + j));
+#pragma unroll
+                    for (int k = 0; k < PER; ++k) acc[k] = fmaf(wj, v[j][k], acc[k]);
+                }
+            }
+        }
     }
+    L = wave_sum(L);
+    const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
         if constexpr (BF16)

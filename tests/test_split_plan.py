@@ -1,11 +1,14 @@
 """Host-side check of the balanced decode split (no GPU).
 
-The device code divides the T = Hkv * sum_s ceil(ctx_s / 64) tiles of a batch into
-W' = min(W, T) ranges [floor(wT/W'), floor((w+1)T/W')), walks each range in
-(sequence, kv head, tile) order, finishes a (sequence, head) that lies inside one
-range, and otherwise leaves a partial in slot 0 (first segment of a wave) and/or
-slot 1 (last segment); the merge takes the first covering wave's slot 1 and every
-later covering wave's slot 0, with owner(u) = ((u + 1) W' - 1) // T.  This test
+The device code divides the T = Hkv * sum_s ceil(ctx_s / 64) tiles of a batch over
+W' = min(W, T) waves: with a lead share f (in 1/1024) and W' = W even, the first
+W'/2 waves share the first F = floor(T f / 1024) tiles evenly and the others the
+remaining T - F (when both classes get at least one tile per wave), otherwise all
+W' waves share the T tiles evenly.  Each wave walks its range in (sequence, kv
+head, tile) order, finishes a (sequence, head) that lies inside its range, and
+otherwise leaves a partial in slot 0 (its first segment) and/or slot 1 (its last
+segment); the merge takes the first covering wave's slot 1 and every later
+covering wave's slot 0, locating the owner of a tile by the same split.  This test
 replays that arithmetic on random mixes of lengths and checks that every tile is
 processed exactly once and that the merge reads exactly the slots that were written
 for that (sequence, head)."""
@@ -13,15 +16,35 @@ import numpy as np
 import pytest
 
 
-def plan(ctx, hkv, W):
+def split(T, Weff, W, lead_q10):
+    """(F, Wl): the first Wl waves take the first F tiles."""
+    if Weff == W and W % 2 == 0:
+        F, Wl = T * lead_q10 // 1024, W // 2
+        if F >= Wl and T - F >= W - Wl:
+            return F, Wl
+    return T, Weff
+
+
+def begin(T, Weff, F, Wl, w):
+    return w * F // Wl if w <= Wl else F + (w - Wl) * (T - F) // (Weff - Wl)
+
+
+def owner(T, Weff, F, Wl, u):
+    if u < F:
+        return ((u + 1) * Wl - 1) // F
+    return Wl + ((u - F + 1) * (Weff - Wl) - 1) // (T - F)
+
+
+def plan(ctx, hkv, W, lead_q10):
     nt = [-(-int(c) // 64) for c in ctx]
     T = hkv * sum(nt)
     Weff = min(W, T)
+    F, Wl = split(T, Weff, W, lead_q10)
     written = {}       # (wave, slot) -> (s, h)
     finished = {}      # (s, h) -> wave
     seen = []
     for w in range(Weff):
-        b, e = w * T // Weff, (w + 1) * T // Weff
+        b, e = begin(T, Weff, F, Wl, w), begin(T, Weff, F, Wl, w + 1)
         assert b < e
         before = 0
         s = 0
@@ -53,10 +76,33 @@ def plan(ctx, hkv, W):
                     s += 1
                     while nt[s] == 0:
                         s += 1
-    return nt, T, Weff, written, finished, seen
+    if T:
+        assert begin(T, Weff, F, Wl, Weff) == T
+    return nt, T, Weff, (F, Wl), written, finished, seen
 
 
-@pytest.mark.parametrize("seed", range(40))
+def check(ctx, hkv, nt, T, Weff, F, Wl, written, finished, seen):
+    S = len(ctx)
+    assert sorted(seen) == [(s, h, t) for s in range(S) for h in range(hkv) for t in range(nt[s])]
+    before = np.concatenate([[0], np.cumsum(nt)])
+    for s in range(S):
+        for h in range(hkv):
+            if nt[s] == 0:
+                assert (s, h) not in finished
+                continue
+            u0 = before[s] * hkv + h * nt[s]
+            w0 = owner(T, Weff, F, Wl, u0)
+            w1 = owner(T, Weff, F, Wl, u0 + nt[s] - 1)
+            if w0 == w1:
+                assert finished.get((s, h)) == w0
+            else:
+                assert (s, h) not in finished
+                assert written[(w0, 1)] == (s, h)
+                for w in range(w0 + 1, w1 + 1):
+                    assert written[(w, 0)] == (s, h)
+
+
+@pytest.mark.parametrize("seed", range(60))
 def test_balanced_split_covers_and_merges(seed):
     rng = np.random.Generator(np.random.PCG64(seed))
     S = int(rng.integers(1, 40))
@@ -71,24 +117,21 @@ def test_balanced_split_covers_and_merges(seed):
     else:
         ctx = rng.integers(60, 70, S)                    # around one tile
     W = int(rng.choice([1, 3, 7, 64, 2048]))
-    nt, T, Weff, written, finished, seen = plan(ctx, hkv, W)
-    # every tile exactly once
-    want = [(s, h, t) for s in range(S) for h in range(hkv) for t in range(nt[s])]
-    assert sorted(seen) == want
-    # merge view
-    before = np.concatenate([[0], np.cumsum(nt)])
-    for s in range(S):
-        for h in range(hkv):
-            if nt[s] == 0:
-                assert (s, h) not in finished
-                continue
-            u0 = before[s] * hkv + h * nt[s]
-            w0 = ((u0 + 1) * Weff - 1) // T
-            w1 = ((u0 + nt[s]) * Weff - 1) // T
-            if w0 == w1:
-                assert finished.get((s, h)) == w0
-            else:
-                assert (s, h) not in finished
-                assert written[(w0, 1)] == (s, h)
-                for w in range(w0 + 1, w1 + 1):
-                    assert written[(w, 0)] == (s, h)
+    lead = int(rng.choice([512, 584, 700, 1000]))
+    nt, T, Weff, (F, Wl), written, finished, seen = plan(ctx, hkv, W, lead)
+    check(ctx, hkv, nt, T, Weff, F, Wl, written, finished, seen)
+
+
+@pytest.mark.parametrize("shape", ["gqa", "long"])
+def test_skewed_split_at_benchmark_shapes(shape):
+    """The split the bf16 kernels take on a 256-CU device: 2048 waves, lead share 584."""
+    rng = np.random.Generator(np.random.PCG64(7))
+    if shape == "gqa":
+        ctx, hkv = rng.integers(128, 4096, 64, endpoint=True), 8
+    else:
+        ctx, hkv = rng.integers(32768, 200000, 8, endpoint=True), 4
+    nt, T, Weff, (F, Wl), written, finished, seen = plan(ctx, hkv, 2048, 584)
+    assert Wl == 1024 and F == T * 584 // 1024          # the skewed path is taken
+    check(ctx, hkv, nt, T, Weff, F, Wl, written, finished, seen)
+    # lead waves hold ~1.33x the tiles of the others
+    assert 1.3 < (F / Wl) / ((T - F) / (Weff - Wl)) < 1.36
