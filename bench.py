@@ -131,13 +131,18 @@ def _dev(a):
     return torch.from_numpy(a).cuda()
 
 
-def make_workload(name):
+def make_workload(name, block_size=16, contiguous=False):
     import workloads as W
+    if contiguous and name not in ("gqa", "long"):
+        raise SystemExit("--layout contiguous applies to the gqa and long workloads")
+    if block_size != 16 and name not in ("gqa", "long"):
+        raise SystemExit("--block-size applies to the gqa and long workloads")
     if name == "gqa":
-        b = W.gqa(poison=False)
+        b = W.gqa(poison=False, block_size=block_size, contiguous=contiguous)
         return dict(batch=b, extra=None, prefill=None)
     if name == "long":
-        return dict(batch=W.long_context(poison=False), extra=None, prefill=None)
+        return dict(batch=W.long_context(poison=False, block_size=block_size, contiguous=contiguous),
+                    extra=None, prefill=None)
     if name == "prefix_cow":
         p = W.prefix_cow(poison=False)
         return dict(batch=p.batch, extra=p, prefill=None)
@@ -152,14 +157,23 @@ def run(args):
     import paged_kv_cache_79_amd as pkv
 
     log(f"building workload {args.workload}")
-    wl = make_workload(args.workload)
+    contig = args.layout == "contiguous"
+    wl = make_workload(args.workload, args.block_size, contig)
     b = wl["batch"]
     log(f"workload ready: {b.num_seqs} sequences, max context {b.max_context_len}")
     elem = 2 if b.dtype == "bf16" else 4
-    pool_bytes = 2 * b.k_pool.nbytes
+    if contig:
+        # the unpaged baseline: the same K/V values in [S][L][Hkv][D] slabs, already
+        # holding the step's new token (no cache write is timed)
+        kc, vc = b.extra.pop("k_cache"), b.extra.pop("v_cache")
+        pool_bytes = 2 * kc.nbytes
+    else:
+        pool_bytes = 2 * b.k_pool.nbytes
     # enough pool copies that a rotation cycle spans well over 4x the 256 MB MALL
     copies = max(2, min(8, int(math.ceil(2.4e9 / max(pool_bytes, 1)))))
-    k0, v0 = _dev(b.k_pool), _dev(b.v_pool)
+    k0, v0 = (_dev(kc), _dev(vc)) if contig else (_dev(b.k_pool), _dev(b.v_pool))
+    if contig:
+        del kc, vc
     pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(copies - 1)]
     q = _dev(b.q)
     tables = _dev(b.block_tables)
@@ -182,10 +196,17 @@ def run(args):
 
     def decode(i):
         kp, vp = pools[i % copies]
+        if contig:
+            pkv.contiguous_attention_decode(out, q, kp, vp, ctx, b.max_context_len, b.scale,
+                                            workspace=ws)
+            return
         pkv.paged_attention_decode(out, q, kp, vp, tables, ctx, b.max_context_len, b.scale,
                                    partition_tokens=pt, workspace=ws)
 
     def step(i):
+        if contig:
+            decode(i)
+            return
         kp, vp = pools[i % copies]
         if cow_map is not None:
             pkv.copy_blocks(kp, vp, cow_map)
@@ -235,14 +256,18 @@ def run(args):
                    "block_size": b.block_size, "max_context_len": b.max_context_len,
                    "mean_context_len": round(float(np.mean(b.context_lens)), 1),
                    "split": "balanced" if pt == 0 else f"partitions of {pt}",
+                   "layout": "contiguous [S][L][Hkv][D], no block table (step = decode only)"
+                             if contig else "paged [NB][Hkv][bs][D]",
                    "pool_copies_rotated": copies},
         "seqs_per_s": round(b.num_seqs / (ms_step * 1e-3), 1),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "kv_bytes_per_step": byts,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(b.name) if pt == 0 else None,
-                     "kernel": "paged_attention_decode (attention kernel + merge kernel)",
+                     "traffic": recorded_traffic(b.name) if pt == 0 and not contig
+                                and args.block_size == 16 else None,
+                     "kernel": ("contiguous_attention_decode" if contig else "paged_attention_decode")
+                               + " (attention kernel + merge kernel)",
                      "avg_us": round(dec_avg * 1e3, 2),
                      "runs_us": [round(x * 1e3, 2) for x in dec_runs]},
     }
@@ -258,7 +283,7 @@ def run(args):
                           "tflops": round(fl / (p_ms * 1e-3) / 1e12, 2),
                           "mfma_frac": round(fl / (p_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
     log(f"GPU: {ms_step * 1e3:.1f} us/step, decode {dec_avg * 1e3:.1f} us")
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not contig:
         log("timing the CPU oracle")
         rec["cpu_baseline"] = cpu_baseline(b)
     else:
@@ -273,6 +298,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gqa", choices=["gqa", "long", "prefix_cow", "mixed"])
     ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--layout", default="paged", choices=["paged", "contiguous"],
+                    help="contiguous: the unpaged baseline on the same K/V values (gqa, long)")
+    ap.add_argument("--block-size", type=int, default=16, choices=[8, 16, 32],
+                    help="pool block size of the gqa and long workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

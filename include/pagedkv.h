@@ -145,6 +145,32 @@ pkv_status paged_attention_decode(pkv_dtype dtype, void* out, const void* q,
                                   size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * contiguous_attention_decode -- the unpaged baseline of paged_attention_decode:
+ * the same attention over K/V stored contiguously per sequence, as a system that
+ * reserves each request's whole maximum length up front would ("vAttention",
+ * the KV cache of a request as one contiguous virtual range).  No block table is
+ * read; token t of sequence s, kv head h is at ((s * max_len + t) * Hkv + h) * D.
+ * It exists to measure what the block-table translation costs; the split, the
+ * tile order and the arithmetic are those of the balanced paged decode, so on
+ * the same K/V values the two return identical bits.
+ *
+ *   out, q        [num_seqs][num_q_heads][head_dim] bf16
+ *   k_cache, v_cache  [num_seqs][max_len][num_kv_heads][head_dim] bf16
+ *   max_len       slab length, a positive multiple of 64; context_lens[s] <= max_len
+ *   workspace     as for paged_attention_decode with partition_tokens 0 (size from
+ *                 paged_attention_decode_workspace_bytes(..., 0)); its contents need
+ *                 no initialisation.
+ * Errors: PKV_ERR_UNSUPPORTED for fp32 or head_dim not in {64, 128}; PKV_ERR_SHAPE for
+ * max_len not a multiple of 64; otherwise as paged_attention_decode.
+ */
+pkv_status contiguous_attention_decode(pkv_dtype dtype, void* out, const void* q,
+                                       const void* k_cache, const void* v_cache, int32_t num_seqs,
+                                       int32_t max_len, int32_t num_kv_heads, int32_t head_dim,
+                                       const int32_t* context_lens, int32_t max_context_len,
+                                       int32_t num_q_heads, float scale, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream);
+
+/*
  * paged_attention_prefill_chunk -- causal attention of prefill query chunks over
  * their paged contexts ("Inside vLLM, part 2", chunked prefill: a long prompt is
  * processed a bounded number of tokens per step, each chunk attending to the

@@ -18,7 +18,7 @@ Parity status of each function is listed in ``PINS`` below.
 """
 from .paged import (  # noqa: F401
     BF16, F32, widen, translate, slot_of, gather_kv, kv_head_of, attend, decode,
-    prefill_chunk, kv_write, copy_blocks, partition_partials, lse_merge, kv_size_bytes,
+    decode_contiguous, prefill_chunk, kv_write, copy_blocks, partition_partials, lse_merge, kv_size_bytes,
     blocks_needed, tail_waste,
 )
 
@@ -29,6 +29,8 @@ PINS = {
     "gather_kv": "worked example + round trip against kv_write + physical-id permutation",
     "attend/decode": "torch scaled_dot_product_attention (fp64, CPU, enable_gqa) on identity "
                      "tables; closed forms (ctx=1, q=0, equal keys); one-hot probe",
+    "decode_contiguous": "SDPA (fp64) on the contiguous slabs; equals decode() on a paged pool "
+                         "cut from the same slabs with shuffled blocks",
     "prefill_chunk": "SDPA with is_causal on a chunk covering the whole context; "
                      "every row equals decode on the truncated context",
     "kv_write": "worked example slots; whole-pool bit comparison; negative slots skipped",

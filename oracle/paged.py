@@ -144,6 +144,30 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, scale: float, dtype: s
     return out
 
 
+def decode_contiguous(q, k_cache, v_cache, context_lens, scale: float, dtype: str,
+                      num_kv_heads: int, seqs=None, heads=None) -> np.ndarray:
+    """Decode attention over K/V kept contiguous per request -- the layout of
+    "vAttention 完全拆解" (section on its core abstraction: each request's KV cache
+    is one virtually contiguous range, and the kernel indexes K[t, h, d] linearly;
+    the comparison with PagedAttention keeps that index unchanged).  Token t of
+    sequence s, kv head h is k_cache[s, t, h].  The attention itself is decode()'s:
+    every query head of sequence s attends to its context_lens[s] tokens.
+
+    Returns float64 [S][Hq][D] (rows outside ``seqs``/``heads`` stay NaN)."""
+    S, Hq, D = q.shape
+    out = np.full((S, Hq, D), np.nan)
+    seqs = range(S) if seqs is None else seqs
+    heads = range(Hq) if heads is None else heads
+    for s in seqs:
+        n = int(context_lens[s])
+        for hq in heads:
+            h = kv_head_of(hq, Hq, num_kv_heads)
+            K = widen(k_cache[s, :n, h, :], dtype)
+            V = widen(v_cache[s, :n, h, :], dtype)
+            out[s, hq] = attend(widen(q[s, hq], dtype), K, V, scale)
+    return out
+
+
 def prefill_chunk(q, cu_q_lens, k_pool, v_pool, block_tables, context_lens, scale: float,
                   dtype: str, num_kv_heads: int, rows=None) -> np.ndarray:
     """Causal attention of a prefill chunk over its paged context.

@@ -22,6 +22,7 @@ EXPORTS = (
     "copy_blocks",
     "paged_attention_decode_workspace_bytes",
     "paged_attention_decode",
+    "contiguous_attention_decode",
     "paged_attention_prefill_chunk",
 )
 
@@ -59,6 +60,9 @@ def load_library(path: Optional[str] = None):
     lib.paged_attention_decode.argtypes = [ctypes.c_int, VP, VP, VP, VP, I32, I32, I32, I32, VP, I32,
                                            VP, I32, I32, I32, F, I32, VP, SZ, VP]
     lib.paged_attention_decode.restype = ctypes.c_int
+    lib.contiguous_attention_decode.argtypes = [ctypes.c_int, VP, VP, VP, VP, I32, I32, I32, I32, VP,
+                                                I32, I32, F, VP, SZ, VP]
+    lib.contiguous_attention_decode.restype = ctypes.c_int
     lib.paged_attention_prefill_chunk.argtypes = [ctypes.c_int, VP, VP, VP, I32, I32, VP, VP, I32, I32,
                                                   I32, I32, VP, I32, VP, I32, I32, F, VP]
     lib.paged_attention_prefill_chunk.restype = ctypes.c_int
@@ -156,6 +160,12 @@ def copy_blocks(k_pool, v_pool, block_mapping, stream=None) -> None:
         _stream(stream)))
 
 
+def decode_workspace(num_bytes: int, device):
+    """Device scratch for a decode call (its contents need no initialisation)."""
+    import torch
+    return torch.empty(max(int(num_bytes), 1), dtype=torch.uint8, device=device)
+
+
 def paged_attention_decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int,
                                            head_dim: int, max_context_len: int,
                                            partition_tokens: int = 0) -> int:
@@ -179,7 +189,7 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens, m
         raise ValueError("block_tables must be [num_seqs][max_blocks], context_lens [num_seqs]")
     need = paged_attention_decode_workspace_bytes(S, hq, hkv, d, max_context_len, partition_tokens)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = decode_workspace(need, q.device)
     if workspace is not None:
         _dev(workspace, "workspace")
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -188,6 +198,35 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens, m
         _dtype_code(q), _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), nb, hkv, bs, d,
         _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), S, int(max_context_len),
         hq, float(scale), int(partition_tokens), _ptr(workspace), wbytes, _stream(stream)))
+
+
+def contiguous_attention_decode(out, q, k_cache, v_cache, context_lens, max_context_len: int,
+                                scale: float, workspace=None, stream=None) -> None:
+    """The unpaged baseline: decode attention over K/V stored contiguously per sequence,
+    k_cache/v_cache [S][max_len][Hkv][D] bf16 (max_len a multiple of 64)."""
+    import torch
+    for n, t in (("out", out), ("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev(t, n)
+    _dev(context_lens, "context_lens", torch.int32)
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape or not k_cache.is_contiguous() or \
+            not v_cache.is_contiguous():
+        raise ValueError("k_cache/v_cache must be contiguous [num_seqs][max_len][num_kv_heads][head_dim]")
+    S, L, hkv, d = (int(x) for x in k_cache.shape)
+    hq = int(q.shape[1])
+    if q.dim() != 3 or q.shape[0] != S or q.shape[2] != d or out.shape != q.shape or \
+            q.dtype != k_cache.dtype or out.dtype != q.dtype or context_lens.shape != (S,):
+        raise ValueError("q/out must be [num_seqs][num_q_heads][head_dim] of the cache dtype")
+    need = paged_attention_decode_workspace_bytes(S, hq, hkv, d, max_context_len, 0)
+    if workspace is None and need > 0:
+        workspace = decode_workspace(need, q.device)
+    if workspace is not None:
+        _dev(workspace, "workspace")
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    lib = load_library()
+    _check("contiguous_attention_decode", lib.contiguous_attention_decode(
+        _dtype_code(q), _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), S, L, hkv, d,
+        _ptr(context_lens), int(max_context_len), hq, float(scale), _ptr(workspace), wbytes,
+        _stream(stream)))
 
 
 def paged_attention_prefill_chunk(out, q, cu_q_lens, k_pool, v_pool, block_tables, context_lens,

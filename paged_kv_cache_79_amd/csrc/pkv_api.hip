@@ -80,6 +80,23 @@ size_t decode_workspace(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_he
     return (size_t)balanced_wave_bound() * 2 * group * (size_t)(head_dim + 2) * sizeof(float);
 }
 
+// Balanced split over the resident waves (`resident`, from the kernel's occupancy):
+// grid size, lead share and the partial-state layout in the workspace.
+pkv_status setup_balanced(DecodeArgs& a, int64_t resident, int32_t num_seqs, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t max_context_len, int group, void* workspace) {
+    // one wave per resident slot, but no more than there are tiles to share out
+    const int64_t tiles_bound = (int64_t)num_seqs * num_kv_heads * cdiv64(max_context_len, 64);
+    if (resident <= 0) return PKV_ERR_LAUNCH;
+    int64_t waves = std::min(resident, balanced_wave_bound());
+    // two waves per SIMD (the bf16 kernels fill every slot): lead waves get more tiles
+    a.lead_share_q10 = waves == balanced_wave_bound() ? kLeadShareQ10 : 512;
+    waves = std::max<int64_t>(1, std::min(waves, tiles_bound));
+    a.num_waves = (int32_t)waves;
+    a.part_o = static_cast<float*>(workspace);
+    a.part_ml = a.part_o + (size_t)waves * 2 * group * head_dim;
+    return PKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -186,6 +203,8 @@ pkv_status paged_attention_decode(pkv_dtype dtype, void* out, const void* q, con
     a.num_parts = 1;
     a.num_waves = 0;
     a.lead_share_q10 = 512;
+    a.contig_seq_stride = 0;
+    a.contig_row_stride = 0;
     a.part_o = static_cast<float*>(workspace);
     a.part_ml = nullptr;
     if (partition_tokens > 0) {
@@ -193,18 +212,68 @@ pkv_status paged_attention_decode(pkv_dtype dtype, void* out, const void* q, con
         if (a.num_parts > 1)
             a.part_ml = a.part_o + (size_t)num_seqs * num_q_heads * a.num_parts * head_dim;
     } else {
-        // one wave per resident slot, but no more than there are tiles to share out
-        const int64_t tiles_bound = (int64_t)num_seqs * num_kv_heads * cdiv64(max_context_len, 64);
-        int64_t waves = decode_balanced_waves(dtype == PKV_BF16, head_dim, group);
-        if (waves <= 0) return PKV_ERR_LAUNCH;
-        waves = std::min(waves, balanced_wave_bound());
-        // two waves per SIMD (the bf16 kernels fill every slot): lead waves get more tiles
-        if (waves == balanced_wave_bound()) a.lead_share_q10 = kLeadShareQ10;
-        waves = std::max<int64_t>(1, std::min(waves, tiles_bound));
-        a.num_waves = (int32_t)waves;
-        a.part_ml = a.part_o + (size_t)waves * 2 * group * head_dim;
+        const pkv_status sb =
+            setup_balanced(a, decode_balanced_waves(dtype == PKV_BF16, head_dim, group), num_seqs,
+                           num_kv_heads, head_dim, max_context_len, group, workspace);
+        if (sb != PKV_OK) return sb;
     }
     return launch_status(launch_decode(a, dtype == PKV_BF16, head_dim, group, num_seqs, stream));
+}
+
+pkv_status contiguous_attention_decode(pkv_dtype dtype, void* out, const void* q,
+                                       const void* k_cache, const void* v_cache, int32_t num_seqs,
+                                       int32_t max_len, int32_t num_kv_heads, int32_t head_dim,
+                                       const int32_t* context_lens, int32_t max_context_len,
+                                       int32_t num_q_heads, float scale, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+    if (dtype != PKV_F32 && dtype != PKV_BF16) return PKV_ERR_DTYPE;
+    if (dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+    if (num_seqs < 0 || max_len <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        max_context_len < 0 || num_q_heads <= 0)
+        return PKV_ERR_SHAPE;
+    if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
+    if (max_len % 64) return PKV_ERR_SHAPE;                 // whole 64-token tiles per slab
+    if (num_q_heads % num_kv_heads) return PKV_ERR_SHAPE;
+    const int group = num_q_heads / num_kv_heads;
+    if (group > 8) return PKV_ERR_UNSUPPORTED;
+    if (!isfinite(scale)) return PKV_ERR_SHAPE;
+    const int64_t row_stride = (int64_t)num_kv_heads * head_dim * 2;
+    if (row_stride * 63 >= ((int64_t)1 << 31)) return PKV_ERR_UNSUPPORTED;  // 32-bit lane offsets
+    if (num_seqs == 0) return PKV_OK;
+    if (!out || !q || !k_cache || !v_cache || !context_lens) return PKV_ERR_NULL;
+    if ((int64_t)num_seqs * num_kv_heads > 65535) return PKV_ERR_UNSUPPORTED;
+    const size_t need = decode_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                         max_context_len, 0);
+    if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+
+    DecodeArgs a;
+    a.out = out;
+    a.q = q;
+    a.k_pool = static_cast<const char*>(k_cache);
+    a.v_pool = static_cast<const char*>(v_cache);
+    a.block_tables = nullptr;                                // no translation
+    a.context_lens = context_lens;
+    // a slab of max_len tokens seen as max_len / 64 blocks of 64 (bounds the lengths)
+    a.g.row_bytes = head_dim * 2;
+    a.g.head_stride_bytes = head_dim * 2;
+    a.g.block_stride_bytes = 64 * row_stride;
+    a.g.num_blocks = max_len / 64;
+    a.g.num_kv_heads = num_kv_heads;
+    a.g.block_size = 64;
+    a.g.log2_bs = 6;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.max_blocks_per_seq = max_len / 64;
+    a.max_context_len = max_context_len;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.part_tokens = 0;
+    a.num_parts = 1;
+    a.contig_seq_stride = (int64_t)max_len * row_stride;
+    a.contig_row_stride = (int32_t)row_stride;
+    const pkv_status sb = setup_balanced(a, decode_contiguous_waves(head_dim, group), num_seqs,
+                                         num_kv_heads, head_dim, max_context_len, group, workspace);
+    if (sb != PKV_OK) return sb;
+    return launch_status(launch_decode_contiguous(a, head_dim, group, num_seqs, stream));
 }
 
 pkv_status paged_attention_prefill_chunk(pkv_dtype dtype, void* out, const void* q,
@@ -229,7 +298,9 @@ pkv_status paged_attention_prefill_chunk(pkv_dtype dtype, void* out, const void*
     if (num_chunks == 0 || max_q_len == 0) return PKV_OK;
     if (!out || !q || !cu_q_lens || !k_pool || !v_pool || !block_tables || !context_lens)
         return PKV_ERR_NULL;
-    if (num_chunks > 65535) return PKV_ERR_UNSUPPORTED;  // grid.z
+    // work items: query tiles (128 / group query positions each) x kv heads x chunks
+    if (cdiv64(max_q_len, 128 / group) * num_kv_heads * num_chunks > ((int64_t)1 << 30))
+        return PKV_ERR_UNSUPPORTED;
 
     PrefillArgs a;
     a.out = out;

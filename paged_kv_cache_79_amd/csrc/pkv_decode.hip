@@ -81,7 +81,8 @@ struct SegState {
 };
 
 // Attend the G query heads of (s, h) to tokens [t_begin, t_end) of the sequence.
-template <bool BF16, int D, int G>
+// CONTIG: the unpaged baseline -- K/V in the contiguous [S][L][Hkv][D] layout, no table.
+template <bool BF16, int D, int G, bool CONTIG = false>
 __device__ __forceinline__ void attend_segment(const DecodeArgs& a, int s, int h, int ctx,
                                                int t_begin, int t_end, char* lds_k,
                                                uint32_t* lds_p, uint32_t* lds_q,
@@ -92,12 +93,15 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, int s, int h
     const int nblk = (ctx + bs - 1) >> a.g.log2_bs;
     const int ra = lane / S::CPR;          // row inside a wave-wide load
     const int rc = lane - ra * S::CPR;     // 16-byte chunk inside the row
-    const uint32_t lane_off = (uint32_t)(ra * S::RB + rc * 16);
-    const int32_t* table = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-    const char* kb = (const char*)pin_uniform(a.k_pool + (int64_t)h * a.g.head_stride_bytes);
-    const char* vb = (const char*)pin_uniform(a.v_pool + (int64_t)h * a.g.head_stride_bytes);
+    const uint32_t row_stride = CONTIG ? (uint32_t)a.contig_row_stride : (uint32_t)S::RB;
+    const uint32_t lane_off = (uint32_t)ra * row_stride + (uint32_t)(rc * 16);
+    const int32_t* table = CONTIG ? nullptr : a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+    const int64_t head_base = CONTIG ? (int64_t)s * a.contig_seq_stride + (int64_t)h * S::RB
+                                     : (int64_t)h * a.g.head_stride_bytes;
+    const char* kb = (const char*)pin_uniform(a.k_pool + head_base);
+    const char* vb = (const char*)pin_uniform(a.v_pool + head_base);
 
-    int tab_cur = load_tile_table(table, t_begin, a.g.log2_bs, nblk, lane);
+    int tab_cur = CONTIG ? 0 : load_tile_table(table, t_begin, a.g.log2_bs, nblk, lane);
     __syncthreads();  // the previous segment is done with lds_q
     {
         const u32x4* qsrc = reinterpret_cast<const u32x4*>(
@@ -125,20 +129,28 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, int s, int h
         asm volatile("" : "+v"(loff));
 #pragma unroll
         for (int i = 0; i < S::NL; ++i) {
-            const int rel = (i * S::R) >> a.g.log2_bs;   // block of this load inside the tile
-            int pb = __builtin_amdgcn_readlane(tab, rel);
-            pb = ((unsigned)pb < (unsigned)a.g.num_blocks) ? pb : 0;   // never dereference a bad id
-            // scalar base: block, head and first row of this load; per-lane part is lane_off.
-            // The 64-bit product is spelled as two 32-bit halves so it stays on the scalar unit.
-            const uint32_t ub = (uint32_t)pb, us = (uint32_t)a.g.block_stride_bytes;
-            const uint64_t base = (((uint64_t)__umulhi(ub, us) << 32) | (uint64_t)(ub * us)) +
-                                  (uint64_t)(((i * S::R) & (bs - 1)) * S::RB);
+            uint64_t base;
+            if constexpr (CONTIG) {
+                // row t0 + i*R of the sequence's slab (the slab holds a whole number of tiles)
+                const uint32_t ur = (uint32_t)(t0 + i * S::R);
+                base = ((uint64_t)__umulhi(ur, row_stride) << 32) | (uint64_t)(ur * row_stride);
+            } else {
+                const int rel = (i * S::R) >> a.g.log2_bs;   // block of this load inside the tile
+                int pb = __builtin_amdgcn_readlane(tab, rel);
+                pb = ((unsigned)pb < (unsigned)a.g.num_blocks) ? pb : 0;   // never a bad id
+                // scalar base: block, head and first row of this load; per-lane part is
+                // lane_off.  The 64-bit product is spelled as two 32-bit halves so it stays
+                // on the scalar unit.
+                const uint32_t ub = (uint32_t)pb, us = (uint32_t)a.g.block_stride_bytes;
+                base = (((uint64_t)__umulhi(ub, us) << 32) | (uint64_t)(ub * us)) +
+                       (uint64_t)(((i * S::R) & (bs - 1)) * S::RB);
+            }
             // K and V are read exactly once: nontemporal loads keep them from
             // displacing reusable lines (tables, q, partials) in the caches
             kreg[i] = __builtin_nontemporal_load((global_ptr<u32x4>)(pin_uniform(kb + base) + loff));
             vreg[i] = __builtin_nontemporal_load((global_ptr<u32x4>)(pin_uniform(vb + base) + loff));
         }
-        tab_cur = load_tile_table(table, t0 + kTile, a.g.log2_bs, nblk, lane);
+        if constexpr (!CONTIG) tab_cur = load_tile_table(table, t0 + kTile, a.g.log2_bs, nblk, lane);
 #pragma unroll
         for (int i = 0; i < S::NL; ++i)
             *reinterpret_cast<u32x4*>(lds_k + (i * S::R + ra) * S::KPITCH + rc * 16) = kreg[i];
@@ -373,7 +385,7 @@ __device__ __forceinline__ int64_t unit_owner(const Split& p, int64_t u) {
                    : p.Wl + ((u - p.F + 1) * (p.W - p.Wl) - 1) / (p.T - p.F);
 }
 
-template <bool BF16, int D, int G>
+template <bool BF16, int D, int G, bool CONTIG = false>
 __global__ __launch_bounds__(64, (BF16 ? 2 : 1)) void decode_balanced_kernel(DecodeArgs a) {
     using S = DecodeShape<BF16, D>;
     __shared__ __attribute__((aligned(16))) char lds_k[kTile * S::KPITCH];
@@ -430,8 +442,8 @@ __global__ __launch_bounds__(64, (BF16 ? 2 : 1)) void decode_balanced_kernel(Dec
         const int seg = (int)min((int64_t)(nt_s - tile), remaining);
         const bool last = seg == remaining;
         const int ctx = clamp_ctx(a, a.context_lens[s]);
-        attend_segment<BF16, D, G>(a, s, h, ctx, tile * kTile, min(ctx, (tile + seg) * kTile),
-                                   lds_k, lds_p, lds_q, st);
+        attend_segment<BF16, D, G, CONTIG>(a, s, h, ctx, tile * kTile,
+                                           min(ctx, (tile + seg) * kTile), lds_k, lds_p, lds_q, st);
         if (tile == 0 && seg == nt_s) {
             write_rows<BF16, D, G>(a, s, h, st);
         } else {
@@ -606,7 +618,7 @@ __global__ __launch_bounds__(64) void decode_partition_merge_kernel(DecodeArgs a
 // --------------------------------------------------------------------------------------
 // host side
 // --------------------------------------------------------------------------------------
-template <bool BF16, int D, int G>
+template <bool BF16, int D, int G, bool CONTIG = false>
 static int balanced_waves_t() {
     // resident waves of the balanced kernel on the current device, cached per device
     static std::mutex mu;
@@ -617,8 +629,9 @@ static int balanced_waves_t() {
     if (cache[dev] == 0) {
         int per_cu = 0, cus = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per_cu, reinterpret_cast<const void*>(decode_balanced_kernel<BF16, D, G>), 64, 0) !=
-                hipSuccess ||
+                &per_cu,
+                reinterpret_cast<const void*>(decode_balanced_kernel<BF16, D, G, CONTIG>), 64,
+                0) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return 0;
         cache[dev] = max(1, per_cu) * max(1, cus);
@@ -657,6 +670,20 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
         default: break;                            \
     }
 
+// the contiguous-layout (unpaged) baseline: bf16, balanced split
+template <bool BF16, int D, int G>
+static hipError_t launch_contig_t(const DecodeArgs& a, hipStream_t st) {
+    hipLaunchKernelGGL((decode_balanced_kernel<true, D, G, true>), dim3(a.num_waves), dim3(64), 0,
+                       st, a);
+    hipLaunchKernelGGL((decode_balanced_merge_kernel<true, D, G>), dim3(a.num_seqs * a.num_q_heads),
+                       dim3(64), 0, st, a);
+    return hipGetLastError();
+}
+template <bool BF16, int D, int G>
+static int contig_waves_t() {
+    return balanced_waves_t<true, D, G, true>();
+}
+
 template <bool BF16, int D>
 static hipError_t launch_decode_g(const DecodeArgs& a, int group, hipStream_t st) {
     PKV_DISPATCH_G(launch_decode_t, BF16, D, group, a, st)
@@ -667,6 +694,20 @@ template <bool BF16, int D>
 static int balanced_waves_g(int group) {
     PKV_DISPATCH_G(balanced_waves_t, BF16, D, group)
     return 0;
+}
+
+int decode_contiguous_waves(int head_dim, int group) {
+    if (head_dim == 128) { PKV_DISPATCH_G(contig_waves_t, true, 128, group) }
+    if (head_dim == 64) { PKV_DISPATCH_G(contig_waves_t, true, 64, group) }
+    return 0;
+}
+
+hipError_t launch_decode_contiguous(const DecodeArgs& a, int head_dim, int group, int num_seqs,
+                                    hipStream_t st) {
+    if (num_seqs == 0) return hipSuccess;
+    if (head_dim == 128) { PKV_DISPATCH_G(launch_contig_t, true, 128, group, a, st) }
+    if (head_dim == 64) { PKV_DISPATCH_G(launch_contig_t, true, 64, group, a, st) }
+    return hipErrorInvalidValue;
 }
 
 int decode_balanced_waves(bool is_bf16, int head_dim, int group) {

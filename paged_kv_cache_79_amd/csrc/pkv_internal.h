@@ -55,6 +55,10 @@ struct DecodeArgs {
     int32_t num_parts;     // fixed partitions per sequence (grid.x)
     int32_t num_waves;     // balanced split: persistent waves (grid.x)
     int32_t lead_share_q10;  // balanced split: tiles given to the first half of the waves, /1024
+    // Contiguous layout (the unpaged baseline): k_pool/v_pool are [S][L][Hkv][D]; token t of
+    // sequence s, head h is at s * seq_stride + t * row_stride + h * row_bytes.
+    int64_t contig_seq_stride;
+    int32_t contig_row_stride;
     float scale_log2;      // scale * log2(e)
 };
 
@@ -67,6 +71,8 @@ constexpr int kLeadShareQ10 = 584;
 
 // Persistent waves the balanced decode launches on the current device.
 int decode_balanced_waves(bool is_bf16, int head_dim, int group);
+// The same for the contiguous-layout decode (bf16 only).
+int decode_contiguous_waves(int head_dim, int group);
 
 struct PrefillArgs {
     void* out;
@@ -88,6 +94,9 @@ hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t st);
 // is_bf16 selects the element type; group = num_q_heads / num_kv_heads (1..8).
 hipError_t launch_decode(const DecodeArgs& a, bool is_bf16, int head_dim, int group,
                          int num_seqs, hipStream_t st);
+// Decode over the contiguous [S][L][Hkv][D] layout (bf16, balanced split).
+hipError_t launch_decode_contiguous(const DecodeArgs& a, int head_dim, int group, int num_seqs,
+                                    hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int group, int num_chunks,
                           int max_q_len, hipStream_t st);
 

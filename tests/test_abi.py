@@ -115,6 +115,29 @@ def test_workspace_sizes(lib):
     assert f(0, 8, 2, 128, 4096, 0) == 0
 
 
+def contig(lib, dtype=1, S=2, L=128, hkv=2, d=128, maxctx=100, hq=8, scale=0.1, ws=P, wsb=1 << 30,
+           ptr=P):
+    return lib.contiguous_attention_decode(dtype, ptr, ptr, ptr, ptr, S, L, hkv, d, ptr, maxctx, hq,
+                                           scale, ws, wsb, None)
+
+
+@dummy_ptrs
+def test_contiguous_validation(lib):
+    assert contig(lib, dtype=7) == DTYPE
+    assert contig(lib, dtype=0) == UNSUP               # fp32: the baseline is bf16 only
+    assert contig(lib, d=96) == UNSUP
+    assert contig(lib, L=100) == SHAPE                 # slab not a whole number of tiles
+    assert contig(lib, L=0) == SHAPE
+    assert contig(lib, hq=9) == SHAPE
+    assert contig(lib, hq=36, hkv=2) == UNSUP          # group of 18 heads
+    assert contig(lib, scale=float("nan")) == SHAPE
+    assert contig(lib, ptr=None) == NULL
+    assert contig(lib, S=0, ptr=None) == OK
+    assert contig(lib, ws=None) == WS
+    need = lib.paged_attention_decode_workspace_bytes(2, 8, 2, 128, 100, 0)
+    assert contig(lib, wsb=need - 1) == WS
+
+
 @dummy_ptrs
 def test_prefill_validation(lib):
     f = lib.paged_attention_prefill_chunk

@@ -149,6 +149,38 @@ def pin_decode_vs_library(seed=1, ctx=(1, 7, 13, 32), hq=8, hkv=2, d=16, bs=4):
         np.testing.assert_allclose(got[s], want, rtol=1e-12, atol=1e-12)
 
 
+def pin_contiguous_decode(seed=3, ctx=(0, 1, 9, 64, 100), hq=6, hkv=3, d=8, L=128, bs=4):
+    """The contiguous-layout decode equals SDPA on each slab, gives a zero row for an
+    empty context, and equals the paged decode of a pool cut from the same slabs into
+    shuffled blocks of bs tokens."""
+    rng = np.random.default_rng(seed)
+    S = len(ctx)
+    q = rng.standard_normal((S, hq, d)).astype(np.float32)
+    kc = rng.standard_normal((S, L, hkv, d)).astype(np.float32)
+    vc = rng.standard_normal((S, L, hkv, d)).astype(np.float32)
+    got = O.decode_contiguous(q, kc, vc, np.array(ctx), 0.29, "f32", hkv)
+    for s, n in enumerate(ctx):
+        if n == 0:
+            assert np.array_equal(got[s], np.zeros((hq, d)))
+            continue
+        K = np.transpose(kc[s, :n], (1, 0, 2))[None].astype(np.float64)  # [1][Hkv][n][D]
+        V = np.transpose(vc[s, :n], (1, 0, 2))[None].astype(np.float64)
+        want = sdpa(q[s][None, :, None, :].astype(np.float64), K, V, 0.29)[0, :, 0, :]
+        np.testing.assert_allclose(got[s], want, rtol=1e-12, atol=1e-12)
+    # the same slabs cut into blocks of bs tokens at shuffled physical ids
+    mb = L // bs
+    perm = rng.permutation(S * mb)
+    tables = perm.reshape(S, mb).astype(np.int32)
+    kp = np.empty((S * mb, hkv, bs, d), np.float32)
+    vp = np.empty_like(kp)
+    for s in range(S):
+        for b in range(mb):
+            kp[tables[s, b]] = np.transpose(kc[s, b * bs:(b + 1) * bs], (1, 0, 2))
+            vp[tables[s, b]] = np.transpose(vc[s, b * bs:(b + 1) * bs], (1, 0, 2))
+    paged = O.decode(q, kp, vp, tables, np.array(ctx), 0.29, "f32", hkv)
+    np.testing.assert_allclose(got, paged, rtol=1e-12, atol=1e-12)
+
+
 def relabel(pool_list, tables, perm):
     """Move physical block b to perm[b] and rewrite the tables to match."""
     outs = []
@@ -362,7 +394,8 @@ def pin_waste_bound():
 PINS = [pin_worked_example, pin_worked_example_write_gather, pin_bf16_widening,
         pin_decode_vs_library, pin_permutation_invariance, pin_closed_forms, pin_one_hot_probe,
         pin_nan_poison, pin_prefix_sharing, pin_cow_divergence, pin_copy_blocks_snapshot,
-        pin_prefill_vs_library, pin_lse_merge, pin_kv_size_model, pin_waste_bound]
+        pin_prefill_vs_library, pin_lse_merge, pin_kv_size_model, pin_waste_bound,
+        pin_contiguous_decode]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -463,6 +496,20 @@ def _mut_prefill_exclusive(q, cu_q_lens, k_pool, v_pool, block_tables, context_l
     return out
 
 
+def _mut_contiguous_heads(q, k_cache, v_cache, context_lens, scale, dtype, num_kv_heads,
+                          seqs=None, heads=None):
+    """Interleaved instead of consecutive query-head groups on the contiguous layout."""
+    S, Hq, D = q.shape
+    out = np.full((S, Hq, D), np.nan)
+    for s in range(S):
+        n = int(context_lens[s])
+        for hq in range(Hq):
+            h = hq % num_kv_heads
+            out[s, hq] = O.attend(O.widen(q[s, hq], dtype), O.widen(k_cache[s, :n, h], dtype),
+                                  O.widen(v_cache[s, :n, h], dtype), scale)
+    return out
+
+
 def _mut_size(layers, length, kv_heads, head_dim, elem_bytes):
     return layers * length * kv_heads * head_dim * elem_bytes
 
@@ -480,6 +527,7 @@ MUTANTS = {
     "copy_reversed_pairs": ("copy_blocks", _mut_copy),
     "prefill_exclusive_causal": ("prefill_chunk", _mut_prefill_exclusive),
     "size_model_missing_factor_2": ("kv_size_bytes", _mut_size),
+    "contiguous_interleaved_heads": ("decode_contiguous", _mut_contiguous_heads),
 }
 
 

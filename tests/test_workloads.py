@@ -104,3 +104,23 @@ def test_mixed_structure():
         slots = dec.slot_mapping[4 + 64 * c: 4 + 64 * (c + 1)]
         want = [O.slot_of(pre.block_tables[c], t, 16) for t in range(n - 64, n)]
         assert list(slots) == want
+
+
+def test_contiguous_slabs_hold_the_paged_values():
+    """The unpaged layout carries the same values as the pool: history at the same
+    positions, the step's new token at ctx - 1, the fill value past the context."""
+    b = W.gqa(num_seqs=5, contiguous=True)
+    kc = b.extra["k_cache"]
+    assert kc.shape == (5, 4096, 8, 128)
+    rng = np.random.default_rng(0)
+    for s in range(5):
+        n = int(b.context_lens[s])
+        assert np.array_equal(kc[s, n - 1], b.k_new[s])
+        assert np.array_equal(b.extra["v_cache"][s, n - 1], b.v_new[s])
+        assert (kc[s, n:] == W.BF16_NAN).all()
+        for t in rng.integers(0, n - 1, 20):
+            pb, off = b.block_tables[s, t // b.block_size], t % b.block_size
+            assert np.array_equal(kc[s, t], b.k_pool[pb, :, off])
+    # the same draws as without the slabs
+    b0 = W.gqa(num_seqs=5)
+    assert np.array_equal(b0.k_pool, b.k_pool) and np.array_equal(b0.q, b.q)

@@ -193,8 +193,10 @@ class PrefillBatch:
 # --------------------------------------------------------------------------
 # generic builder
 # --------------------------------------------------------------------------
-def _fill_history(rng, pool_k, pool_v, table_row, n_hist, block_size, dtype, hkv, d):
-    """Write positions [0, n_hist) of one sequence, as earlier steps would have."""
+def _fill_history(rng, pool_k, pool_v, table_row, n_hist, block_size, dtype, hkv, d,
+                  slab_k=None, slab_v=None):
+    """Write positions [0, n_hist) of one sequence, as earlier steps would have (and,
+    when slabs [L][Hkv][D] are given, the same values at the same positions there)."""
     if n_hist <= 0:
         return
     # bounded chunks keep peak host memory modest for 200K-token contexts
@@ -207,12 +209,20 @@ def _fill_history(rng, pool_k, pool_v, table_row, n_hist, block_size, dtype, hkv
         kv = rng.standard_normal((2, p1 - p0, hkv, d), dtype=np.float32)
         pool_k[pb, :, off, :] = _encode(kv[0], dtype)
         pool_v[pb, :, off, :] = _encode(kv[1], dtype)
+        if slab_k is not None:
+            slab_k[p0:p1] = _encode(kv[0], dtype)
+            slab_v[p0:p1] = _encode(kv[1], dtype)
 
 
 def build_decode_batch(*, name, dtype, context_lens, num_q_heads, num_kv_heads, head_dim,
                        block_size, seed, pool_factor=1.25, poison=True, fixed_tables=None,
-                       num_blocks=None, scale=None, rng=None) -> DecodeBatch:
-    """Decode step: history K/V in the pool, one new token per sequence to write."""
+                       num_blocks=None, scale=None, rng=None, contiguous=False) -> DecodeBatch:
+    """Decode step: history K/V in the pool, one new token per sequence to write.
+
+    contiguous=True also keeps the same values in the unpaged layout: extra["k_cache"],
+    extra["v_cache"] [S][L][Hkv][D] with L the longest context rounded up to 64, holding
+    each sequence's history and its new token at position ctx - 1 (the state after the
+    step's write); positions past a context hold the fill value."""
     rng = rng if rng is not None else np.random.Generator(np.random.PCG64(seed))
     ctx = np.asarray(context_lens, dtype=np.int64)
     S = int(ctx.shape[0])
@@ -236,16 +246,29 @@ def build_decode_batch(*, name, dtype, context_lens, num_q_heads, num_kv_heads, 
     fill = _fill_value(dtype, poison)
     k_pool = np.full((num_blocks, hkv, bs, d), fill, dtype=st)
     v_pool = np.full((num_blocks, hkv, bs, d), fill, dtype=st)
+    extra = {}
+    if contiguous:
+        L = max(64, cdiv(int(ctx.max()) if S else 1, 64) * 64)
+        extra["k_cache"] = np.full((S, L, hkv, d), fill, dtype=st)
+        extra["v_cache"] = np.full((S, L, hkv, d), fill, dtype=st)
     for s in range(S):
-        _fill_history(rng, k_pool, v_pool, tables[s], int(ctx[s]) - 1, bs, dtype, hkv, d)
+        _fill_history(rng, k_pool, v_pool, tables[s], int(ctx[s]) - 1, bs, dtype, hkv, d,
+                      extra["k_cache"][s] if contiguous else None,
+                      extra["v_cache"][s] if contiguous else None)
     new = rng.standard_normal((2, S, hkv, d), dtype=np.float32)
+    if contiguous:
+        for s in range(S):
+            if ctx[s] > 0:
+                extra["k_cache"][s, int(ctx[s]) - 1] = _encode(new[0, s], dtype)
+                extra["v_cache"][s, int(ctx[s]) - 1] = _encode(new[1, s], dtype)
     slots = np.array([slots_for_positions(tables[s], [int(ctx[s]) - 1], bs)[0] if ctx[s] > 0 else -1
                       for s in range(S)], dtype=np.int64)
     return DecodeBatch(
         name=name, dtype=dtype, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=bs,
         num_blocks=num_blocks, scale=float(scale if scale is not None else 1.0 / math.sqrt(d)),
         context_lens=ctx.astype(np.int32), block_tables=tables, q=q, k_pool=k_pool, v_pool=v_pool,
-        slot_mapping=slots, k_new=_encode(new[0], dtype), v_new=_encode(new[1], dtype), seed=seed)
+        slot_mapping=slots, k_new=_encode(new[0], dtype), v_new=_encode(new[1], dtype), seed=seed,
+        extra=extra)
 
 
 # --------------------------------------------------------------------------
@@ -270,26 +293,27 @@ def tiny(poison=True) -> DecodeBatch:
                               fixed_tables=tables, num_blocks=32, scale=1.0 / 8.0, rng=rng)
 
 
-def gqa(poison=True, seed=None, num_seqs=64) -> DecodeBatch:
+def gqa(poison=True, seed=None, num_seqs=64, block_size=16, contiguous=False) -> DecodeBatch:
     """bf16 Llama-style GQA decode: 64 sequences, ctx ~ U[128, 4096], 32 q / 8 kv heads,
     D 128, block_size 16, shuffled blocks from a pool of 1.25x the blocks needed."""
     seed = SEED_BASE + 2 if seed is None else seed
     rng = np.random.Generator(np.random.PCG64(seed))
     ctx = rng.integers(128, 4096, size=num_seqs, endpoint=True)
     return build_decode_batch(name="gqa_decode_bf16", dtype=BF16, context_lens=ctx, num_q_heads=32,
-                              num_kv_heads=8, head_dim=128, block_size=16, seed=seed, poison=poison,
-                              rng=rng)
+                              num_kv_heads=8, head_dim=128, block_size=block_size, seed=seed,
+                              poison=poison, rng=rng, contiguous=contiguous)
 
 
-def long_context(poison=True, seed=None, num_seqs=8, ctx_range=(32768, 200000)) -> DecodeBatch:
+def long_context(poison=True, seed=None, num_seqs=8, ctx_range=(32768, 200000), block_size=16,
+                 contiguous=False) -> DecodeBatch:
     """bf16 long-context decode shaped like one TP=2 shard of the vAttention page's Yi-34B
     example: 8 sequences, ctx ~ U[32768, 200000], 28 q / 4 kv heads, D 128, block_size 16."""
     seed = SEED_BASE + 3 if seed is None else seed
     rng = np.random.Generator(np.random.PCG64(seed))
     ctx = rng.integers(ctx_range[0], ctx_range[1], size=num_seqs, endpoint=True)
     return build_decode_batch(name="long_decode_bf16", dtype=BF16, context_lens=ctx, num_q_heads=28,
-                              num_kv_heads=4, head_dim=128, block_size=16, seed=seed, poison=poison,
-                              rng=rng)
+                              num_kv_heads=4, head_dim=128, block_size=block_size, seed=seed,
+                              poison=poison, rng=rng, contiguous=contiguous)
 
 
 @dataclass
