@@ -152,6 +152,77 @@ def make_workload(name, block_size=16, contiguous=False):
     raise SystemExit(f"unknown workload {name}")
 
 
+def run_spec(args):
+    """Speculative-decode verification: each sequence writes its k + 1 newest tokens and
+    attends with k + 1 causal queries (paged_kv_write + paged_attention_prefill_chunk)."""
+    import torch
+    import paged_kv_cache_79_amd as pkv
+    import workloads as W
+    log("building workload spec")
+    sb = W.spec_decode(poison=False, block_size=args.block_size)
+    pre = sb.prefill
+    nq = sb.draft + 1
+    pool_bytes = 2 * sb.k_pool.nbytes
+    copies = max(2, min(8, int(math.ceil(2.4e9 / max(pool_bytes, 1)))))
+    k0, v0 = _dev(sb.k_pool), _dev(sb.v_pool)
+    pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(copies - 1)]
+    q, cu = _dev(pre.q), _dev(pre.cu_q_lens)
+    tab, ctx = _dev(pre.block_tables), _dev(pre.context_lens)
+    k_new, v_new, slots = _dev(sb.k_new), _dev(sb.v_new), _dev(sb.slot_mapping)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def attend(i):
+        kp, vp = pools[i % copies]
+        pkv.paged_attention_prefill_chunk(out, q, cu, kp, vp, tab, ctx, nq, pre.max_context_len,
+                                          pre.scale)
+
+    def step(i):
+        kp, vp = pools[i % copies]
+        pkv.paged_kv_write(kp, vp, k_new, v_new, slots)
+        attend(i)
+
+    def timed(fn, n):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for i in range(n):
+            fn(i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / n
+
+    for i in range(args.warmup):
+        step(i)
+    ms_step = timed(step, args.steps)
+    runs = [timed(attend, args.steps) for _ in range(3)]
+    att = sorted(runs)[1]
+    byts = kv_bytes(pre.context_lens, pre.num_kv_heads, pre.head_dim, 2)
+    value = byts / (ms_step * 1e-3) / 1e9
+    achieved = byts / (att * 1e-3) / 1e9
+    return {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "spec_decode_bf16", "num_seqs": pre.num_chunks,
+                   "queries_per_seq": nq, "num_q_heads": pre.num_q_heads,
+                   "num_kv_heads": pre.num_kv_heads, "head_dim": pre.head_dim,
+                   "block_size": pre.block_size, "max_context_len": pre.max_context_len,
+                   "mean_context_len": round(float(np.mean(pre.context_lens)), 1),
+                   "pool_copies_rotated": copies},
+        "seqs_per_s": round(pre.num_chunks / (ms_step * 1e-3), 1),
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "kv_bytes_per_step": byts,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "paged_attention_prefill_chunk with k + 1 queries per sequence",
+                     "avg_us": round(att * 1e3, 2), "runs_us": [round(x * 1e3, 2) for x in runs]},
+        "cpu_baseline": None,
+    }
+
+
 def run(args):
     import torch
     import paged_kv_cache_79_amd as pkv
@@ -296,7 +367,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="gqa", choices=["gqa", "long", "prefix_cow", "mixed"])
+    ap.add_argument("--workload", default="gqa", choices=["gqa", "long", "prefix_cow", "mixed", "spec"])
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--layout", default="paged", choices=["paged", "contiguous"],
                     help="contiguous: the unpaged baseline on the same K/V values (gqa, long)")
@@ -308,7 +379,7 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
-    rec = run(args)
+    rec = run_spec(args) if args.workload == "spec" else run(args)
     print(json.dumps(rec), flush=True)
 
 

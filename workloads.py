@@ -448,6 +448,58 @@ def mixed(poison=True, seed=None, num_chunks=4, chunk_len=512, chunk_ctx=(2048, 
     return MixedBatch(decode=dec, prefill=pre, num_decode_tokens=num_decode)
 
 
+@dataclass
+class SpecDecodeBatch:
+    """Multi-token decode (speculative verification): every sequence writes its k + 1
+    newest tokens (the last accepted one and k draft tokens) and attends with k + 1
+    queries at the last k + 1 positions of its context, causally."""
+    prefill: PrefillBatch             # queries [S (k + 1)][Hq][D]; cu_q_lens = (k + 1) * arange
+    k_pool: np.ndarray
+    v_pool: np.ndarray
+    slot_mapping: np.ndarray          # int64 [S (k + 1)]: slots of positions ctx-k-1 .. ctx-1
+    k_new: np.ndarray                 # [S (k + 1)][Hkv][D]
+    v_new: np.ndarray
+    num_blocks: int
+    draft: int                        # k
+
+
+def spec_decode(poison=True, seed=None, num_seqs=64, draft=3, ctx_range=(128, 4096),
+                num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16) -> SpecDecodeBatch:
+    """bf16 speculative-decode verification step shaped like the GQA decode batch:
+    64 sequences with contexts U[128, 4096] that include k = 3 draft tokens (4 queries
+    per sequence), 32 q / 8 kv heads, D 128, block_size 16, shuffled blocks from a pool
+    of 1.25x the blocks needed.  Blocks are reserved for the whole context, draft
+    slots included, before the step writes the k + 1 new tokens."""
+    seed = SEED_BASE + 6 if seed is None else seed
+    rng = np.random.Generator(np.random.PCG64(seed))
+    hq, hkv, d, bs, nq = num_q_heads, num_kv_heads, head_dim, block_size, draft + 1
+    ctx = rng.integers(max(ctx_range[0], nq), ctx_range[1], size=num_seqs, endpoint=True)
+    need = [cdiv(int(c), bs) for c in ctx]
+    num_blocks = math.ceil(1.25 * sum(need))
+    alloc = BlockAllocator(num_blocks, rng.permutation(num_blocks))
+    mb = max(need)
+    tab = np.full((num_seqs, mb), -1, dtype=np.int32)
+    for s in range(num_seqs):
+        tab[s, :need[s]] = alloc.allocate(need[s])
+    st = _storage(BF16)
+    q = _encode(rng.standard_normal((num_seqs * nq, hq, d), dtype=np.float32), BF16)
+    fill = _fill_value(BF16, poison)
+    k_pool = np.full((num_blocks, hkv, bs, d), fill, dtype=st)
+    v_pool = np.full((num_blocks, hkv, bs, d), fill, dtype=st)
+    for s in range(num_seqs):
+        _fill_history(rng, k_pool, v_pool, tab[s], int(ctx[s]) - nq, bs, BF16, hkv, d)
+    new = rng.standard_normal((2, num_seqs * nq, hkv, d), dtype=np.float32)
+    slots = np.concatenate([slots_for_positions(tab[s], np.arange(int(ctx[s]) - nq, int(ctx[s])), bs)
+                            for s in range(num_seqs)]).astype(np.int64)
+    pre = PrefillBatch(dtype=BF16, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=bs,
+                       scale=1.0 / math.sqrt(d),
+                       cu_q_lens=(np.arange(num_seqs + 1) * nq).astype(np.int32),
+                       context_lens=ctx.astype(np.int32), block_tables=tab, q=q)
+    return SpecDecodeBatch(prefill=pre, k_pool=k_pool, v_pool=v_pool, slot_mapping=slots,
+                           k_new=_encode(new[0], BF16), v_new=_encode(new[1], BF16),
+                           num_blocks=num_blocks, draft=draft)
+
+
 def prefill_only(*, seed, dtype=BF16, chunk_lens, contexts, num_q_heads, num_kv_heads, head_dim,
                  block_size, poison=True, pool_factor=1.25):
     """Small chunked-prefill case for tests: every context fully written (chunk included)."""
@@ -484,4 +536,5 @@ WORKLOADS = {
     "long": long_context,
     "prefix_cow": prefix_cow,
     "mixed": mixed,
+    "spec": spec_decode,
 }
