@@ -223,6 +223,52 @@ def run_spec(args):
     }
 
 
+def run_swap(args):
+    """Preemption by swapping: 2048 blocks of the GQA geometry (8 kv heads x 16 tokens x
+    D 128, bf16; 64 KiB of K+V per block) copied device -> pinned host -> device, with
+    scattered device ids (one DMA copy per block) and with contiguous runs."""
+    import torch
+    import paged_kv_cache_79_amd as pkv
+    nb_dev, n, hkv, bs, d = 16384, 2048, 8, 16, 128
+    k = torch.randn((nb_dev, hkv, bs, d), device="cuda").to(torch.bfloat16)
+    v = torch.randn((nb_dev, hkv, bs, d), device="cuda").to(torch.bfloat16)
+    hk = torch.empty((n, hkv, bs, d), dtype=torch.bfloat16, pin_memory=True)
+    hv = torch.empty_like(hk, pin_memory=True)
+    rng = np.random.Generator(np.random.PCG64(79007))
+    scattered = rng.choice(nb_dev, n, replace=False)
+    maps = {"scattered": scattered, "runs": np.arange(n) + 4096}
+    stream = torch.cuda.current_stream()
+    byts = 2 * n * hkv * bs * d * 2
+    res = {}
+    for name, ids in maps.items():
+        out_map = np.stack([ids, np.arange(n)], axis=1)
+        in_map = np.stack([np.arange(n), ids], axis=1)
+        for direction, (dk, dv, sk, sv, mp) in {"out": (hk, hv, k, v, out_map),
+                                               "in": (k, v, hk, hv, in_map)}.items():
+            pkv.swap_blocks(dk, dv, sk, sv, mp)
+            torch.cuda.synchronize()
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            h0 = time.perf_counter()
+            t0.record(stream)
+            reps = max(2, args.steps // 10)
+            for _ in range(reps):
+                pkv.swap_blocks(dk, dv, sk, sv, mp)
+            t1.record(stream)
+            host_s = (time.perf_counter() - h0) / reps
+            torch.cuda.synchronize()
+            ms = t0.elapsed_time(t1) / reps
+            res[f"{name}_{direction}"] = {"ms": round(ms, 4), "GB/s": round(byts / (ms * 1e-3) / 1e9, 2),
+                                          "host_enqueue_ms": round(host_s * 1e3, 3)}
+    best = max(r["GB/s"] for r in res.values())
+    return {"metric": "swap_blocks GB/s (device <-> pinned host), 1xMI355X", "value": best,
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": res["scattered_out"]["ms"], "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "swap", "blocks": n, "bytes_per_direction": byts,
+                       "block_bytes_kv": 2 * hkv * bs * d * 2},
+            "swap": res, "roofline": None, "cpu_baseline": None}
+
+
 def run(args):
     import torch
     import paged_kv_cache_79_amd as pkv
@@ -367,7 +413,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="gqa", choices=["gqa", "long", "prefix_cow", "mixed", "spec"])
+    ap.add_argument("--workload", default="gqa", choices=["gqa", "long", "prefix_cow", "mixed", "spec",
+                                                             "swap"])
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--layout", default="paged", choices=["paged", "contiguous"],
                     help="contiguous: the unpaged baseline on the same K/V values (gqa, long)")
@@ -379,7 +426,8 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
-    rec = run_spec(args) if args.workload == "spec" else run(args)
+    runners = {"spec": run_spec, "swap": run_swap}
+    rec = runners.get(args.workload, run)(args)
     print(json.dumps(rec), flush=True)
 
 

@@ -61,7 +61,8 @@ typedef enum pkv_status {
     PKV_ERR_DTYPE = 3,         /* unknown pkv_dtype */
     PKV_ERR_UNSUPPORTED = 4,   /* valid but not implemented (head_dim, block_size, group size, dtype) */
     PKV_ERR_WORKSPACE = 5,     /* workspace missing or smaller than required */
-    PKV_ERR_LAUNCH = 6         /* the HIP runtime refused a launch */
+    PKV_ERR_LAUNCH = 6,        /* the HIP runtime refused a launch or copy */
+    PKV_ERR_NO_BLOCKS = 7      /* block pool: not enough free blocks (nothing was taken) */
 } pkv_status;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -195,6 +196,77 @@ pkv_status paged_attention_prefill_chunk(pkv_dtype dtype, void* out, const void*
                                          int32_t max_blocks_per_seq, const int32_t* context_lens,
                                          int32_t max_context_len, int32_t num_q_heads, float scale,
                                          hipStream_t stream);
+
+/*
+ * swap_blocks -- preemption by swapping ("2.1 PagedAttention", section 7: a
+ * request's KV blocks are copied from GPU memory to CPU memory and back when it
+ * resumes).  For each pair (src, dst) of block_mapping, the whole block (all kv
+ * heads, K and V) src of the source pools is copied to block dst of the
+ * destination pools.  Either side may be device memory or pinned host memory
+ * (hipHostMalloc, torch's pin_memory); the copies are DMA transfers enqueued on
+ * the stream (runs of consecutive pairs become one transfer).
+ *   dst_k, dst_v      [dst_num_blocks][num_kv_heads][block_size][head_dim]
+ *   src_k, src_v      [src_num_blocks][num_kv_heads][block_size][head_dim]
+ *   block_mapping     int64 [num_pairs][2] (src, dst) in HOST memory, read before
+ *                     the call returns; destinations distinct.
+ * Errors: PKV_ERR_SHAPE for an id out of range (nothing enqueued); PKV_ERR_LAUNCH if
+ * the runtime refuses a copy (earlier copies of the call may have been enqueued).
+ */
+pkv_status swap_blocks(pkv_dtype dtype, void* dst_k, void* dst_v, int32_t dst_num_blocks,
+                       const void* src_k, const void* src_v, int32_t src_num_blocks,
+                       int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
+                       const int64_t* block_mapping, int32_t num_pairs, hipStream_t stream);
+
+/*
+ * Host block manager ("2.1 PagedAttention", the V1 engine walk-through: the block
+ * pool with per-block reference counts and a doubly linked free queue; "Inside
+ * vLLM, part 2": prefix caching by chained block hashes).  Pure host code; one pool
+ * per KV cache; not thread-safe (one caller at a time).
+ *
+ * Free queue: initially blocks 0..n-1 in order.  allocate takes blocks from its
+ * head (a block that still carried a prefix hash loses it: its contents will be
+ * overwritten).  free decrements counts in the order given -- a request passes
+ * its blocks tail first -- and a block reaching zero goes to the queue's tail if
+ * it carries a hash (kept longer, reusable) or to its head otherwise (reused
+ * first).  touch revives blocks on a prefix-cache hit: a block at zero leaves the
+ * queue (wherever it is) and every count goes up by one.
+ */
+typedef struct pkv_block_pool pkv_block_pool;
+
+/* A pool of num_blocks blocks, all free; NULL if num_blocks <= 0 or out of memory. */
+pkv_block_pool* pkv_pool_create(int32_t num_blocks);
+void pkv_pool_destroy(pkv_block_pool* pool);
+/* Free blocks (-1 for a NULL pool). */
+int32_t pkv_pool_num_free(const pkv_block_pool* pool);
+/* Reference count of block id (-1 if out of range). */
+int32_t pkv_pool_ref_count(const pkv_block_pool* pool, int32_t id);
+/* n blocks from the head of the free queue into ids[n], each with count 1;
+ * PKV_ERR_NO_BLOCKS (and nothing taken) when fewer than n are free. */
+pkv_status pkv_pool_allocate(pkv_block_pool* pool, int32_t n, int32_t* ids);
+/* Drop one reference per listed id (PKV_ERR_SHAPE, nothing changed, if an id is out
+ * of range or listed more often than it is referenced). */
+pkv_status pkv_pool_free(pkv_block_pool* pool, const int32_t* ids, int32_t n);
+/* Add one reference per listed id; blocks at zero leave the free queue. */
+pkv_status pkv_pool_touch(pkv_block_pool* pool, const int32_t* ids, int32_t n);
+/* Index full blocks under their hashes.  A block that already has a hash, or a hash
+ * already held by another block, is left as it is. */
+pkv_status pkv_pool_cache_blocks(pkv_block_pool* pool, const int32_t* ids,
+                                 const uint64_t* hashes, int32_t n);
+/* Longest cached prefix: the number k of leading hashes[] found (stopping at the
+ * first miss), their blocks in ids[0..k); -1 on a bad argument. */
+int32_t pkv_pool_longest_hit(const pkv_block_pool* pool, const uint64_t* hashes, int32_t n,
+                             int32_t* ids);
+/* Copy-on-write trigger ("2.1 PagedAttention", section 6) before writing into block
+ * id: sole owner (count 1) -> *out_id = id, *copy_needed = 0; shared -> a fresh
+ * block is allocated, id loses the writer's reference, *out_id = the fresh block and
+ * *copy_needed = 1 (the caller copies with copy_blocks and re-points its table).
+ * PKV_ERR_NO_BLOCKS when no block is free (nothing changed). */
+pkv_status pkv_pool_cow(pkv_block_pool* pool, int32_t id, int32_t* out_id, int32_t* copy_needed);
+/* The free queue from head to tail into ids[0..capacity); returns its length. */
+int32_t pkv_pool_free_queue(const pkv_block_pool* pool, int32_t* ids, int32_t capacity);
+/* Chained block hash: 64-bit FNV-1a over the parent hash (8 bytes, little endian)
+ * followed by the block's token ids (4 bytes each, little endian). */
+uint64_t pkv_block_hash(uint64_t parent, const int32_t* tokens, int32_t n);
 
 #ifdef __cplusplus
 }

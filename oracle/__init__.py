@@ -18,7 +18,8 @@ Parity status of each function is listed in ``PINS`` below.
 """
 from .paged import (  # noqa: F401
     BF16, F32, widen, translate, slot_of, gather_kv, kv_head_of, attend, decode,
-    decode_contiguous, prefill_chunk, kv_write, copy_blocks, partition_partials, lse_merge, kv_size_bytes,
+    decode_contiguous, prefill_chunk, kv_write, copy_blocks, swap_blocks, partition_partials,
+    lse_merge, kv_size_bytes,
     blocks_needed, tail_waste,
 )
 
@@ -35,6 +36,10 @@ PINS = {
                      "every row equals decode on the truncated context",
     "kv_write": "worked example slots; whole-pool bit comparison; negative slots skipped",
     "copy_blocks": "snapshot semantics on hand-built pairs; CoW divergence scenario",
+    "swap_blocks": "bit copies between two pools on hand-built pairs; a round trip restores "
+                   "the original blocks",
+    "block_pool.BlockPoolModel/block_hash": "the pages' pool rules as scenarios and published "
+                                            "FNV-1a vectors (tests/test_block_pool.py)",
     "partition_partials/lse_merge": "merge over any partition equals the unsplit result",
     "kv_size_bytes": "Yi-34B TP=2 sizing printed on the vAttention page",
     "blocks_needed/tail_waste": "waste bound of the 2.1 chapter, section 4",

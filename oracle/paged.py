@@ -277,6 +277,18 @@ def copy_blocks(pool, block_mapping):
 # --------------------------------------------------------------------------
 # KV size model (vAttention page, opening section)
 # --------------------------------------------------------------------------
+def swap_blocks(dst_pool, src_pool, block_mapping):
+    """Swapping ("2.1 PagedAttention", section 7: a preempted request's KV blocks are
+    copied from GPU memory to CPU memory and copied back on resume): for each (src, dst)
+    pair, block dst of the destination pool becomes a bit copy of block src of the source
+    pool.  Returns the new destination pool; the source is unchanged."""
+    out = np.array(dst_pool, copy=True)
+    src = np.asarray(src_pool)
+    for s, d in np.asarray(block_mapping, dtype=np.int64).reshape(-1, 2):
+        _bits(out[d])[...] = _bits(src[s])
+    return out
+
+
 def kv_size_bytes(layers: int, length: int, kv_heads: int, head_dim: int, elem_bytes: int) -> int:
     """M_KV = 2 N L H D P: K and V for N layers, L tokens, H KV heads of D elements of
     P bytes each."""

@@ -24,9 +24,23 @@ EXPORTS = (
     "paged_attention_decode",
     "contiguous_attention_decode",
     "paged_attention_prefill_chunk",
+    "swap_blocks",
+    "pkv_pool_create",
+    "pkv_pool_destroy",
+    "pkv_pool_num_free",
+    "pkv_pool_ref_count",
+    "pkv_pool_allocate",
+    "pkv_pool_free",
+    "pkv_pool_touch",
+    "pkv_pool_cache_blocks",
+    "pkv_pool_longest_hit",
+    "pkv_pool_cow",
+    "pkv_pool_free_queue",
+    "pkv_block_hash",
 )
 
 PKV_F32, PKV_BF16 = 0, 1
+PKV_ERR_NO_BLOCKS = 7
 
 _lib = None
 
@@ -66,6 +80,34 @@ def load_library(path: Optional[str] = None):
     lib.paged_attention_prefill_chunk.argtypes = [ctypes.c_int, VP, VP, VP, I32, I32, VP, VP, I32, I32,
                                                   I32, I32, VP, I32, VP, I32, I32, F, VP]
     lib.paged_attention_prefill_chunk.restype = ctypes.c_int
+    U64 = ctypes.c_uint64
+    lib.swap_blocks.argtypes = [ctypes.c_int, VP, VP, I32, VP, VP, I32, I32, I32, I32, VP, I32, VP]
+    lib.swap_blocks.restype = ctypes.c_int
+    lib.pkv_pool_create.argtypes = [I32]
+    lib.pkv_pool_create.restype = VP
+    lib.pkv_pool_destroy.argtypes = [VP]
+    lib.pkv_pool_destroy.restype = None
+    for fn in ("pkv_pool_num_free",):
+        getattr(lib, fn).argtypes = [VP]
+        getattr(lib, fn).restype = I32
+    lib.pkv_pool_ref_count.argtypes = [VP, I32]
+    lib.pkv_pool_ref_count.restype = I32
+    lib.pkv_pool_allocate.argtypes = [VP, I32, VP]
+    lib.pkv_pool_allocate.restype = ctypes.c_int
+    lib.pkv_pool_free.argtypes = [VP, VP, I32]
+    lib.pkv_pool_free.restype = ctypes.c_int
+    lib.pkv_pool_touch.argtypes = [VP, VP, I32]
+    lib.pkv_pool_touch.restype = ctypes.c_int
+    lib.pkv_pool_cache_blocks.argtypes = [VP, VP, VP, I32]
+    lib.pkv_pool_cache_blocks.restype = ctypes.c_int
+    lib.pkv_pool_longest_hit.argtypes = [VP, VP, I32, VP]
+    lib.pkv_pool_longest_hit.restype = I32
+    lib.pkv_pool_cow.argtypes = [VP, I32, VP, VP]
+    lib.pkv_pool_cow.restype = ctypes.c_int
+    lib.pkv_pool_free_queue.argtypes = [VP, VP, I32]
+    lib.pkv_pool_free_queue.restype = I32
+    lib.pkv_block_hash.argtypes = [U64, VP, I32]
+    lib.pkv_block_hash.restype = U64
     del I64
     if path is None:
         _lib = lib
@@ -249,3 +291,126 @@ def paged_attention_prefill_chunk(out, q, cu_q_lens, k_pool, v_pool, block_table
         _dtype_code(q), _ptr(out), _ptr(q), _ptr(cu_q_lens), nc, int(max_q_len), _ptr(k_pool),
         _ptr(v_pool), nb, hkv, bs, d, _ptr(block_tables), int(block_tables.shape[1]),
         _ptr(context_lens), int(max_context_len), int(q.shape[1]), float(scale), _stream(stream)))
+
+
+# ----------------------------------------------------------------------------
+# swapping and the host block manager
+# ----------------------------------------------------------------------------
+def swap_blocks(dst_k, dst_v, src_k, src_v, block_mapping, stream=None) -> None:
+    """Copy whole blocks src -> dst (pairs of block_mapping, a host int64 [n][2] array)
+    between pools in device memory or pinned host memory, as DMA copies on the stream."""
+    import numpy as np
+    for n, t in (("dst_k", dst_k), ("dst_v", dst_v), ("src_k", src_k), ("src_v", src_v)):
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+        if not t.is_cuda and not t.is_pinned():
+            raise ValueError(f"{n} must be device memory or pinned host memory")
+    if dst_k.dim() != 4 or src_k.dim() != 4 or dst_k.shape[1:] != src_k.shape[1:] or \
+            dst_v.shape != dst_k.shape or src_v.shape != src_k.shape or dst_k.dtype != src_k.dtype:
+        raise ValueError("pools must be [num_blocks][num_kv_heads][block_size][head_dim] of one dtype")
+    m = np.ascontiguousarray(np.asarray(block_mapping, dtype=np.int64).reshape(-1, 2))
+    _, hkv, bs, d = (int(x) for x in src_k.shape)
+    lib = load_library()
+    _check("swap_blocks", lib.swap_blocks(
+        _dtype_code(src_k), _ptr(dst_k), _ptr(dst_v), int(dst_k.shape[0]), _ptr(src_k), _ptr(src_v),
+        int(src_k.shape[0]), hkv, bs, d, m.ctypes.data if m.size else None, int(m.shape[0]),
+        _stream(stream)))
+
+
+def block_hash(parent: int, tokens) -> int:
+    """Chained hash of a full block: FNV-1a 64 over the parent hash and the token ids."""
+    import numpy as np
+    t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+    return int(load_library().pkv_block_hash(ctypes.c_uint64(parent & (2**64 - 1)),
+                                             t.ctypes.data if t.size else None, int(t.size)))
+
+
+class BlockPool:
+    """The library's host block manager (pkv_pool_*): reference counts, the doubly
+    linked free queue, prefix-hash index and the copy-on-write trigger."""
+
+    def __init__(self, num_blocks: int):
+        self._lib = load_library()
+        self._h = self._lib.pkv_pool_create(int(num_blocks))
+        if not self._h:
+            raise ValueError("pkv_pool_create failed (num_blocks must be positive)")
+
+    def close(self):
+        if self._h:
+            self._lib.pkv_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @staticmethod
+    def _ids(ids):
+        import numpy as np
+        a = np.ascontiguousarray(np.asarray(ids, dtype=np.int32).reshape(-1))
+        return a, (a.ctypes.data if a.size else None), int(a.size)
+
+    @property
+    def num_free(self) -> int:
+        return int(self._lib.pkv_pool_num_free(self._h))
+
+    def ref_count(self, block_id: int) -> int:
+        return int(self._lib.pkv_pool_ref_count(self._h, int(block_id)))
+
+    def allocate(self, n: int):
+        """n blocks from the head of the free queue, or None when fewer are free."""
+        import numpy as np
+        out = np.zeros(max(int(n), 1), dtype=np.int32)
+        st = self._lib.pkv_pool_allocate(self._h, int(n), out.ctypes.data)
+        if st == PKV_ERR_NO_BLOCKS:
+            return None
+        _check("pkv_pool_allocate", st)
+        return out[:int(n)].tolist()
+
+    def free(self, ids) -> None:
+        a, p, n = self._ids(ids)
+        _check("pkv_pool_free", self._lib.pkv_pool_free(self._h, p, n))
+
+    def touch(self, ids) -> None:
+        a, p, n = self._ids(ids)
+        _check("pkv_pool_touch", self._lib.pkv_pool_touch(self._h, p, n))
+
+    def cache_blocks(self, ids, hashes) -> None:
+        import numpy as np
+        a, p, n = self._ids(ids)
+        h = np.ascontiguousarray(np.asarray([x & (2**64 - 1) for x in hashes], dtype=np.uint64))
+        if h.size != n:
+            raise ValueError("one hash per block")
+        _check("pkv_pool_cache_blocks", self._lib.pkv_pool_cache_blocks(
+            self._h, p, h.ctypes.data if h.size else None, n))
+
+    def longest_hit(self, hashes):
+        """Blocks of the longest prefix of hashes that is cached."""
+        import numpy as np
+        h = np.ascontiguousarray(np.asarray([x & (2**64 - 1) for x in hashes], dtype=np.uint64))
+        out = np.zeros(max(h.size, 1), dtype=np.int32)
+        k = self._lib.pkv_pool_longest_hit(self._h, h.ctypes.data if h.size else None, int(h.size),
+                                           out.ctypes.data)
+        if k < 0:
+            raise ValueError("pkv_pool_longest_hit: bad argument")
+        return out[:k].tolist()
+
+    def cow(self, block_id: int):
+        """(block to write, copy needed) before writing into block_id; None if no block
+        is free for the private copy."""
+        a = ctypes.c_int32(0)
+        c = ctypes.c_int32(0)
+        st = self._lib.pkv_pool_cow(self._h, int(block_id), ctypes.byref(a), ctypes.byref(c))
+        if st == PKV_ERR_NO_BLOCKS:
+            return None
+        _check("pkv_pool_cow", st)
+        return int(a.value), bool(c.value)
+
+    def free_queue(self):
+        import numpy as np
+        n = self._lib.pkv_pool_free_queue(self._h, None, 0)
+        out = np.zeros(max(n, 1), dtype=np.int32)
+        self._lib.pkv_pool_free_queue(self._h, out.ctypes.data, n)
+        return out[:n].tolist()

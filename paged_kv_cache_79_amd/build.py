@@ -20,7 +20,8 @@ OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
 ARCH = "gfx950"
 
-SOURCES = ["pkv_api.hip", "pkv_write_copy.hip", "pkv_decode.hip", "pkv_prefill.hip"]
+SOURCES = ["pkv_api.hip", "pkv_write_copy.hip", "pkv_decode.hip", "pkv_prefill.hip",
+           "pkv_block_pool.cpp"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

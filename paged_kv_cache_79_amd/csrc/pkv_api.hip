@@ -109,7 +109,8 @@ const char* pkv_status_string(pkv_status s) {
         case PKV_ERR_DTYPE: return "PKV_ERR_DTYPE: unknown element type";
         case PKV_ERR_UNSUPPORTED: return "PKV_ERR_UNSUPPORTED: configuration not implemented";
         case PKV_ERR_WORKSPACE: return "PKV_ERR_WORKSPACE: workspace missing or too small";
-        case PKV_ERR_LAUNCH: return "PKV_ERR_LAUNCH: kernel launch failed";
+        case PKV_ERR_LAUNCH: return "PKV_ERR_LAUNCH: kernel launch or copy failed";
+        case PKV_ERR_NO_BLOCKS: return "PKV_ERR_NO_BLOCKS: not enough free blocks in the pool";
     }
     return "PKV_ERR_UNKNOWN";
 }
@@ -158,6 +159,89 @@ size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_he
                                               int32_t max_context_len, int32_t partition_tokens) {
     return decode_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
                             partition_tokens);
+}
+
+pkv_status swap_blocks(pkv_dtype dtype, void* dst_k, void* dst_v, int32_t dst_num_blocks,
+                       const void* src_k, const void* src_v, int32_t src_num_blocks,
+                       int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
+                       const int64_t* block_mapping, int32_t num_pairs, hipStream_t stream) {
+    PoolGeom g;
+    const int32_t nb = std::max(dst_num_blocks, src_num_blocks);
+    const pkv_status st = check_geom(dtype, nb, num_kv_heads, block_size, head_dim, &g);
+    if (st != PKV_OK) return st;
+    if (dst_num_blocks <= 0 || src_num_blocks <= 0 || num_pairs < 0) return PKV_ERR_SHAPE;
+    if (num_pairs == 0) return PKV_OK;
+    if (!dst_k || !dst_v || !src_k || !src_v || !block_mapping) return PKV_ERR_NULL;
+    for (int32_t i = 0; i < num_pairs; ++i) {
+        const int64_t s = block_mapping[2 * i], d = block_mapping[2 * i + 1];
+        if (s < 0 || s >= src_num_blocks || d < 0 || d >= dst_num_blocks) return PKV_ERR_SHAPE;
+    }
+    const size_t blk = (size_t)g.block_stride_bytes;
+    // runs of pairs whose sources and destinations both advance by one block
+    int32_t runs = 0;
+    for (int32_t i = 0; i < num_pairs; ++i)
+        if (i == 0 || block_mapping[2 * i] != block_mapping[2 * i - 2] + 1 ||
+            block_mapping[2 * i + 1] != block_mapping[2 * i - 1] + 1)
+            ++runs;
+    // Scattered blocks: one copy kernel over device pointers, if every pool is device
+    // memory or pinned host memory with a device mapping (a DMA copy per block costs
+    // ~10 us of engine overhead).  Long runs: DMA copies.
+    void* dev_ptr[4] = {dst_k, dst_v, const_cast<void*>(src_k), const_cast<void*>(src_v)};
+    bool kernel_ok = runs * 4 > num_pairs;
+    for (int i = 0; i < 4 && kernel_ok; ++i) {
+        hipPointerAttribute_t at;
+        if (hipPointerGetAttributes(&at, dev_ptr[i]) != hipSuccess) {
+            (void)hipGetLastError();
+            kernel_ok = false;
+            break;
+        }
+        if (at.type == hipMemoryTypeHost) {
+            void* d = nullptr;
+            if (hipHostGetDevicePointer(&d, dev_ptr[i], 0) != hipSuccess || !d) {
+                (void)hipGetLastError();
+                kernel_ok = false;
+                break;
+            }
+            dev_ptr[i] = d;
+        } else if (at.type != hipMemoryTypeDevice) {
+            kernel_ok = false;
+        }
+    }
+    if (kernel_ok) {
+        SwapArgs a;
+        a.dst_k = static_cast<char*>(dev_ptr[0]);
+        a.dst_v = static_cast<char*>(dev_ptr[1]);
+        a.src_k = static_cast<const char*>(dev_ptr[2]);
+        a.src_v = static_cast<const char*>(dev_ptr[3]);
+        a.block_bytes = (int64_t)blk;
+        for (int32_t i0 = 0; i0 < num_pairs; i0 += kSwapPairsPerLaunch) {
+            a.num_pairs = std::min(kSwapPairsPerLaunch, num_pairs - i0);
+            for (int32_t k = 0; k < a.num_pairs; ++k) {
+                a.src[k] = (int32_t)block_mapping[2 * (i0 + k)];
+                a.dst[k] = (int32_t)block_mapping[2 * (i0 + k) + 1];
+            }
+            if (launch_swap(a, stream) != hipSuccess) return PKV_ERR_LAUNCH;
+        }
+        return PKV_OK;
+    }
+    for (int32_t i = 0; i < num_pairs;) {
+        int32_t j = i + 1;
+        while (j < num_pairs && block_mapping[2 * j] == block_mapping[2 * j - 2] + 1 &&
+               block_mapping[2 * j + 1] == block_mapping[2 * j - 1] + 1)
+            ++j;
+        const size_t off_s = (size_t)block_mapping[2 * i] * blk;
+        const size_t off_d = (size_t)block_mapping[2 * i + 1] * blk;
+        const size_t bytes = (size_t)(j - i) * blk;
+        if (hipMemcpyAsync(static_cast<char*>(dst_k) + off_d,
+                           static_cast<const char*>(src_k) + off_s, bytes, hipMemcpyDefault,
+                           stream) != hipSuccess ||
+            hipMemcpyAsync(static_cast<char*>(dst_v) + off_d,
+                           static_cast<const char*>(src_v) + off_s, bytes, hipMemcpyDefault,
+                           stream) != hipSuccess)
+            return PKV_ERR_LAUNCH;
+        i = j;
+    }
+    return PKV_OK;
 }
 
 pkv_status paged_attention_decode(pkv_dtype dtype, void* out, const void* q, const void* k_pool,

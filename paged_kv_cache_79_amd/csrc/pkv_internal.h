@@ -34,6 +34,21 @@ struct CopyArgs {
     PoolGeom g;
 };
 
+// swap_blocks through a copy kernel: pools are device pointers (pinned host pools
+// through their device mapping); up to kSwapPairsPerLaunch (src, dst) pairs travel in
+// the kernel arguments.
+constexpr int kSwapPairsPerLaunch = 240;
+struct SwapArgs {
+    char* dst_k;
+    char* dst_v;
+    const char* src_k;
+    const char* src_v;
+    int64_t block_bytes;
+    int32_t num_pairs;
+    int32_t src[kSwapPairsPerLaunch];
+    int32_t dst[kSwapPairsPerLaunch];
+};
+
 struct DecodeArgs {
     void* out;
     const void* q;
@@ -91,6 +106,7 @@ struct PrefillArgs {
 
 hipError_t launch_kv_write(const WriteArgs& a, hipStream_t st);
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t st);
+hipError_t launch_swap(const SwapArgs& a, hipStream_t st);
 // is_bf16 selects the element type; group = num_q_heads / num_kv_heads (1..8).
 hipError_t launch_decode(const DecodeArgs& a, bool is_bf16, int head_dim, int group,
                          int num_seqs, hipStream_t st);

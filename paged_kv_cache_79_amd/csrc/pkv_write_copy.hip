@@ -58,6 +58,27 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a) {
     for (; i < n16; i += 256) d[i] = s[i];
 }
 
+// One workgroup per (pair, K or V): a whole block between two pools, either of which
+// may be pinned host memory seen through its device mapping (PCIe / xGMI traffic).
+__global__ __launch_bounds__(256) void swap_kernel(SwapArgs a) {
+    const int p = blockIdx.x;
+    const int64_t src = a.src[p], dst = a.dst[p];
+    const char* sp = (blockIdx.y ? a.src_v : a.src_k) + src * a.block_bytes;
+    char* dp = (blockIdx.y ? a.dst_v : a.dst_k) + dst * a.block_bytes;
+    const uint4* s = reinterpret_cast<const uint4*>(sp);
+    uint4* d = reinterpret_cast<uint4*>(dp);
+    const int n16 = (int)(a.block_bytes >> 4);
+    int i = threadIdx.x;
+    for (; i + 3 * 256 < n16; i += 4 * 256) {
+        const uint4 x0 = s[i], x1 = s[i + 256], x2 = s[i + 512], x3 = s[i + 768];
+        d[i] = x0;
+        d[i + 256] = x1;
+        d[i + 512] = x2;
+        d[i + 768] = x3;
+    }
+    for (; i < n16; i += 256) d[i] = s[i];
+}
+
 hipError_t launch_kv_write(const WriteArgs& a, hipStream_t st) {
     const int64_t work = (int64_t)a.num_tokens * a.g.num_kv_heads * (a.g.row_bytes >> 4);
     if (work == 0) return hipSuccess;
@@ -69,6 +90,12 @@ hipError_t launch_kv_write(const WriteArgs& a, hipStream_t st) {
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t st) {
     if (a.num_pairs == 0) return hipSuccess;
     hipLaunchKernelGGL(copy_blocks_kernel, dim3(a.num_pairs, 2), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_swap(const SwapArgs& a, hipStream_t st) {
+    if (a.num_pairs <= 0) return hipSuccess;
+    hipLaunchKernelGGL(swap_kernel, dim3(a.num_pairs, 2), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

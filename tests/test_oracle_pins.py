@@ -181,6 +181,21 @@ def pin_contiguous_decode(seed=3, ctx=(0, 1, 9, 64, 100), hq=6, hkv=3, d=8, L=12
     np.testing.assert_allclose(got, paged, rtol=1e-12, atol=1e-12)
 
 
+def pin_swap_round_trip():
+    """Swap-out copies the listed device blocks into host blocks bit for bit; swapping
+    them back into other device blocks restores their contents; nothing else changes."""
+    rng = np.random.default_rng(8)
+    dev_pool = rng.standard_normal((6, 2, 4, 3)).astype(np.float32)
+    host_pool = np.full((3, 2, 4, 3), np.nan, np.float32)
+    out = O.swap_blocks(host_pool, dev_pool, [[4, 0], [1, 2]])
+    assert np.array_equal(out[0].view(np.uint32), dev_pool[4].view(np.uint32))
+    assert np.array_equal(out[2].view(np.uint32), dev_pool[1].view(np.uint32))
+    assert np.isnan(out[1]).all()
+    back = O.swap_blocks(np.zeros_like(dev_pool), out, [[0, 5], [2, 0]])
+    assert np.array_equal(back[5], dev_pool[4]) and np.array_equal(back[0], dev_pool[1])
+    assert (back[1:5] == 0).all()
+
+
 def relabel(pool_list, tables, perm):
     """Move physical block b to perm[b] and rewrite the tables to match."""
     outs = []
@@ -395,7 +410,7 @@ PINS = [pin_worked_example, pin_worked_example_write_gather, pin_bf16_widening,
         pin_decode_vs_library, pin_permutation_invariance, pin_closed_forms, pin_one_hot_probe,
         pin_nan_poison, pin_prefix_sharing, pin_cow_divergence, pin_copy_blocks_snapshot,
         pin_prefill_vs_library, pin_lse_merge, pin_kv_size_model, pin_waste_bound,
-        pin_contiguous_decode]
+        pin_contiguous_decode, pin_swap_round_trip]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
