@@ -1,7 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark of the paged KV-cache hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gqa|long|prefix_cow|mixed]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gqa|long|prefix_cow|mixed|spec|swap]
+                    [--layout paged|contiguous] [--block-size 8|16|32] [--shared-prefix]
 
 One step is one pass of the path over one synthetic batch: the step's cache
 write (paged_kv_write) followed by paged decode attention (split-context
@@ -40,6 +41,13 @@ def kv_bytes(context_lens, num_kv_heads, head_dim, elem) -> int:
     """Algorithmic bytes of one decode call: K and V of every valid token, each read
     once per (sequence, kv head) -- 2*N*L*H*D*P of the vAttention page with N = 1."""
     return int(2 * np.asarray(context_lens, dtype=np.int64).sum() * num_kv_heads * head_dim * elem)
+
+
+def shared_kv_bytes(context_lens, prefix_len, num_kv_heads, head_dim, elem) -> int:
+    """Algorithmic bytes of a decode whose sequences all share their first prefix_len
+    tokens: the prefix K/V once per kv head, then each sequence's own tokens."""
+    own = np.asarray(context_lens, dtype=np.int64) - prefix_len
+    return int(2 * (prefix_len + own.sum()) * num_kv_heads * head_dim * elem)
 
 
 def prefill_flops(pre) -> int:
@@ -211,7 +219,9 @@ def run_spec(args):
                    "num_kv_heads": pre.num_kv_heads, "head_dim": pre.head_dim,
                    "block_size": pre.block_size, "max_context_len": pre.max_context_len,
                    "mean_context_len": round(float(np.mean(pre.context_lens)), 1),
-                   "pool_copies_rotated": copies},
+                   "pool_copies_rotated": copies,
+                   **({"decode": f"shared prefix: one group of {b.num_seqs}, "
+                                 f"{shared['plen']}-token prefix"} if shared else {})},
         "seqs_per_s": round(pre.num_chunks / (ms_step * 1e-3), 1),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "kv_bytes_per_step": byts,
@@ -300,9 +310,21 @@ def run(args):
     pt = args.partition_tokens            # 0: balanced split over the resident waves
     ws_bytes = pkv.paged_attention_decode_workspace_bytes(b.num_seqs, b.num_q_heads, b.num_kv_heads,
                                                           b.head_dim, b.max_context_len, pt)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     extra = wl["extra"]
     cow_map = _dev(extra.block_mapping) if args.workload == "prefix_cow" else None
+    shared = None
+    if args.shared_prefix:
+        if args.workload != "prefix_cow" or pt != 0:
+            raise SystemExit("--shared-prefix applies to the prefix_cow workload (balanced split)")
+        # one group of every sequence; the blocks still shared after copy-on-write
+        plen = (len(extra.prefix_blocks) - 1) * b.block_size
+        S = b.num_seqs
+        shared = dict(plen=plen, seq_prefix=_dev(np.full(S, plen, np.int32)),
+                      first=_dev(np.array([0], np.int32)), num=_dev(np.array([S], np.int32)),
+                      pre=_dev(np.array([plen], np.int32)))
+        ws_bytes = pkv.paged_attention_decode_shared_prefix_workspace_bytes(
+            b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim, b.max_context_len, plen)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     pre = wl["prefill"]
     if pre is not None:
         pq, pcu = _dev(pre.q), _dev(pre.cu_q_lens)
@@ -316,6 +338,12 @@ def run(args):
         if contig:
             pkv.contiguous_attention_decode(out, q, kp, vp, ctx, b.max_context_len, b.scale,
                                             workspace=ws)
+            return
+        if shared is not None:
+            pkv.paged_attention_decode_shared_prefix(
+                out, q, kp, vp, tables, ctx, b.max_context_len, b.scale, shared["seq_prefix"],
+                shared["first"], shared["num"], shared["pre"], b.num_seqs, shared["plen"],
+                workspace=ws)
             return
         pkv.paged_attention_decode(out, q, kp, vp, tables, ctx, b.max_context_len, b.scale,
                                    partition_tokens=pt, workspace=ws)
@@ -354,7 +382,11 @@ def run(args):
     dec_avg = sorted(dec_runs)[1]
     byts = kv_bytes(b.context_lens, b.num_kv_heads, b.head_dim, elem)
     value = byts / (ms_step * 1e-3) / 1e9
-    achieved = byts / (dec_avg * 1e-3) / 1e9
+    # the roofline counts what the path has to read: with a shared prefix its K/V once
+    # per kv head, plus every sequence's own tokens
+    unique = byts if shared is None else shared_kv_bytes(b.context_lens, shared["plen"],
+                                                         b.num_kv_heads, b.head_dim, elem)
+    achieved = unique / (dec_avg * 1e-3) / 1e9
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -382,9 +414,12 @@ def run(args):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic(b.name) if pt == 0 and not contig
-                                and args.block_size == 16 else None,
-                     "kernel": ("contiguous_attention_decode" if contig else "paged_attention_decode")
-                               + " (attention kernel + merge kernel)",
+                                and args.block_size == 16 and shared is None else None,
+                     "kernel": ("contiguous_attention_decode" if contig else
+                                "paged_attention_decode_shared_prefix (prefix pass + "
+                                "attention kernel + merge kernel)" if shared else
+                                "paged_attention_decode (attention kernel + merge kernel)"),
+                     "algorithmic_bytes": unique,
                      "avg_us": round(dec_avg * 1e3, 2),
                      "runs_us": [round(x * 1e3, 2) for x in dec_runs]},
     }
@@ -420,6 +455,8 @@ def main():
                     help="contiguous: the unpaged baseline on the same K/V values (gqa, long)")
     ap.add_argument("--block-size", type=int, default=16, choices=[8, 16, 32],
                     help="pool block size of the gqa and long workloads")
+    ap.add_argument("--shared-prefix", action="store_true",
+                    help="prefix_cow: decode through the shared-prefix path (prefix read once)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

@@ -172,6 +172,45 @@ pkv_status contiguous_attention_decode(pkv_dtype dtype, void* out, const void* q
                                        size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * paged_attention_decode_shared_prefix -- decode attention for batches in which
+ * groups of sequences share the physical blocks of a common prefix ("2.1
+ * PagedAttention", section 6: several block tables point at the same blocks, read
+ * only, e.g. one system prompt).  The result is that of paged_attention_decode on
+ * the same tables; what changes is the traffic: each group's prefix K/V is read once
+ * per kv head for up to 128/G members at a time (a dense product on the matrix
+ * cores) instead of once per member, and each member's own tokens after the prefix
+ * go through the balanced decode, which merges both by log-sum-exp.
+ *
+ * Groups (device arrays, num_groups entries): members are the consecutive sequences
+ * group_first_seq[g] .. group_first_seq[g] + group_num_seqs[g] - 1 (groups do not
+ * overlap), whose first group_prefix_lens[g] tokens (rounded down to whole blocks)
+ * sit in the same physical blocks, read through the table of the first member.
+ * seq_prefix_lens[s] (device, [num_seqs]) is the prefix length of the group of s,
+ * 0 for a sequence in no group; a member's context must not end before its
+ * prefix (it may end at it: the result is then the prefix's alone).
+ * max_group_seqs >= every group_num_seqs[g] and max_prefix_len >= every
+ * group_prefix_lens[g] are host bounds (they size the prefix pass).  These device
+ * contents are preconditions; violating them gives unspecified output but never an
+ * out-of-range access.  bf16 only.  With num_groups == 0 this is
+ * paged_attention_decode.
+ *
+ * Workspace: paged_attention_decode_shared_prefix_workspace_bytes(); its contents
+ * need no initialisation.
+ */
+size_t paged_attention_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                                            int32_t num_kv_heads, int32_t head_dim,
+                                                            int32_t max_context_len,
+                                                            int32_t max_prefix_len);
+pkv_status paged_attention_decode_shared_prefix(
+    pkv_dtype dtype, void* out, const void* q, const void* k_pool, const void* v_pool,
+    int32_t num_blocks, int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    int32_t num_seqs, int32_t max_context_len, int32_t num_q_heads, float scale,
+    const int32_t* seq_prefix_lens, const int32_t* group_first_seq, const int32_t* group_num_seqs,
+    const int32_t* group_prefix_lens, int32_t num_groups, int32_t max_group_seqs,
+    int32_t max_prefix_len, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * paged_attention_prefill_chunk -- causal attention of prefill query chunks over
  * their paged contexts ("Inside vLLM, part 2", chunked prefill: a long prompt is
  * processed a bounded number of tokens per step, each chunk attending to the

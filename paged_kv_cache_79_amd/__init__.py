@@ -23,6 +23,8 @@ EXPORTS = (
     "paged_attention_decode_workspace_bytes",
     "paged_attention_decode",
     "contiguous_attention_decode",
+    "paged_attention_decode_shared_prefix_workspace_bytes",
+    "paged_attention_decode_shared_prefix",
     "paged_attention_prefill_chunk",
     "swap_blocks",
     "pkv_pool_create",
@@ -77,6 +79,12 @@ def load_library(path: Optional[str] = None):
     lib.contiguous_attention_decode.argtypes = [ctypes.c_int, VP, VP, VP, VP, I32, I32, I32, I32, VP,
                                                 I32, I32, F, VP, SZ, VP]
     lib.contiguous_attention_decode.restype = ctypes.c_int
+    lib.paged_attention_decode_shared_prefix_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32]
+    lib.paged_attention_decode_shared_prefix_workspace_bytes.restype = SZ
+    lib.paged_attention_decode_shared_prefix.argtypes = [
+        ctypes.c_int, VP, VP, VP, VP, I32, I32, I32, I32, VP, I32, VP, I32, I32, I32, F,
+        VP, VP, VP, VP, I32, I32, I32, VP, SZ, VP]
+    lib.paged_attention_decode_shared_prefix.restype = ctypes.c_int
     lib.paged_attention_prefill_chunk.argtypes = [ctypes.c_int, VP, VP, VP, I32, I32, VP, VP, I32, I32,
                                                   I32, I32, VP, I32, VP, I32, I32, F, VP]
     lib.paged_attention_prefill_chunk.restype = ctypes.c_int
@@ -269,6 +277,58 @@ def contiguous_attention_decode(out, q, k_cache, v_cache, context_lens, max_cont
         _dtype_code(q), _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), S, L, hkv, d,
         _ptr(context_lens), int(max_context_len), hq, float(scale), _ptr(workspace), wbytes,
         _stream(stream)))
+
+
+def paged_attention_decode_shared_prefix_workspace_bytes(num_seqs: int, num_q_heads: int,
+                                                         num_kv_heads: int, head_dim: int,
+                                                         max_context_len: int,
+                                                         max_prefix_len: int) -> int:
+    return int(load_library().paged_attention_decode_shared_prefix_workspace_bytes(
+        num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, max_prefix_len))
+
+
+def paged_attention_decode_shared_prefix(out, q, k_pool, v_pool, block_tables, context_lens,
+                                         max_context_len: int, scale: float, seq_prefix_lens,
+                                         group_first_seq, group_num_seqs, group_prefix_lens,
+                                         max_group_seqs: int, max_prefix_len: int, workspace=None,
+                                         stream=None) -> None:
+    """paged_attention_decode for batches whose groups of consecutive sequences share the
+    physical blocks of a prefix: the prefix K/V is read once per group and kv head.
+    Group arrays are int32 device tensors of one length; max_group_seqs and
+    max_prefix_len are host bounds over them."""
+    import torch
+    for n, t in (("out", out), ("q", q), ("k_pool", k_pool), ("v_pool", v_pool)):
+        _dev(t, n)
+    for n, t in (("block_tables", block_tables), ("context_lens", context_lens),
+                 ("seq_prefix_lens", seq_prefix_lens), ("group_first_seq", group_first_seq),
+                 ("group_num_seqs", group_num_seqs), ("group_prefix_lens", group_prefix_lens)):
+        _dev(t, n, torch.int32)
+    nb, hkv, bs, d = _pool_geom(k_pool, v_pool)
+    S, hq = int(q.shape[0]), int(q.shape[1])
+    if q.dim() != 3 or q.shape[2] != d or out.shape != q.shape or q.dtype != k_pool.dtype or \
+            out.dtype != q.dtype:
+        raise ValueError("q/out must be [num_seqs][num_q_heads][head_dim] of the pool dtype")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,) or \
+            seq_prefix_lens.shape != (S,):
+        raise ValueError("block_tables must be [num_seqs][max_blocks], context_lens and "
+                         "seq_prefix_lens [num_seqs]")
+    G = int(group_first_seq.numel())
+    if group_num_seqs.numel() != G or group_prefix_lens.numel() != G:
+        raise ValueError("group_first_seq, group_num_seqs, group_prefix_lens differ in length")
+    need = paged_attention_decode_shared_prefix_workspace_bytes(S, hq, hkv, d, max_context_len,
+                                                                max_prefix_len)
+    if workspace is None and need > 0:
+        workspace = decode_workspace(need, q.device)
+    if workspace is not None:
+        _dev(workspace, "workspace")
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    lib = load_library()
+    _check("paged_attention_decode_shared_prefix", lib.paged_attention_decode_shared_prefix(
+        _dtype_code(q), _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), nb, hkv, bs, d,
+        _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), S,
+        int(max_context_len), hq, float(scale), _ptr(seq_prefix_lens), _ptr(group_first_seq),
+        _ptr(group_num_seqs), _ptr(group_prefix_lens), G, int(max_group_seqs),
+        int(max_prefix_len), _ptr(workspace), wbytes, _stream(stream)))
 
 
 def paged_attention_prefill_chunk(out, q, cu_q_lens, k_pool, v_pool, block_tables, context_lens,

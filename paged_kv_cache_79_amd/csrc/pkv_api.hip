@@ -80,6 +80,23 @@ size_t decode_workspace(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_he
     return (size_t)balanced_wave_bound() * 2 * group * (size_t)(head_dim + 2) * sizeof(float);
 }
 
+// Shared-prefix pass: the prefix keys are cut into at most kMaxPreSplits splits of a
+// multiple of 64 tokens (chosen from the host bound alone, so both the workspace size
+// and the launch agree on it).
+int32_t prefix_split_tokens(int32_t max_prefix_len) {
+    const int64_t per = cdiv64(std::max(max_prefix_len, 1), kMaxPreSplits);
+    return (int32_t)std::max<int64_t>(64, cdiv64(per, 64) * 64);
+}
+int32_t prefix_splits(int32_t max_prefix_len) {
+    return max_prefix_len <= 0 ? 0
+                               : (int32_t)cdiv64(max_prefix_len, prefix_split_tokens(max_prefix_len));
+}
+size_t prefix_state_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                          int32_t max_prefix_len) {
+    return (size_t)num_seqs * num_q_heads * prefix_splits(max_prefix_len) *
+           (size_t)(head_dim + 2) * sizeof(float);
+}
+
 // Balanced split over the resident waves (`resident`, from the kernel's occupancy):
 // grid size, lead share and the partial-state layout in the workspace.
 pkv_status setup_balanced(DecodeArgs& a, int64_t resident, int32_t num_seqs, int32_t num_kv_heads,
@@ -289,6 +306,10 @@ pkv_status paged_attention_decode(pkv_dtype dtype, void* out, const void* q, con
     a.lead_share_q10 = 512;
     a.contig_seq_stride = 0;
     a.contig_row_stride = 0;
+    a.seq_prefix = nullptr;
+    a.pre_o = a.pre_ml = nullptr;
+    a.pre_splits = 0;
+    a.pre_split_tokens = 64;
     a.part_o = static_cast<float*>(workspace);
     a.part_ml = nullptr;
     if (partition_tokens > 0) {
@@ -354,10 +375,114 @@ pkv_status contiguous_attention_decode(pkv_dtype dtype, void* out, const void* q
     a.num_parts = 1;
     a.contig_seq_stride = (int64_t)max_len * row_stride;
     a.contig_row_stride = (int32_t)row_stride;
+    a.seq_prefix = nullptr;
+    a.pre_o = a.pre_ml = nullptr;
+    a.pre_splits = 0;
+    a.pre_split_tokens = 64;
     const pkv_status sb = setup_balanced(a, decode_contiguous_waves(head_dim, group), num_seqs,
                                          num_kv_heads, head_dim, max_context_len, group, workspace);
     if (sb != PKV_OK) return sb;
     return launch_status(launch_decode_contiguous(a, head_dim, group, num_seqs, stream));
+}
+
+size_t paged_attention_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                                            int32_t num_kv_heads, int32_t head_dim,
+                                                            int32_t max_context_len,
+                                                            int32_t max_prefix_len) {
+    const size_t dec = decode_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                        max_context_len, 0);
+    if (dec == 0) return 0;
+    return dec + prefix_state_bytes(num_seqs, num_q_heads, head_dim, std::max(max_prefix_len, 0));
+}
+
+pkv_status paged_attention_decode_shared_prefix(
+    pkv_dtype dtype, void* out, const void* q, const void* k_pool, const void* v_pool,
+    int32_t num_blocks, int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    int32_t num_seqs, int32_t max_context_len, int32_t num_q_heads, float scale,
+    const int32_t* seq_prefix_lens, const int32_t* group_first_seq, const int32_t* group_num_seqs,
+    const int32_t* group_prefix_lens, int32_t num_groups, int32_t max_group_seqs,
+    int32_t max_prefix_len, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    PoolGeom g;
+    const pkv_status st = check_geom(dtype, num_blocks, num_kv_heads, block_size, head_dim, &g);
+    if (st != PKV_OK) return st;
+    if (dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+    if (num_seqs < 0 || max_context_len < 0 || max_blocks_per_seq <= 0 || num_q_heads <= 0 ||
+        num_groups < 0 || max_group_seqs < 0 || max_prefix_len < 0)
+        return PKV_ERR_SHAPE;
+    if (num_q_heads % num_kv_heads) return PKV_ERR_SHAPE;
+    const int group = num_q_heads / num_kv_heads;
+    if (group > 8) return PKV_ERR_UNSUPPORTED;
+    if (!isfinite(scale)) return PKV_ERR_SHAPE;
+    if (num_seqs == 0) return PKV_OK;
+    if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PKV_ERR_NULL;
+    if (num_groups > 0 && (!seq_prefix_lens || !group_first_seq || !group_num_seqs ||
+                           !group_prefix_lens))
+        return PKV_ERR_NULL;
+    if ((int64_t)num_seqs * num_kv_heads > 65535) return PKV_ERR_UNSUPPORTED;
+    const size_t need = paged_attention_decode_shared_prefix_workspace_bytes(
+        num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, max_prefix_len);
+    if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+    if (num_groups == 0 || max_group_seqs == 0 || max_prefix_len == 0)   // nothing shared
+        return paged_attention_decode(dtype, out, q, k_pool, v_pool, num_blocks, num_kv_heads,
+                                      block_size, head_dim, block_tables, max_blocks_per_seq,
+                                      context_lens, num_seqs, max_context_len, num_q_heads, scale,
+                                      0, workspace, workspace_bytes, stream);
+
+    const size_t dec = decode_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                        max_context_len, 0);
+    float* pre_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + dec);
+    const int32_t nsplit = prefix_splits(max_prefix_len);
+    float* pre_ml = pre_o + (size_t)num_seqs * num_q_heads * nsplit * head_dim;
+
+    // 1. every group's members against their shared prefix (matrix cores)
+    PrefixArgs pa;
+    pa.pre_o = pre_o;
+    pa.pre_ml = pre_ml;
+    pa.q = q;
+    pa.k_pool = static_cast<const char*>(k_pool);
+    pa.v_pool = static_cast<const char*>(v_pool);
+    pa.block_tables = block_tables;
+    pa.group_first_seq = group_first_seq;
+    pa.group_num_seqs = group_num_seqs;
+    pa.group_prefix_len = group_prefix_lens;
+    pa.g = g;
+    pa.num_seqs = num_seqs;
+    pa.num_q_heads = num_q_heads;
+    pa.max_blocks_per_seq = max_blocks_per_seq;
+    pa.num_splits = nsplit;
+    pa.split_tokens = prefix_split_tokens(max_prefix_len);
+    pa.scale_log2 = scale * 1.4426950408889634f;
+    const hipError_t e1 = launch_prefix(pa, head_dim, group, num_groups, max_group_seqs, stream);
+    if (e1 != hipSuccess) return launch_status(e1);
+
+    // 2. every sequence's own tokens after its prefix, merged with the prefix states
+    DecodeArgs a;
+    a.out = out;
+    a.q = q;
+    a.k_pool = static_cast<const char*>(k_pool);
+    a.v_pool = static_cast<const char*>(v_pool);
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.g = g;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.max_context_len = max_context_len;
+    a.scale_log2 = pa.scale_log2;
+    a.part_tokens = 0;
+    a.num_parts = 1;
+    a.contig_seq_stride = 0;
+    a.contig_row_stride = 0;
+    a.seq_prefix = seq_prefix_lens;
+    a.pre_o = pre_o;
+    a.pre_ml = pre_ml;
+    a.pre_splits = nsplit;
+    a.pre_split_tokens = pa.split_tokens;
+    const pkv_status sb = setup_balanced(a, decode_prefix_waves(head_dim, group), num_seqs,
+                                         num_kv_heads, head_dim, max_context_len, group, workspace);
+    if (sb != PKV_OK) return sb;
+    return launch_status(launch_decode_prefix(a, head_dim, group, num_seqs, stream));
 }
 
 pkv_status paged_attention_prefill_chunk(pkv_dtype dtype, void* out, const void* q,

@@ -1,0 +1,140 @@
+// Tile helpers of the matrix-core attention kernels (chunked prefill and the
+// shared-prefix pass of decode): 64-key K/V tiles staged from the paged pool through
+// registers into LDS -- K rows as they are, V transposed for the O^T += V^T P^T
+// product -- with the block ids of a tile fetched one tile ahead.
+#pragma once
+
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+constexpr int kRowsPerWg = 128;   // packed (query, head) rows per workgroup
+constexpr int kKeyTile = 64;      // keys per tile
+constexpr int kXcds = 8;          // MI355X: workgroups are dealt round-robin to 8 XCDs
+
+template <int D>
+struct PrefillShape {
+    static constexpr int RB = D * 2;                  // bytes of a K/V row (bf16)
+    static constexpr int CPR = RB / 16;               // 16-byte chunks per row
+    static constexpr int KPITCH = RB + 16;            // K tile row pitch in LDS (bytes)
+    static constexpr int VPITCH = kKeyTile * 2 + 16;  // V^T row pitch in LDS (bytes): 36 dwords
+    static constexpr int KSTEPS = D / 16;             // QK k-steps of 16
+    static constexpr int DT = D / 32;                 // 32-row output tiles
+    static constexpr int KLOADS = kKeyTile * CPR / 256;   // K chunks per thread per tile
+    static constexpr int VLOADS = CPR / 8;            // V chunk pairs per thread per tile
+};
+
+// Position of key k (0..63) inside the transposed V tile.  Within a group of 16
+// keys, the C registers of a 32x32 MFMA hold key 8b+4h+j (b, h in {0,1}, j < 4) at
+// B-operand slot 8h+4b+j of the next MFMA: bits 2 and 3 swap.  The map is its own
+// inverse.
+__device__ __forceinline__ int vt_slot(int k) {
+    return (k & ~0xC) | ((k & 4) << 1) | ((k & 8) >> 1);
+}
+
+// Byte offset of 16-byte group g (8 key slots) of V^T row d: groups are XOR-swizzled
+// by d / 8 so that rows 8 apart never share banks.
+template <int D>
+__device__ __forceinline__ int vt_off(int d, int g) {
+    return d * PrefillShape<D>::VPITCH + ((g ^ ((d >> 3) & 7)) << 4);
+}
+
+// Thread t loads K rows t / CPR + (256 / CPR) i (whole rows per wave) and the V
+// rows of key pair t / 8, chunks t % 8 + 8 j (half rows per lane).
+template <int D>
+__device__ __forceinline__ int k_row(int i, int tid) {
+    using P = PrefillShape<D>;
+    return i * (256 / P::CPR) + tid / P::CPR;
+}
+
+template <int D>
+struct KvStage {
+    u32x4 k[PrefillShape<D>::KLOADS];
+    u32x4 v[2 * PrefillShape<D>::VLOADS];
+};
+
+// Physical block ids behind the rows one thread loads from a tile.
+template <int D>
+struct TileIds {
+    int k[PrefillShape<D>::KLOADS];
+    int v[2];
+};
+
+// Block ids for the tile starting at t0.  Rows past the context are clamped to its
+// last token (their data is replaced by zeros when loaded), so every table read
+// stays inside the sequence's used blocks.
+template <int D>
+__device__ __forceinline__ void load_ids(TileIds<D>& ids, const int32_t* table, int log2_bs,
+                                         int ctx, int t0, int tid) {
+    using P = PrefillShape<D>;
+#pragma unroll
+    for (int i = 0; i < P::KLOADS; ++i)
+        ids.k[i] = table[min(t0 + k_row<D>(i, tid), ctx - 1) >> log2_bs];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+        ids.v[r] = table[min(t0 + 2 * (tid >> 3) + r, ctx - 1) >> log2_bs];
+}
+
+template <int D>
+__device__ __forceinline__ const u32x4* row_chunk(const char* base, int pb, int tok, int chunk,
+                                                  const PoolGeom& g) {
+    const uint32_t ub = ((unsigned)pb < (unsigned)g.num_blocks) ? pb : 0;   // never a bad id
+    return reinterpret_cast<const u32x4*>(
+        base + (uint64_t)ub * (uint32_t)g.block_stride_bytes +
+        (uint32_t)((tok & (g.block_size - 1)) * PrefillShape<D>::RB + chunk * 16));
+}
+
+// Global loads of the 64-key tile starting at t0; keys >= ctx read as zero.
+template <int D>
+__device__ __forceinline__ void load_tile(KvStage<D>& st, const TileIds<D>& ids,
+                                          const PoolGeom& g, const char* kb, const char* vb,
+                                          int ctx, int t0, int tid) {
+    using P = PrefillShape<D>;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < P::KLOADS; ++i) {
+        const int tok = t0 + k_row<D>(i, tid);
+        const u32x4 x = __builtin_nontemporal_load(
+            row_chunk<D>(kb, ids.k[i], min(tok, ctx - 1), tid % P::CPR, g));
+        st.k[i] = tok < ctx ? x : zero;
+    }
+    const int kp = tid >> 3, c0 = tid & 7;
+#pragma unroll
+    for (int j = 0; j < P::VLOADS; ++j)
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int tok = t0 + 2 * kp + r;
+            const u32x4 x = __builtin_nontemporal_load(
+                row_chunk<D>(vb, ids.v[r], min(tok, ctx - 1), c0 + 8 * j, g));
+            st.v[2 * j + r] = tok < ctx ? x : zero;
+        }
+}
+
+// Staged tile -> LDS: K rows as they are, V transposed (pairs of keys per dword).
+template <int D>
+__device__ __forceinline__ void store_tile(const KvStage<D>& st, char* lds_k, char* lds_vt, int tid) {
+    using P = PrefillShape<D>;
+#pragma unroll
+    for (int i = 0; i < P::KLOADS; ++i)
+        *reinterpret_cast<u32x4*>(lds_k + k_row<D>(i, tid) * P::KPITCH + (tid % P::CPR) * 16) =
+            st.k[i];
+    const int kp = tid >> 3, c0 = tid & 7;
+    const int slot = vt_slot(2 * kp);           // even: keys 2kp, 2kp+1 share one dword
+    const int g = slot >> 3, within = (slot & 7) * 2;
+#pragma unroll
+    for (int j = 0; j < P::VLOADS; ++j) {
+        const u32x4 x0 = st.v[2 * j], x1 = st.v[2 * j + 1];
+        const uint32_t a0[4] = {x0.x, x0.y, x0.z, x0.w};
+        const uint32_t a1[4] = {x1.x, x1.y, x1.z, x1.w};
+        const int dbase = (c0 + 8 * j) * 8;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int d = dbase + 2 * q;
+            *reinterpret_cast<uint32_t*>(lds_vt + vt_off<D>(d, g) + within) = pair_lo(a0[q], a1[q]);
+            *reinterpret_cast<uint32_t*>(lds_vt + vt_off<D>(d + 1, g) + within) = pair_hi(a0[q], a1[q]);
+        }
+    }
+}
+
+}  // namespace pkv

@@ -345,17 +345,132 @@ __device__ __forceinline__ int wave_sum_int(int x) {
     return __builtin_amdgcn_readfirstlane((int)(q[0] + q[1]));
 }
 
+// First token of sequence s that the decode attends: in the shared-prefix mode the
+// tokens before it (whole blocks) were attended by the prefix pass.
+template <bool PREFIX>
+__device__ __forceinline__ int seq_start(const DecodeArgs& a, int s, int ctx) {
+    if constexpr (!PREFIX) {
+        return 0;
+    } else {
+        const int p = max(a.seq_prefix[s], 0) & ~(a.g.block_size - 1);
+        return min(p, ctx);
+    }
+}
+// Tiles of sequence s (per kv head).
+template <bool PREFIX>
+__device__ __forceinline__ int unit_tiles(const DecodeArgs& a, int s) {
+    const int ctx = clamp_ctx(a, a.context_lens[s]);
+    return ntiles_of(ctx - seq_start<PREFIX>(a, s, ctx));
+}
+
 // Tiles of the whole batch (all sequences, one kv head) and tiles before sequence `upto`.
+// Four chunks of 64 sequences per pass, their loads issued together.
+template <bool PREFIX = false>
 __device__ __forceinline__ void count_tiles(const DecodeArgs& a, int upto, int64_t& total,
                                             int64_t& before) {
     const int lane = threadIdx.x;
     total = 0;
     before = 0;
-    for (int c0 = 0; c0 < a.num_seqs; c0 += 64) {
-        const int sl = c0 + lane;
-        const int nt = sl < a.num_seqs ? ntiles_of(clamp_ctx(a, a.context_lens[sl])) : 0;
-        total += wave_sum_int(nt);
-        before += wave_sum_int(sl < upto ? nt : 0);
+    for (int c0 = 0; c0 < a.num_seqs; c0 += 256) {
+        int nt[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int sl = c0 + q * 64 + lane;
+            nt[q] = sl < a.num_seqs ? unit_tiles<PREFIX>(a, sl) : 0;
+        }
+        int t = 0, u = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            t += nt[q];
+            u += c0 + q * 64 + lane < upto ? nt[q] : 0;
+        }
+        total += wave_sum_int(t);
+        before += wave_sum_int(u);
+    }
+}
+
+// Shared-prefix mode: combine the prefix pass's partial states of (s, h) (one per key
+// split) with the decode's own state, by log-sum-exp, before the rows are written.
+// All loads are issued before any of them is used: lane hh*K + k reads the (max, sum)
+// of head hh, split k; row group r of the wave reads the o rows of splits r, r + R, ...
+template <bool BF16, int D, int G>
+__device__ __forceinline__ void fold_prefix(const DecodeArgs& a, int s, int h, int start,
+                                            SegState<BF16, D, G>& st) {
+    using S = DecodeShape<BF16, D>;
+    constexpr int K = kMaxPreSplits;
+    constexpr int J = (K + S::R - 1) / S::R;          // splits per row group
+    constexpr int HB = G <= 4 ? G : 1;                // heads whose rows are loaded together
+    static_assert(G * K <= 64, "one lane per (head, split)");
+    const int lane = threadIdx.x;
+    const int ra = lane / S::CPR, rc = lane - ra * S::CPR;
+    // never past the splits the workspace holds, whatever the device lengths say
+    const int ns = min((start + a.pre_split_tokens - 1) / a.pre_split_tokens, a.pre_splits);
+    if (ns <= 0) return;
+    const int ps = a.pre_splits;
+    const int64_t row0 = ((int64_t)s * a.num_q_heads + h * G) * ps;   // (hh, k): row0 + hh*ps + k
+
+    const int lh = lane / K, lk = lane - (lane / K) * K;
+    float2 ml = make_float2(-INFINITY, 0.f);
+    if (lh < G && lk < ns)
+        ml = *reinterpret_cast<const float2*>(a.pre_ml + (row0 + (int64_t)lh * ps + lk) * 2);
+
+    // new max per head: the decode's and the prefix splits' (8-lane groups)
+    float gm = ml.x;
+#pragma unroll
+    for (int d = 1; d < K; d <<= 1) gm = fmaxf(gm, __shfl_xor(gm, d));
+    float Mh[G], c[G];
+    float Ml = 0.f;
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+        Mh[hh] = fmaxf(st.m[hh], u2f(__builtin_amdgcn_readlane(f2u(gm), hh * K)));
+        c[hh] = fast_exp2(st.m[hh] - Mh[hh]);
+        if (lh == hh) Ml = Mh[hh];
+    }
+    const float wl = (lh < G && lk < ns) ? fast_exp2(ml.x - Ml) : 0.f;
+    float ls = wl * ml.y;
+#pragma unroll
+    for (int d = 1; d < K; d <<= 1) ls += __shfl_xor(ls, d);
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+        st.l[hh] = fmaf(st.l[hh], c[hh], u2f(__builtin_amdgcn_readlane(f2u(ls), hh * K)));
+        st.m[hh] = Mh[hh];
+    }
+
+#pragma unroll
+    for (int h0 = 0; h0 < G; h0 += HB) {
+        float v[HB][J][S::EPC];
+#pragma unroll
+        for (int i = 0; i < HB; ++i)
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                const int k = min(ra + j * S::R, ns - 1);   // splits past ns get weight 0
+                const float4* src = reinterpret_cast<const float4*>(
+                    a.pre_o + (row0 + (int64_t)(h0 + i) * ps + k) * D + rc * S::EPC);
+#pragma unroll
+                for (int e4 = 0; e4 < S::EPC / 4; ++e4) {
+                    const float4 x = src[e4];
+                    v[i][j][4 * e4 + 0] = x.x;
+                    v[i][j][4 * e4 + 1] = x.y;
+                    v[i][j][4 * e4 + 2] = x.z;
+                    v[i][j][4 * e4 + 3] = x.w;
+                }
+            }
+#pragma unroll
+        for (int i = 0; i < HB; ++i) {
+            float acc[S::EPC];
+#pragma unroll
+            for (int e = 0; e < S::EPC; ++e) acc[e] = 0.f;
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                const int k = ra + j * S::R;
+                const float wk = k < K ? __shfl(wl, (h0 + i) * K + min(k, K - 1)) : 0.f;
+#pragma unroll
+                for (int e = 0; e < S::EPC; ++e) acc[e] = fmaf(wk, v[i][j][e], acc[e]);
+            }
+#pragma unroll
+            for (int e = 0; e < S::EPC; ++e)
+                st.o[h0 + i][e] = fmaf(st.o[h0 + i][e], c[h0 + i], group_sum<S::R>(acc[e]));
+        }
     }
 }
 
@@ -385,7 +500,7 @@ __device__ __forceinline__ int64_t unit_owner(const Split& p, int64_t u) {
                    : p.Wl + ((u - p.F + 1) * (p.W - p.Wl) - 1) / (p.T - p.F);
 }
 
-template <bool BF16, int D, int G, bool CONTIG = false>
+template <bool BF16, int D, int G, bool CONTIG = false, bool PREFIX = false>
 __global__ __launch_bounds__(64, (BF16 ? 2 : 1)) void decode_balanced_kernel(DecodeArgs a) {
     using S = DecodeShape<BF16, D>;
     __shared__ __attribute__((aligned(16))) char lds_k[kTile * S::KPITCH];
@@ -399,7 +514,7 @@ __global__ __launch_bounds__(64, (BF16 ? 2 : 1)) void decode_balanced_kernel(Dec
     // units = 64-token tiles, ordered by (sequence, kv head, tile); with W <= T every
     // wave's range [wT/W, (w+1)T/W) is non-empty
     int64_t tiles_all, unused;
-    count_tiles(a, 0, tiles_all, unused);
+    count_tiles<PREFIX>(a, 0, tiles_all, unused);
     const int64_t T = tiles_all * Hkv;
     const int64_t W = min((int64_t)a.num_waves, T);
     if (w >= W) return;
@@ -413,7 +528,7 @@ __global__ __launch_bounds__(64, (BF16 ? 2 : 1)) void decode_balanced_kernel(Dec
         int64_t carry = 0;
         for (int c0 = 0; c0 < a.num_seqs; c0 += 64) {
             const int sl = c0 + lane;
-            const int nt = sl < a.num_seqs ? ntiles_of(clamp_ctx(a, a.context_lens[sl])) : 0;
+            const int nt = sl < a.num_seqs ? unit_tiles<PREFIX>(a, sl) : 0;
             int incl = nt;
 #pragma unroll
             for (int d = 1; d < 64; d <<= 1) {
@@ -431,7 +546,7 @@ __global__ __launch_bounds__(64, (BF16 ? 2 : 1)) void decode_balanced_kernel(Dec
             carry += __builtin_amdgcn_readlane(incl, 63);
         }
     }
-    int nt_s = ntiles_of(clamp_ctx(a, a.context_lens[s]));
+    int nt_s = unit_tiles<PREFIX>(a, s);
     const int64_t rel = b - before * Hkv;
     int h = (int)(rel / nt_s);
     int tile = (int)(rel - (int64_t)h * nt_s);
@@ -442,9 +557,14 @@ __global__ __launch_bounds__(64, (BF16 ? 2 : 1)) void decode_balanced_kernel(Dec
         const int seg = (int)min((int64_t)(nt_s - tile), remaining);
         const bool last = seg == remaining;
         const int ctx = clamp_ctx(a, a.context_lens[s]);
-        attend_segment<BF16, D, G, CONTIG>(a, s, h, ctx, tile * kTile,
-                                           min(ctx, (tile + seg) * kTile), lds_k, lds_p, lds_q, st);
+        const int t_first = seq_start<PREFIX>(a, s, ctx);    // 0 unless in the prefix mode
+        attend_segment<BF16, D, G, CONTIG>(a, s, h, ctx, t_first + tile * kTile,
+                                           min(ctx, t_first + (tile + seg) * kTile), lds_k, lds_p,
+                                           lds_q, st);
         if (tile == 0 && seg == nt_s) {
+            if constexpr (PREFIX) {
+                if (t_first > 0) fold_prefix<BF16, D, G>(a, s, h, t_first, st);
+            }
             write_rows<BF16, D, G>(a, s, h, st);
         } else {
             if (first) write_partial<BF16, D, G>(a, (w * 2 + 0) * G, 1, st);
@@ -458,7 +578,7 @@ __global__ __launch_bounds__(64, (BF16 ? 2 : 1)) void decode_balanced_kernel(Dec
                 h = 0;
                 do {
                     ++s;
-                    nt_s = ntiles_of(clamp_ctx(a, a.context_lens[s]));
+                    nt_s = unit_tiles<PREFIX>(a, s);
                 } while (nt_s == 0);
             }
         }
@@ -467,8 +587,10 @@ __global__ __launch_bounds__(64, (BF16 ? 2 : 1)) void decode_balanced_kernel(Dec
 
 // Merge the pieces of each (sequence, kv head) that straddles waves, one wave per
 // query head; write zero rows for empty contexts.  The first covering wave holds
-// its piece in its last slot, every later covering wave in its first slot.
-template <bool BF16, int D, int G>
+// its piece in its last slot, every later covering wave in its first slot.  In the
+// shared-prefix mode the prefix pass's states of the row are merged in as well (a
+// row with no token after its prefix is the prefix states alone).
+template <bool BF16, int D, int G, bool PREFIX = false>
 __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(DecodeArgs a) {
     constexpr int PER = D / 64;
     const int lane = threadIdx.x;
@@ -477,10 +599,39 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(DecodeArgs a)
     const int hq = blockIdx.x - s * a.num_q_heads;
     const int h = hq / G, hh = hq - h * G;
     int64_t tiles_all, before;
-    count_tiles(a, s, tiles_all, before);
-    const int nt = ntiles_of(clamp_ctx(a, a.context_lens[s]));
+    count_tiles<PREFIX>(a, s, tiles_all, before);
+    const int ctx = clamp_ctx(a, a.context_lens[s]);
+    const int start = seq_start<PREFIX>(a, s, ctx);
+    const int nt = ntiles_of(ctx - start);
+    const int ns =
+        PREFIX ? min((start + a.pre_split_tokens - 1) / a.pre_split_tokens, a.pre_splits) : 0;
+    const int64_t pre_row0 = ((int64_t)s * a.num_q_heads + hq) * a.pre_splits;
     const int64_t o = ((int64_t)s * a.num_q_heads + hq) * D + lane * PER;
-    if (nt == 0) {
+    int64_t w0 = 0;
+    int npieces = 0;
+    if (nt > 0) {
+        const int64_t T = tiles_all * Hkv, W = min((int64_t)a.num_waves, T);
+        const int64_t u0 = before * Hkv + (int64_t)h * nt;
+        const Split sp = make_split(a, T, W);
+        w0 = unit_owner(sp, u0);
+        const int64_t w1 = unit_owner(sp, u0 + nt - 1);
+        if (w0 == w1) return;  // finished by one wave (prefix states folded in there)
+        npieces = (int)(w1 - w0 + 1);
+    }
+    // the prefix states of the row, all loads in flight together (clamped to ns)
+    constexpr int KP = PREFIX ? kMaxPreSplits : 1;
+    float2 pml[KP];
+    float pv[KP][PER];
+    if (ns > 0) {
+#pragma unroll
+        for (int k = 0; k < KP; ++k) {
+            const int64_t r = pre_row0 + min(k, ns - 1);
+            pml[k] = *reinterpret_cast<const float2*>(a.pre_ml + r * 2);
+#pragma unroll
+            for (int e = 0; e < PER; ++e) pv[k][e] = a.pre_o[r * D + lane * PER + e];
+        }
+    }
+    if (npieces == 0 && ns == 0) {
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
             if constexpr (BF16)
@@ -490,16 +641,13 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(DecodeArgs a)
         }
         return;
     }
-    const int64_t T = tiles_all * Hkv, W = min((int64_t)a.num_waves, T);
-    const int64_t u0 = before * Hkv + (int64_t)h * nt;
-    const Split sp = make_split(a, T, W);
-    const int64_t w0 = unit_owner(sp, u0), w1 = unit_owner(sp, u0 + nt - 1);
-    if (w0 == w1) return;  // finished by one wave
-    const int npieces = (int)(w1 - w0 + 1);
     auto slot_row = [&](int p) -> int64_t { return ((w0 + p) * 2 + (p == 0 ? 1 : 0)) * G + hh; };
     float M = kNoMax;
     for (int p = lane; p < npieces; p += 64) M = fmaxf(M, a.part_ml[slot_row(p) * 2]);
     M = wave_max(M);
+#pragma unroll
+    for (int k = 0; k < KP; ++k)
+        if (k < ns) M = fmaxf(M, pml[k].x);
     // pieces in chunks of 64: lane p holds the weight of piece c0 + p; the output rows
     // of kBatch pieces are loaded together (unconditionally, clamped to the chunk, so
     // that the whole batch is in flight at once), then weighted by readlane
@@ -535,6 +683,15 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(DecodeArgs a)
         }
     }
     L = wave_sum(L);
+#pragma unroll
+    for (int k = 0; k < KP; ++k) {          // prefix states: (max, sum) the same for every lane
+        if (k < ns) {
+            const float wk = fast_exp2(pml[k].x - M);
+            L = fmaf(wk, pml[k].y, L);
+#pragma unroll
+            for (int e = 0; e < PER; ++e) acc[e] = fmaf(wk, pv[k][e], acc[e]);
+        }
+    }
     const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
@@ -618,7 +775,7 @@ __global__ __launch_bounds__(64) void decode_partition_merge_kernel(DecodeArgs a
 // --------------------------------------------------------------------------------------
 // host side
 // --------------------------------------------------------------------------------------
-template <bool BF16, int D, int G, bool CONTIG = false>
+template <bool BF16, int D, int G, bool CONTIG = false, bool PREFIX = false>
 static int balanced_waves_t() {
     // resident waves of the balanced kernel on the current device, cached per device
     static std::mutex mu;
@@ -630,8 +787,8 @@ static int balanced_waves_t() {
         int per_cu = 0, cus = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
                 &per_cu,
-                reinterpret_cast<const void*>(decode_balanced_kernel<BF16, D, G, CONTIG>), 64,
-                0) != hipSuccess ||
+                reinterpret_cast<const void*>(decode_balanced_kernel<BF16, D, G, CONTIG, PREFIX>),
+                64, 0) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return 0;
         cache[dev] = max(1, per_cu) * max(1, cus);
@@ -684,6 +841,20 @@ static int contig_waves_t() {
     return balanced_waves_t<true, D, G, true>();
 }
 
+// the shared-prefix mode: bf16, balanced split over the tokens after each prefix
+template <bool BF16, int D, int G>
+static hipError_t launch_prefix_decode_t(const DecodeArgs& a, hipStream_t st) {
+    hipLaunchKernelGGL((decode_balanced_kernel<true, D, G, false, true>), dim3(a.num_waves),
+                       dim3(64), 0, st, a);
+    hipLaunchKernelGGL((decode_balanced_merge_kernel<true, D, G, true>),
+                       dim3(a.num_seqs * a.num_q_heads), dim3(64), 0, st, a);
+    return hipGetLastError();
+}
+template <bool BF16, int D, int G>
+static int prefix_waves_t() {
+    return balanced_waves_t<true, D, G, false, true>();
+}
+
 template <bool BF16, int D>
 static hipError_t launch_decode_g(const DecodeArgs& a, int group, hipStream_t st) {
     PKV_DISPATCH_G(launch_decode_t, BF16, D, group, a, st)
@@ -694,6 +865,20 @@ template <bool BF16, int D>
 static int balanced_waves_g(int group) {
     PKV_DISPATCH_G(balanced_waves_t, BF16, D, group)
     return 0;
+}
+
+int decode_prefix_waves(int head_dim, int group) {
+    if (head_dim == 128) { PKV_DISPATCH_G(prefix_waves_t, true, 128, group) }
+    if (head_dim == 64) { PKV_DISPATCH_G(prefix_waves_t, true, 64, group) }
+    return 0;
+}
+
+hipError_t launch_decode_prefix(const DecodeArgs& a, int head_dim, int group, int num_seqs,
+                                hipStream_t st) {
+    if (num_seqs == 0) return hipSuccess;
+    if (head_dim == 128) { PKV_DISPATCH_G(launch_prefix_decode_t, true, 128, group, a, st) }
+    if (head_dim == 64) { PKV_DISPATCH_G(launch_prefix_decode_t, true, 64, group, a, st) }
+    return hipErrorInvalidValue;
 }
 
 int decode_contiguous_waves(int head_dim, int group) {

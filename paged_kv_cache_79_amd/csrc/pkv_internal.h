@@ -49,6 +49,10 @@ struct SwapArgs {
     int32_t dst[kSwapPairsPerLaunch];
 };
 
+// Most key splits of a shared prefix (the prefix pass writes one partial state per
+// split; the decode folds them in with all loads in flight at once).
+constexpr int kMaxPreSplits = 8;
+
 struct DecodeArgs {
     void* out;
     const void* q;
@@ -74,6 +78,15 @@ struct DecodeArgs {
     // sequence s, head h is at s * seq_stride + t * row_stride + h * row_bytes.
     int64_t contig_seq_stride;
     int32_t contig_row_stride;
+    // Shared-prefix mode: the first seq_prefix[s] tokens of sequence s were attended by
+    // the prefix pass, whose partial states are pre_o [S][Hq][pre_splits][D] and pre_ml
+    // [S][Hq][pre_splits][2] (splits of pre_split_tokens keys); the decode covers the
+    // rest of the context and merges them.  seq_prefix == nullptr: no prefix.
+    const int32_t* seq_prefix;
+    const float* pre_o;
+    const float* pre_ml;
+    int32_t pre_splits;
+    int32_t pre_split_tokens;
     float scale_log2;      // scale * log2(e)
 };
 
@@ -86,7 +99,30 @@ constexpr int kLeadShareQ10 = 584;
 
 // Persistent waves the balanced decode launches on the current device.
 int decode_balanced_waves(bool is_bf16, int head_dim, int group);
-// The same for the contiguous-layout decode (bf16 only).
+// The same for the shared-prefix mode (bf16 only).
+int decode_prefix_waves(int head_dim, int group);
+
+// The shared-prefix pass: groups of consecutive sequences whose first
+// group_prefix_len[g] tokens sit in the same physical blocks.
+struct PrefixArgs {
+    float* pre_o;
+    float* pre_ml;
+    const void* q;
+    const char* k_pool;
+    const char* v_pool;
+    const int32_t* block_tables;
+    const int32_t* group_first_seq;
+    const int32_t* group_num_seqs;
+    const int32_t* group_prefix_len;
+    PoolGeom g;
+    int32_t num_seqs;
+    int32_t num_q_heads;
+    int32_t max_blocks_per_seq;
+    int32_t num_splits;      // key splits per group prefix
+    int32_t split_tokens;    // keys per split (a multiple of 64)
+    float scale_log2;
+};
+// Persistent waves of the contiguous-layout decode (bf16 only).
 int decode_contiguous_waves(int head_dim, int group);
 
 struct PrefillArgs {
@@ -113,6 +149,11 @@ hipError_t launch_decode(const DecodeArgs& a, bool is_bf16, int head_dim, int gr
 // Decode over the contiguous [S][L][Hkv][D] layout (bf16, balanced split).
 hipError_t launch_decode_contiguous(const DecodeArgs& a, int head_dim, int group, int num_seqs,
                                     hipStream_t st);
+hipError_t launch_prefix(const PrefixArgs& a, int head_dim, int group, int num_groups,
+                         int max_group_seqs, hipStream_t st);
+// Decode over the tokens after each sequence's shared prefix, merging the prefix pass.
+hipError_t launch_decode_prefix(const DecodeArgs& a, int head_dim, int group, int num_seqs,
+                                hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int group, int num_chunks,
                           int max_q_len, hipStream_t st);
 

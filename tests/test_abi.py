@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in range(7):
+    for code in range(8):
         assert pkv.status_string(code).startswith("PKV_")
     assert "UNKNOWN" in pkv.status_string(99)
 
@@ -136,6 +136,43 @@ def test_contiguous_validation(lib):
     assert contig(lib, ws=None) == WS
     need = lib.paged_attention_decode_workspace_bytes(2, 8, 2, 128, 100, 0)
     assert contig(lib, wsb=need - 1) == WS
+
+
+def shared(lib, dtype=1, nb=8, hkv=2, bs=16, d=128, mb=4, S=2, maxctx=64, hq=8, scale=0.1,
+           ngroups=1, mgs=2, mpl=32, ws=P, wsb=1 << 30, ptr=P, gptr=P):
+    return lib.paged_attention_decode_shared_prefix(
+        dtype, ptr, ptr, ptr, ptr, nb, hkv, bs, d, ptr, mb, ptr, S, maxctx, hq, scale,
+        gptr, gptr, gptr, gptr, ngroups, mgs, mpl, ws, wsb, None)
+
+
+@dummy_ptrs
+def test_shared_prefix_validation(lib):
+    assert shared(lib, dtype=7) == DTYPE
+    assert shared(lib, dtype=0) == UNSUP               # the prefix pass is bf16 only
+    assert shared(lib, d=96) == UNSUP
+    assert shared(lib, hq=9) == SHAPE
+    assert shared(lib, hq=36, hkv=2) == UNSUP          # group of 18 heads
+    assert shared(lib, ngroups=-1) == SHAPE
+    assert shared(lib, mgs=-1) == SHAPE
+    assert shared(lib, mpl=-1) == SHAPE
+    assert shared(lib, scale=float("nan")) == SHAPE
+    assert shared(lib, ptr=None) == NULL
+    assert shared(lib, gptr=None) == NULL              # groups given without their arrays
+    assert shared(lib, S=0, ptr=None, gptr=None) == OK
+    assert shared(lib, ws=None) == WS
+    need = lib.paged_attention_decode_shared_prefix_workspace_bytes(2, 8, 2, 128, 64, 32)
+    assert shared(lib, wsb=need - 1) == WS
+
+
+def test_shared_prefix_workspace_sizes(lib):
+    f = lib.paged_attention_decode_shared_prefix_workspace_bytes
+    dec = lib.paged_attention_decode_workspace_bytes(4, 8, 2, 128, 4096, 0)
+    assert f(4, 8, 2, 128, 4096, 0) == dec
+    # prefix states: S * Hq * splits * (D + 2) floats; at most 8 splits of a multiple of
+    # 64 keys: 2032 keys -> 8 splits of 256, 100 -> 2 of 64, 64 -> 1
+    for mpl, splits in ((2032, 8), (100, 2), (64, 1), (1, 1), (20000, 8)):
+        assert f(4, 8, 2, 128, 4096, mpl) - dec == 4 * 8 * splits * 130 * 4, mpl
+    assert f(0, 8, 2, 128, 4096, 2032) == 0
 
 
 @dummy_ptrs

@@ -449,6 +449,81 @@ def mixed(poison=True, seed=None, num_chunks=4, chunk_len=512, chunk_ctx=(2048, 
 
 
 @dataclass
+class PrefixGroups:
+    """Decode batch whose sequences come in groups sharing the physical blocks of a prefix."""
+    batch: DecodeBatch
+    group_first_seq: np.ndarray       # int32 [G]
+    group_num_seqs: np.ndarray        # int32 [G]
+    group_prefix_lens: np.ndarray     # int32 [G], whole blocks
+    seq_prefix_lens: np.ndarray       # int32 [S], 0 outside every group
+
+
+def prefix_groups(seed, layout, suffix_range=(1, 200), num_q_heads=8, num_kv_heads=2,
+                  head_dim=128, block_size=16, poison=True) -> PrefixGroups:
+    """bf16 decode batch laid out by ``layout``: a list of (members, prefix_blocks);
+    prefix_blocks 0 makes one unshared sequence per member.  Members of a group share
+    their first prefix_blocks physical blocks (written once) and own a suffix of
+    U[suffix_range] tokens, the step's new token included."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    hq, hkv, d, bs = num_q_heads, num_kv_heads, head_dim, block_size
+    seqs = []                                  # (group index or -1, prefix tokens)
+    for gi, (members, pblocks) in enumerate(layout):
+        seqs += [(gi if pblocks else -1, pblocks * bs)] * members
+    S = len(seqs)
+    suffix = rng.integers(suffix_range[0], suffix_range[1], size=S, endpoint=True)
+    ctx = np.array([p + int(x) for (_, p), x in zip(seqs, suffix)], dtype=np.int64)
+    need = [cdiv(int(c), bs) for c in ctx]
+    shared_blocks = sum(p for m, p in layout if p)
+    num_blocks = math.ceil(1.25 * (shared_blocks + sum(n - p // bs for n, (_, p) in zip(need, seqs))))
+    alloc = BlockAllocator(num_blocks, rng.permutation(num_blocks))
+    mb = max(need)
+    tab = np.full((S, mb), -1, dtype=np.int32)
+    st = _storage(BF16)
+    fill = _fill_value(BF16, poison)
+    k_pool = np.full((num_blocks, hkv, bs, d), fill, dtype=st)
+    v_pool = np.full((num_blocks, hkv, bs, d), fill, dtype=st)
+    q = _encode(rng.standard_normal((S, hq, d), dtype=np.float32), BF16)
+    gfirst, gnum, gpre = [], [], []
+    s = 0
+    for gi, (members, pblocks) in enumerate(layout):
+        if pblocks:
+            prefix = np.array(alloc.allocate(pblocks), dtype=np.int32)
+            for j in range(1, members):
+                alloc.share(prefix)
+            _fill_history(rng, k_pool, v_pool, prefix, pblocks * bs, bs, BF16, hkv, d)
+            gfirst.append(s)
+            gnum.append(members)
+            gpre.append(pblocks * bs)
+        for j in range(members):
+            p = pblocks * bs
+            if pblocks:
+                tab[s, :pblocks] = prefix
+            tail = alloc.allocate(need[s] - pblocks)
+            tab[s, pblocks:need[s]] = tail
+            # the member's own history: positions p .. ctx-2
+            n_hist = int(ctx[s]) - 1
+            if n_hist > p:
+                pos = np.arange(p, n_hist, dtype=np.int64)
+                kv = rng.standard_normal((2, pos.size, hkv, d), dtype=np.float32)
+                k_pool[tab[s][pos // bs], :, pos % bs, :] = _encode(kv[0], BF16)
+                v_pool[tab[s][pos // bs], :, pos % bs, :] = _encode(kv[1], BF16)
+            s += 1
+    new = rng.standard_normal((2, S, hkv, d), dtype=np.float32)
+    slots = np.array([slots_for_positions(tab[i], [int(ctx[i]) - 1], bs)[0] for i in range(S)],
+                     dtype=np.int64)
+    batch = DecodeBatch(name="prefix_groups_bf16", dtype=BF16, num_q_heads=hq, num_kv_heads=hkv,
+                        head_dim=d, block_size=bs, num_blocks=num_blocks,
+                        scale=1.0 / math.sqrt(d), context_lens=ctx.astype(np.int32),
+                        block_tables=tab, q=q, k_pool=k_pool, v_pool=v_pool, slot_mapping=slots,
+                        k_new=_encode(new[0], BF16), v_new=_encode(new[1], BF16), seed=seed)
+    return PrefixGroups(batch=batch, group_first_seq=np.array(gfirst, dtype=np.int32),
+                        group_num_seqs=np.array(gnum, dtype=np.int32),
+                        group_prefix_lens=np.array(gpre, dtype=np.int32),
+                        seq_prefix_lens=np.array([p if g >= 0 else 0 for g, p in seqs],
+                                                 dtype=np.int32))
+
+
+@dataclass
 class SpecDecodeBatch:
     """Multi-token decode (speculative verification): every sequence writes its k + 1
     newest tokens (the last accepted one and k draft tokens) and attends with k + 1
