@@ -180,10 +180,19 @@ def run_spec(args):
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
 
+    mq = args.spec_path == "multi_query"
+    if mq:
+        ws = pkv.decode_workspace(pkv.paged_attention_decode_multi_query_workspace_bytes(
+            pre.num_chunks, nq, pre.num_q_heads, pre.num_kv_heads, pre.head_dim), q.device)
+
     def attend(i):
         kp, vp = pools[i % copies]
-        pkv.paged_attention_prefill_chunk(out, q, cu, kp, vp, tab, ctx, nq, pre.max_context_len,
-                                          pre.scale)
+        if mq:
+            pkv.paged_attention_decode_multi_query(out, q, kp, vp, tab, ctx, nq,
+                                                   pre.max_context_len, pre.scale, workspace=ws)
+        else:
+            pkv.paged_attention_prefill_chunk(out, q, cu, kp, vp, tab, ctx, nq,
+                                              pre.max_context_len, pre.scale)
 
     def step(i):
         kp, vp = pools[i % copies]
@@ -219,15 +228,15 @@ def run_spec(args):
                    "num_kv_heads": pre.num_kv_heads, "head_dim": pre.head_dim,
                    "block_size": pre.block_size, "max_context_len": pre.max_context_len,
                    "mean_context_len": round(float(np.mean(pre.context_lens)), 1),
-                   "pool_copies_rotated": copies,
-                   **({"decode": f"shared prefix: one group of {b.num_seqs}, "
-                                 f"{shared['plen']}-token prefix"} if shared else {})},
+                   "path": args.spec_path, "pool_copies_rotated": copies},
         "seqs_per_s": round(pre.num_chunks / (ms_step * 1e-3), 1),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "kv_bytes_per_step": byts,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "paged_attention_prefill_chunk with k + 1 queries per sequence",
+                     "kernel": ("paged_attention_decode_multi_query (attention kernel + merge "
+                                "kernel)" if mq else
+                                "paged_attention_prefill_chunk with k + 1 queries per sequence"),
                      "avg_us": round(att * 1e3, 2), "runs_us": [round(x * 1e3, 2) for x in runs]},
         "cpu_baseline": None,
     }
@@ -407,7 +416,9 @@ def run(args):
                    "split": "balanced" if pt == 0 else f"partitions of {pt}",
                    "layout": "contiguous [S][L][Hkv][D], no block table (step = decode only)"
                              if contig else "paged [NB][Hkv][bs][D]",
-                   "pool_copies_rotated": copies},
+                   "pool_copies_rotated": copies,
+                   **({"decode": f"shared prefix: one group of {b.num_seqs}, "
+                                 f"{shared['plen']}-token prefix"} if shared else {})},
         "seqs_per_s": round(b.num_seqs / (ms_step * 1e-3), 1),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "kv_bytes_per_step": byts,
@@ -457,6 +468,8 @@ def main():
                     help="pool block size of the gqa and long workloads")
     ap.add_argument("--shared-prefix", action="store_true",
                     help="prefix_cow: decode through the shared-prefix path (prefix read once)")
+    ap.add_argument("--spec-path", default="multi_query", choices=["multi_query", "prefill"],
+                    help="spec: attention through the multi-query decode or chunked prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

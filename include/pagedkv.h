@@ -172,6 +172,36 @@ pkv_status contiguous_attention_decode(pkv_dtype dtype, void* out, const void* q
                                        size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * paged_attention_decode_multi_query -- decode with n = queries_per_seq query
+ * positions per sequence, for verifying speculative tokens ("Inside vLLM, part 2",
+ * speculative decoding: the k proposed tokens and the last accepted one are scored
+ * in one step).  Query i of sequence s sits at position context_lens[s] - n + i and
+ * attends causally: keys t <= that position, read through the block table.  The K/V
+ * of all n positions must already be in the cache (paged_kv_write earlier on the
+ * stream), and n must not exceed a sequence's context.
+ *
+ *   out, q        [num_seqs * n][num_q_heads][head_dim] bf16 (query i of sequence s
+ *                 is token s * n + i: the packed layout of paged_attention_prefill_chunk
+ *                 with every chunk of length n)
+ *   other arguments as paged_attention_decode.
+ *
+ * The result equals paged_attention_prefill_chunk with cu_q_lens = 0, n, 2n, ...
+ * Supported: bf16, (num_q_heads / num_kv_heads) * n <= 16 (the rows of one
+ * matrix-core tile); otherwise PKV_ERR_UNSUPPORTED (use the prefill entry point).
+ * Workspace: paged_attention_decode_multi_query_workspace_bytes(); its contents need
+ * no initialisation.
+ */
+size_t paged_attention_decode_multi_query_workspace_bytes(int32_t num_seqs, int32_t queries_per_seq,
+                                                         int32_t num_q_heads, int32_t num_kv_heads,
+                                                         int32_t head_dim);
+pkv_status paged_attention_decode_multi_query(
+    pkv_dtype dtype, void* out, const void* q, const void* k_pool, const void* v_pool,
+    int32_t num_blocks, int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    int32_t num_seqs, int32_t queries_per_seq, int32_t max_context_len, int32_t num_q_heads,
+    float scale, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * paged_attention_decode_shared_prefix -- decode attention for batches in which
  * groups of sequences share the physical blocks of a common prefix ("2.1
  * PagedAttention", section 6: several block tables point at the same blocks, read

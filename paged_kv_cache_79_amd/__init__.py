@@ -25,6 +25,8 @@ EXPORTS = (
     "contiguous_attention_decode",
     "paged_attention_decode_shared_prefix_workspace_bytes",
     "paged_attention_decode_shared_prefix",
+    "paged_attention_decode_multi_query_workspace_bytes",
+    "paged_attention_decode_multi_query",
     "paged_attention_prefill_chunk",
     "swap_blocks",
     "pkv_pool_create",
@@ -85,6 +87,12 @@ def load_library(path: Optional[str] = None):
         ctypes.c_int, VP, VP, VP, VP, I32, I32, I32, I32, VP, I32, VP, I32, I32, I32, F,
         VP, VP, VP, VP, I32, I32, I32, VP, SZ, VP]
     lib.paged_attention_decode_shared_prefix.restype = ctypes.c_int
+    lib.paged_attention_decode_multi_query_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
+    lib.paged_attention_decode_multi_query_workspace_bytes.restype = SZ
+    lib.paged_attention_decode_multi_query.argtypes = [
+        ctypes.c_int, VP, VP, VP, VP, I32, I32, I32, I32, VP, I32, VP, I32, I32, I32, I32, F, VP,
+        SZ, VP]
+    lib.paged_attention_decode_multi_query.restype = ctypes.c_int
     lib.paged_attention_prefill_chunk.argtypes = [ctypes.c_int, VP, VP, VP, I32, I32, VP, VP, I32, I32,
                                                   I32, I32, VP, I32, VP, I32, I32, F, VP]
     lib.paged_attention_prefill_chunk.restype = ctypes.c_int
@@ -329,6 +337,47 @@ def paged_attention_decode_shared_prefix(out, q, k_pool, v_pool, block_tables, c
         int(max_context_len), hq, float(scale), _ptr(seq_prefix_lens), _ptr(group_first_seq),
         _ptr(group_num_seqs), _ptr(group_prefix_lens), G, int(max_group_seqs),
         int(max_prefix_len), _ptr(workspace), wbytes, _stream(stream)))
+
+
+def paged_attention_decode_multi_query_workspace_bytes(num_seqs: int, queries_per_seq: int,
+                                                       num_q_heads: int, num_kv_heads: int,
+                                                       head_dim: int) -> int:
+    return int(load_library().paged_attention_decode_multi_query_workspace_bytes(
+        num_seqs, queries_per_seq, num_q_heads, num_kv_heads, head_dim))
+
+
+def paged_attention_decode_multi_query(out, q, k_pool, v_pool, block_tables, context_lens,
+                                       queries_per_seq: int, max_context_len: int, scale: float,
+                                       workspace=None, stream=None) -> None:
+    """Decode with n = queries_per_seq causal queries per sequence (speculative
+    verification): q/out [num_seqs * n][Hq][D] bf16, query i of sequence s at position
+    context_lens[s] - n + i."""
+    import torch
+    for nm, t in (("out", out), ("q", q), ("k_pool", k_pool), ("v_pool", v_pool)):
+        _dev(t, nm)
+    _dev(block_tables, "block_tables", torch.int32)
+    _dev(context_lens, "context_lens", torch.int32)
+    nb, hkv, bs, d = _pool_geom(k_pool, v_pool)
+    n = int(queries_per_seq)
+    S = int(context_lens.shape[0])
+    hq = int(q.shape[1])
+    if q.dim() != 3 or q.shape[0] != S * n or q.shape[2] != d or out.shape != q.shape or \
+            q.dtype != k_pool.dtype or out.dtype != q.dtype:
+        raise ValueError("q/out must be [num_seqs * queries_per_seq][num_q_heads][head_dim] of the "
+                         "pool dtype")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("block_tables must be [num_seqs][max_blocks]")
+    need = paged_attention_decode_multi_query_workspace_bytes(S, n, hq, hkv, d)
+    if workspace is None and need > 0:
+        workspace = decode_workspace(need, q.device)
+    if workspace is not None:
+        _dev(workspace, "workspace")
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    lib = load_library()
+    _check("paged_attention_decode_multi_query", lib.paged_attention_decode_multi_query(
+        _dtype_code(q), _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), nb, hkv, bs, d,
+        _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), S, n,
+        int(max_context_len), hq, float(scale), _ptr(workspace), wbytes, _stream(stream)))
 
 
 def paged_attention_prefill_chunk(out, q, cu_q_lens, k_pool, v_pool, block_tables, context_lens,

@@ -385,6 +385,69 @@ pkv_status contiguous_attention_decode(pkv_dtype dtype, void* out, const void* q
     return launch_status(launch_decode_contiguous(a, head_dim, group, num_seqs, stream));
 }
 
+size_t paged_attention_decode_multi_query_workspace_bytes(int32_t num_seqs, int32_t queries_per_seq,
+                                                         int32_t num_q_heads, int32_t num_kv_heads,
+                                                         int32_t head_dim) {
+    if (num_seqs <= 0 || queries_per_seq <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+        head_dim <= 0 || num_q_heads % num_kv_heads)
+        return 0;
+    const int64_t rows = (int64_t)(num_q_heads / num_kv_heads) * queries_per_seq;
+    return (size_t)balanced_wave_bound() * 2 * rows * (size_t)(head_dim + 2) * sizeof(float);
+}
+
+pkv_status paged_attention_decode_multi_query(
+    pkv_dtype dtype, void* out, const void* q, const void* k_pool, const void* v_pool,
+    int32_t num_blocks, int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    int32_t num_seqs, int32_t queries_per_seq, int32_t max_context_len, int32_t num_q_heads,
+    float scale, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    PoolGeom g;
+    const pkv_status st = check_geom(dtype, num_blocks, num_kv_heads, block_size, head_dim, &g);
+    if (st != PKV_OK) return st;
+    if (dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+    if (num_seqs < 0 || queries_per_seq <= 0 || max_context_len < 0 || max_blocks_per_seq <= 0 ||
+        num_q_heads <= 0)
+        return PKV_ERR_SHAPE;
+    if (num_q_heads % num_kv_heads) return PKV_ERR_SHAPE;
+    const int group = num_q_heads / num_kv_heads;
+    if (group > 8 || (int64_t)group * queries_per_seq > 16) return PKV_ERR_UNSUPPORTED;
+    if (!isfinite(scale)) return PKV_ERR_SHAPE;
+    if (num_seqs == 0) return PKV_OK;
+    if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PKV_ERR_NULL;
+    if ((int64_t)num_seqs * queries_per_seq * num_q_heads > ((int64_t)1 << 30))
+        return PKV_ERR_UNSUPPORTED;
+    const size_t need = paged_attention_decode_multi_query_workspace_bytes(
+        num_seqs, queries_per_seq, num_q_heads, num_kv_heads, head_dim);
+    if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+
+    DecodeArgs a;
+    a.out = out;
+    a.q = q;
+    a.k_pool = static_cast<const char*>(k_pool);
+    a.v_pool = static_cast<const char*>(v_pool);
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.g = g;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.max_context_len = max_context_len;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.part_tokens = 0;
+    a.num_parts = 1;
+    a.contig_seq_stride = 0;
+    a.contig_row_stride = 0;
+    a.seq_prefix = nullptr;
+    a.pre_o = a.pre_ml = nullptr;
+    a.pre_splits = 0;
+    a.pre_split_tokens = 64;
+    const pkv_status sb = setup_balanced(a, decode_mq_waves(head_dim, group), num_seqs, num_kv_heads,
+                                         head_dim, max_context_len, group * queries_per_seq,
+                                         workspace);
+    if (sb != PKV_OK) return sb;
+    return launch_status(launch_decode_mq(a, head_dim, group, queries_per_seq, num_seqs, stream));
+}
+
 size_t paged_attention_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                                             int32_t num_kv_heads, int32_t head_dim,
                                                             int32_t max_context_len,

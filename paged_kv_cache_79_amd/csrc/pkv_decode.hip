@@ -35,12 +35,9 @@
 // is by sequence position instead and does not depend on the device.
 #include <mutex>
 
-#include "pkv_device.h"
-#include "pkv_internal.h"
+#include "pkv_split.h"
 
 namespace pkv {
-
-constexpr int kTile = 64;
 
 template <bool BF16, int D>
 struct DecodeShape {
@@ -58,19 +55,6 @@ template <bool BF16>
 struct DecodeLds {
     static constexpr int PWORDS = BF16 ? kTile / 2 * 8 : kTile * 8;   // probabilities (dwords)
 };
-
-__device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int c) {
-    return max(0, min(c, min(a.max_context_len, a.max_blocks_per_seq * a.g.block_size)));
-}
-__device__ __forceinline__ int ntiles_of(int ctx) { return (ctx + kTile - 1) / kTile; }
-
-// Block-table entries of the 64-token tile starting at t0: lane j holds the physical
-// block of logical block t0/bs + j (clamped to the sequence's last block), so one
-// vector load fetches every entry a tile needs.
-__device__ __forceinline__ int load_tile_table(const int32_t* table, int t0, int log2_bs, int nblk,
-                                               int lane) {
-    return table[min((t0 >> log2_bs) + lane, nblk - 1)];
-}
 
 // Softmax state of one segment of one (sequence, kv head) for its G query heads,
 // after the per-lane pieces have been combined: m and l are uniform; lanes of row
@@ -330,65 +314,6 @@ __device__ __forceinline__ void zero_rows(const DecodeArgs& a, int s, int h) {
     }
 }
 
-// --------------------------------------------------------------------------------------
-// balanced split
-// --------------------------------------------------------------------------------------
-__device__ __forceinline__ int wave_sum_int(int x) {
-    x += (int)__builtin_amdgcn_update_dpp(0u, (uint32_t)x, 0x128, 0xF, 0xF, false);
-    x += (int)__builtin_amdgcn_update_dpp(0u, (uint32_t)x, 0x124, 0xF, 0xF, false);
-    x += (int)__builtin_amdgcn_update_dpp(0u, (uint32_t)x, 0x122, 0xF, 0xF, false);
-    x += (int)__builtin_amdgcn_update_dpp(0u, (uint32_t)x, 0x121, 0xF, 0xF, false);
-    auto r = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
-    x = (int)(r[0] + r[1]);
-    auto q = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
-    // every lane holds the total; readfirstlane tells the compiler it is uniform
-    return __builtin_amdgcn_readfirstlane((int)(q[0] + q[1]));
-}
-
-// First token of sequence s that the decode attends: in the shared-prefix mode the
-// tokens before it (whole blocks) were attended by the prefix pass.
-template <bool PREFIX>
-__device__ __forceinline__ int seq_start(const DecodeArgs& a, int s, int ctx) {
-    if constexpr (!PREFIX) {
-        return 0;
-    } else {
-        const int p = max(a.seq_prefix[s], 0) & ~(a.g.block_size - 1);
-        return min(p, ctx);
-    }
-}
-// Tiles of sequence s (per kv head).
-template <bool PREFIX>
-__device__ __forceinline__ int unit_tiles(const DecodeArgs& a, int s) {
-    const int ctx = clamp_ctx(a, a.context_lens[s]);
-    return ntiles_of(ctx - seq_start<PREFIX>(a, s, ctx));
-}
-
-// Tiles of the whole batch (all sequences, one kv head) and tiles before sequence `upto`.
-// Four chunks of 64 sequences per pass, their loads issued together.
-template <bool PREFIX = false>
-__device__ __forceinline__ void count_tiles(const DecodeArgs& a, int upto, int64_t& total,
-                                            int64_t& before) {
-    const int lane = threadIdx.x;
-    total = 0;
-    before = 0;
-    for (int c0 = 0; c0 < a.num_seqs; c0 += 256) {
-        int nt[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int sl = c0 + q * 64 + lane;
-            nt[q] = sl < a.num_seqs ? unit_tiles<PREFIX>(a, sl) : 0;
-        }
-        int t = 0, u = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            t += nt[q];
-            u += c0 + q * 64 + lane < upto ? nt[q] : 0;
-        }
-        total += wave_sum_int(t);
-        before += wave_sum_int(u);
-    }
-}
-
 // Shared-prefix mode: combine the prefix pass's partial states of (s, h) (one per key
 // split) with the decode's own state, by log-sum-exp, before the rows are written.
 // All loads are issued before any of them is used: lane hh*K + k reads the (max, sum)
@@ -474,32 +399,6 @@ __device__ __forceinline__ void fold_prefix(const DecodeArgs& a, int s, int h, i
     }
 }
 
-// The split of T tiles over W waves: the first Wl waves share the first F tiles
-// evenly, the other W - Wl waves the remaining T - F (every range non-empty).
-struct Split {
-    int64_t T, W, F, Wl;
-};
-__device__ __forceinline__ Split make_split(const DecodeArgs& a, int64_t T, int64_t W) {
-    Split p{T, W, T, W};                       // even split: one class of waves
-    if (W == a.num_waves && W % 2 == 0) {
-        const int64_t F = T * a.lead_share_q10 / 1024, Wl = W / 2;
-        if (F >= Wl && T - F >= W - Wl) {
-            p.F = F;
-            p.Wl = Wl;
-        }
-    }
-    return p;
-}
-// First tile of wave w's range [begin(w), begin(w + 1)); begin(Wl) = F, begin(W) = T.
-__device__ __forceinline__ int64_t range_begin(const Split& p, int64_t w) {
-    return w <= p.Wl ? w * p.F / p.Wl : p.F + (w - p.Wl) * (p.T - p.F) / (p.W - p.Wl);
-}
-// Wave whose range holds tile u.
-__device__ __forceinline__ int64_t unit_owner(const Split& p, int64_t u) {
-    return u < p.F ? ((u + 1) * p.Wl - 1) / p.F
-                   : p.Wl + ((u - p.F + 1) * (p.W - p.Wl) - 1) / (p.T - p.F);
-}
-
 template <bool BF16, int D, int G, bool CONTIG = false, bool PREFIX = false>
 __global__ __launch_bounds__(64, (BF16 ? 2 : 1)) void decode_balanced_kernel(DecodeArgs a) {
     using S = DecodeShape<BF16, D>;
@@ -521,31 +420,9 @@ __global__ __launch_bounds__(64, (BF16 ? 2 : 1)) void decode_balanced_kernel(Dec
     const Split sp = make_split(a, T, W);
     const int64_t b = range_begin(sp, w), e = range_begin(sp, w + 1);
 
-    // locate the sequence holding unit b: first s with Hkv * (tiles up to s) > b
     int s = 0;
     int64_t before = 0;
-    {
-        int64_t carry = 0;
-        for (int c0 = 0; c0 < a.num_seqs; c0 += 64) {
-            const int sl = c0 + lane;
-            const int nt = sl < a.num_seqs ? unit_tiles<PREFIX>(a, sl) : 0;
-            int incl = nt;
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const int y = __shfl_up(incl, d);
-                if (lane >= d) incl += y;
-            }
-            const uint64_t hit = __ballot((carry + incl) * Hkv > b);
-            if (hit) {
-                const int ln = __ffsll((unsigned long long)hit) - 1;
-                s = c0 + ln;
-                // readlane with a uniform lane: the compiler then knows the value is uniform
-                before = carry + __builtin_amdgcn_readlane(incl - nt, ln);
-                break;
-            }
-            carry += __builtin_amdgcn_readlane(incl, 63);
-        }
-    }
+    locate_unit<PREFIX>(a, b, Hkv, s, before);
     int nt_s = unit_tiles<PREFIX>(a, s);
     const int64_t rel = b - before * Hkv;
     int h = (int)(rel / nt_s);
@@ -590,14 +467,18 @@ __global__ __launch_bounds__(64, (BF16 ? 2 : 1)) void decode_balanced_kernel(Dec
 // its piece in its last slot, every later covering wave in its first slot.  In the
 // shared-prefix mode the prefix pass's states of the row are merged in as well (a
 // row with no token after its prefix is the prefix states alone).
+// With nq queries per sequence (multi-query decode) the output row blockIdx.x is
+// (s * nq + i) * Hq + hq, and a (sequence, kv head) has nq * G partial rows.
 template <bool BF16, int D, int G, bool PREFIX = false>
-__global__ __launch_bounds__(64) void decode_balanced_merge_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64) void decode_balanced_merge_kernel(DecodeArgs a, int nq) {
     constexpr int PER = D / 64;
     const int lane = threadIdx.x;
     const int Hkv = a.g.num_kv_heads;
-    const int s = blockIdx.x / a.num_q_heads;
-    const int hq = blockIdx.x - s * a.num_q_heads;
-    const int h = hq / G, hh = hq - h * G;
+    const int sq = blockIdx.x / a.num_q_heads;
+    const int hq = blockIdx.x - sq * a.num_q_heads;
+    const int s = sq / nq;
+    const int h = hq / G;
+    const int rows = nq * G, r = (sq - s * nq) * G + (hq - h * G);
     int64_t tiles_all, before;
     count_tiles<PREFIX>(a, s, tiles_all, before);
     const int ctx = clamp_ctx(a, a.context_lens[s]);
@@ -606,7 +487,7 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(DecodeArgs a)
     const int ns =
         PREFIX ? min((start + a.pre_split_tokens - 1) / a.pre_split_tokens, a.pre_splits) : 0;
     const int64_t pre_row0 = ((int64_t)s * a.num_q_heads + hq) * a.pre_splits;
-    const int64_t o = ((int64_t)s * a.num_q_heads + hq) * D + lane * PER;
+    const int64_t o = (int64_t)blockIdx.x * D + lane * PER;
     int64_t w0 = 0;
     int npieces = 0;
     if (nt > 0) {
@@ -641,55 +522,61 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(DecodeArgs a)
         }
         return;
     }
-    auto slot_row = [&](int p) -> int64_t { return ((w0 + p) * 2 + (p == 0 ? 1 : 0)) * G + hh; };
-    float M = kNoMax;
-    for (int p = lane; p < npieces; p += 64) M = fmaxf(M, a.part_ml[slot_row(p) * 2]);
-    M = wave_max(M);
-#pragma unroll
-    for (int k = 0; k < KP; ++k)
-        if (k < ns) M = fmaxf(M, pml[k].x);
-    // pieces in chunks of 64: lane p holds the weight of piece c0 + p; the output rows
-    // of kBatch pieces are loaded together (unconditionally, clamped to the chunk, so
-    // that the whole batch is in flight at once), then weighted by readlane
-    constexpr int kBatch = 32;
-    float L = 0.f;
+    auto slot_row = [&](int p) -> int64_t { return ((w0 + p) * 2 + (p == 0 ? 1 : 0)) * rows + r; };
+    // pieces in batches of kBatch, each batch one round of loads: lane j holds the
+    // (max, sum) of piece c0 + j while every lane loads its part of all the batch's
+    // output rows (unconditionally, clamped to the batch); a running maximum rescales
+    // what earlier batches accumulated, as in the online softmax
+    constexpr int kBatch = 16;
+    float M = kNoMax, L = 0.f;                 // L: per-lane sum, reduced at the end
     float acc[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) acc[k] = 0.f;
-    for (int c0 = 0; c0 < npieces; c0 += 64) {
-        const int cnt = min(64, npieces - c0);
-        float wgt = 0.f;
-        if (lane < cnt) {
-            const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + slot_row(c0 + lane) * 2);
-            wgt = fast_exp2(ml.x - M);
-            L = fmaf(wgt, ml.y, L);
+    for (int c0 = 0; c0 < npieces; c0 += kBatch) {
+        const int cnt = min(kBatch, npieces - c0);
+        float2 ml = make_float2(-INFINITY, 0.f);
+        if (lane < cnt) ml = *reinterpret_cast<const float2*>(a.part_ml + slot_row(c0 + lane) * 2);
+        float v[kBatch][PER];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            const float* src = a.part_o + slot_row(c0 + min(j, cnt - 1)) * D + lane * PER;
+#pragma unroll
+            for (int k = 0; k < PER; ++k) v[j][k] = src[k];
         }
-        for (int j0 = 0; j0 < cnt; j0 += kBatch) {
-            float v[kBatch][PER];
+        const float Mn = fmaxf(M, wave_max(ml.x));
+        const float c = fast_exp2(M - Mn);
+        M = Mn;
+        const float wgt = lane < cnt ? fast_exp2(ml.x - Mn) : 0.f;
+        L = fmaf(L, c, wgt * ml.y);
 #pragma unroll
-            for (int j = 0; j < kBatch; ++j) {
-                const float* src = a.part_o + slot_row(c0 + min(j0 + j, cnt - 1)) * D + lane * PER;
+        for (int k = 0; k < PER; ++k) acc[k] *= c;
 #pragma unroll
-                for (int k = 0; k < PER; ++k) v[j][k] = src[k];
-            }
+        for (int j = 0; j < kBatch; ++j) {
+            if (j < cnt) {
+                const float wj = u2f(__builtin_amdgcn_readlane(f2u(wgt), j));
 #pragma unroll
-            for (int j = 0; j < kBatch; ++j) {
-                if (j0 + j < cnt) {
-                    const float wj = u2f(__builtin_amdgcn_readlane(f2u(wgt), j0 + j));
-#pragma unroll
-                    for (int k = 0; k < PER; ++k) acc[k] = fmaf(wj, v[j][k], acc[k]);
-                }
+                for (int k = 0; k < PER; ++k) acc[k] = fmaf(wj, v[j][k], acc[k]);
             }
         }
     }
     L = wave_sum(L);
+    if (ns > 0) {                           // prefix states: (max, sum) the same for every lane
+        float Mp = M;
 #pragma unroll
-    for (int k = 0; k < KP; ++k) {          // prefix states: (max, sum) the same for every lane
-        if (k < ns) {
-            const float wk = fast_exp2(pml[k].x - M);
-            L = fmaf(wk, pml[k].y, L);
+        for (int k = 0; k < KP; ++k)
+            if (k < ns) Mp = fmaxf(Mp, pml[k].x);
+        const float c = fast_exp2(M - Mp);
+        L *= c;
 #pragma unroll
-            for (int e = 0; e < PER; ++e) acc[e] = fmaf(wk, pv[k][e], acc[e]);
+        for (int e = 0; e < PER; ++e) acc[e] *= c;
+#pragma unroll
+        for (int k = 0; k < KP; ++k) {
+            if (k < ns) {
+                const float wk = fast_exp2(pml[k].x - Mp);
+                L = fmaf(wk, pml[k].y, L);
+#pragma unroll
+                for (int e = 0; e < PER; ++e) acc[e] = fmaf(wk, pv[k][e], acc[e]);
+            }
         }
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -809,7 +696,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
         hipLaunchKernelGGL((decode_balanced_kernel<BF16, D, G>), dim3(a.num_waves), dim3(64), 0, st,
                            a);
         hipLaunchKernelGGL((decode_balanced_merge_kernel<BF16, D, G>), dim3(S * a.num_q_heads),
-                           dim3(64), 0, st, a);
+                           dim3(64), 0, st, a, 1);
     }
     return hipGetLastError();
 }
@@ -833,7 +720,7 @@ static hipError_t launch_contig_t(const DecodeArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((decode_balanced_kernel<true, D, G, true>), dim3(a.num_waves), dim3(64), 0,
                        st, a);
     hipLaunchKernelGGL((decode_balanced_merge_kernel<true, D, G>), dim3(a.num_seqs * a.num_q_heads),
-                       dim3(64), 0, st, a);
+                       dim3(64), 0, st, a, 1);
     return hipGetLastError();
 }
 template <bool BF16, int D, int G>
@@ -847,12 +734,27 @@ static hipError_t launch_prefix_decode_t(const DecodeArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((decode_balanced_kernel<true, D, G, false, true>), dim3(a.num_waves),
                        dim3(64), 0, st, a);
     hipLaunchKernelGGL((decode_balanced_merge_kernel<true, D, G, true>),
-                       dim3(a.num_seqs * a.num_q_heads), dim3(64), 0, st, a);
+                       dim3(a.num_seqs * a.num_q_heads), dim3(64), 0, st, a, 1);
     return hipGetLastError();
 }
 template <bool BF16, int D, int G>
 static int prefix_waves_t() {
     return balanced_waves_t<true, D, G, false, true>();
+}
+
+// the merge of the multi-query decode (bf16): nq * G partial rows per (sequence, kv head)
+template <bool BF16, int D, int G>
+static hipError_t launch_merge_mq_t(const DecodeArgs& a, int nq, hipStream_t st) {
+    hipLaunchKernelGGL((decode_balanced_merge_kernel<true, D, G>),
+                       dim3(a.num_seqs * nq * a.num_q_heads), dim3(64), 0, st, a, nq);
+    return hipGetLastError();
+}
+
+hipError_t launch_balanced_merge_mq(const DecodeArgs& a, int head_dim, int group, int nq,
+                                    hipStream_t st) {
+    if (head_dim == 128) { PKV_DISPATCH_G(launch_merge_mq_t, true, 128, group, a, nq, st) }
+    if (head_dim == 64) { PKV_DISPATCH_G(launch_merge_mq_t, true, 64, group, a, nq, st) }
+    return hipErrorInvalidValue;
 }
 
 template <bool BF16, int D>

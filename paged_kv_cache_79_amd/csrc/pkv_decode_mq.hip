@@ -1,0 +1,373 @@
+// Multi-query paged decode on the gfx950 matrix cores.
+//
+// What is computed ("Inside vLLM, part 2", speculative decoding: the target model
+// checks k proposed tokens in one step, so every sequence brings k + 1 query
+// positions, and each attends causally to the paged context): query i of the n
+// queries of sequence s sits at position ctx_s - n + i and sees keys t <= that
+// position, read through the block table as in decode ("2.1 PagedAttention",
+// sections 3 and 5).
+//
+// Mapping.  The work split is decode's balanced split: every 64-key tile of every
+// (sequence, kv head) is one unit, and a persistent grid of resident waves takes
+// contiguous ranges of units.  A wave attends all n * G rows of a (sequence, kv
+// head) -- G query heads share each K/V read -- with rows packed into the 16
+// columns of 16x16x32 bf16 MFMAs (lane 16q + n holds A[n][8q..8q+7],
+// B[8q..8q+7][n] and C[4q..4q+3][n]):
+//   S^T = K Q^T     K comes straight from the pool in the A layout (lane 16q + n
+//                   loads 16 bytes of key n at d = 32c + 8q), Q^T stays in B
+//                   registers for the whole segment;
+//   softmax         a lane holds 16 keys of its row: lane-local max and sum plus
+//                   two permlane swaps across the four lanes of the row;
+//   O^T += V^T P^T  P^T is the S^T registers converted to bf16 in place; V^T is
+//                   staged through LDS, written transposed with keys permuted to
+//                   match P^T's register order.
+// Straddling (sequence, kv head) pairs leave partial states that the balanced
+// merge combines, as for decode.
+#include <mutex>
+
+#include "pkv_split.h"
+
+namespace pkv {
+
+template <int D>
+struct MqShape {
+    static constexpr int RB = D * 2;                 // bytes of a K/V row (bf16)
+    static constexpr int KC = D / 32;                // QK k-steps of 32 over the head dim
+    static constexpr int DT = D / 16;                // 16-row tiles of O^T
+    static constexpr int CPR = RB / 16;              // 16-byte chunks per row
+    static constexpr int VJ = CPR / 8;               // chunks per key per lane in the V load
+    static constexpr int VPITCH = kTile * 2 + 16;    // bytes of a V^T row in LDS
+    static constexpr int ROWS = 16;                  // MFMA columns: query rows per wave
+};
+
+// Slot of key kk (0..63) in the V^T tile.  Within a group of 32 keys, the S^T
+// registers of lane 16q + n hold keys 4q + j and 16 + 4q + j (j < 4), which the PV
+// product takes as B-operand slots 8q + j and 8q + 4 + j.
+__device__ __forceinline__ int mq_slot(int kk) {
+    return (kk & 32) | (((kk & 15) >> 2) << 3) | (((kk >> 4) & 1) << 2) | (kk & 3);
+}
+
+// Byte offset of slot group g (8 slots, 16 bytes) of V^T row d; groups are
+// XOR-swizzled by d / 8 so that the transposing writes of rows 8 apart spread over
+// the banks.
+template <int D>
+__device__ __forceinline__ int mq_vt_off(int d, int g) {
+    return d * MqShape<D>::VPITCH + ((g ^ ((d >> 3) & 7)) << 4);
+}
+
+template <int D>
+struct MqState {
+    floatx4_t o[MqShape<D>::DT];   // O^T of this lane's row n: d = 16 dt + 4q + j
+    float m, l;                    // running max (log2 units) and sum of the row
+};
+
+__device__ __forceinline__ floatx4_t mfma16(u32x4 a, u32x4 b, floatx4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Attend the nq * G rows of (s, h) to keys [t_begin, t_end) of the sequence.
+template <int D, int G>
+__device__ __forceinline__ void attend_mq(const DecodeArgs& a, int s, int h, int ctx, int nq,
+                                          int t_begin, int t_end, char* lds_vt,
+                                          MqState<D>& st) {
+    using P = MqShape<D>;
+    const int lane = threadIdx.x;
+    const int n = lane & 15, q = lane >> 4;
+    const int bs = a.g.block_size, lbs = a.g.log2_bs;
+    const int nblk = (ctx + bs - 1) >> lbs;
+    const int rows = nq * G;
+    const int32_t* table = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+    const char* kb = a.k_pool + (int64_t)h * a.g.head_stride_bytes;
+    const char* vb = a.v_pool + (int64_t)h * a.g.head_stride_bytes;
+    const uint64_t bstride = (uint64_t)a.g.block_stride_bytes;
+
+    // Q^T: column n is row (query qi, head h*G + hh); padding columns are zero
+    const bool live = n < rows;
+    const int qi = live ? n / G : nq - 1;
+    const int hh = live ? n - (n / G) * G : 0;
+    u32x4 qreg[P::KC];
+    {
+        const char* qp = reinterpret_cast<const char*>(a.q) +
+                         (((int64_t)s * nq + qi) * a.num_q_heads + h * G + hh) * P::RB + q * 16;
+#pragma unroll
+        for (int c = 0; c < P::KC; ++c)
+            qreg[c] = live ? *reinterpret_cast<const u32x4*>(qp + c * 64) : u32x4{0u, 0u, 0u, 0u};
+    }
+    const int lim = ctx - nq + qi;     // last key this row sees
+
+    float m = kNoMax, l = 0.f;
+    floatx4_t o[P::DT];
+#pragma unroll
+    for (int dt = 0; dt < P::DT; ++dt) o[dt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    const float sl2 = a.scale_log2;
+    const int kp = lane >> 3, c0 = lane & 7;
+
+    int tab_cur = load_tile_table(table, t_begin, lbs, nblk, lane);
+    for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
+        const int tab = tab_cur;
+        const int b0 = t0 >> lbs;
+        // ---- loads: K in the A layout, V as key pairs (both clamped to the context;
+        //      keys past it are masked out of the scores, so their values never count)
+        u32x4 kreg[4][P::KC];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const int key = min(t0 + 16 * mt + n, ctx - 1);
+            int pb = __shfl(tab, (key >> lbs) - b0);
+            pb = ((unsigned)pb < (unsigned)a.g.num_blocks) ? pb : 0;   // never a bad id
+            const char* row = kb + (uint64_t)(uint32_t)pb * bstride +
+                              (uint32_t)((key & (bs - 1)) * P::RB + q * 16);
+#pragma unroll
+            for (int c = 0; c < P::KC; ++c)
+                kreg[mt][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + c * 64));
+        }
+        u32x4 vreg[4][2][P::VJ];
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int key = min(t0 + 2 * (8 * p + kp) + r, ctx - 1);
+                int pb = __shfl(tab, (key >> lbs) - b0);
+                pb = ((unsigned)pb < (unsigned)a.g.num_blocks) ? pb : 0;
+                const char* row = vb + (uint64_t)(uint32_t)pb * bstride +
+                                  (uint32_t)((key & (bs - 1)) * P::RB + c0 * 16);
+#pragma unroll
+                for (int j = 0; j < P::VJ; ++j)
+                    vreg[p][r][j] =
+                        __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + j * 128));
+            }
+        tab_cur = load_tile_table(table, t0 + kTile, lbs, nblk, lane);
+
+        // ---- S^T = K Q^T: lane holds keys t0 + 16mt + 4q + j of row n -----------------
+        floatx4_t sacc[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            sacc[mt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < P::KC; ++c) sacc[mt] = mfma16(kreg[mt][c], qreg[c], sacc[mt]);
+        }
+
+        // ---- online softmax over the row's 64 keys (4 lanes x 16) ---------------------
+        const bool full = t0 + kTile - 1 <= ctx - nq;    // every key visible to every row
+        float mx = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int key = t0 + 16 * mt + 4 * q + j;
+                const float sc = (full || key <= lim) ? sacc[mt][j] * sl2 : -INFINITY;
+                sacc[mt][j] = sc;
+                mx = fmaxf(mx, sc);
+            }
+        mx = swap32_max(swap16_max(mx));
+        const float mn = fmaxf(m, mx);
+        const float alpha = fast_exp2(m - mn);
+        m = mn;
+        float ps = 0.f;
+        u32x4 pk[2];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            float p[2][4];
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    p[u][j] = fast_exp2(sacc[2 * s2 + u][j] - mn);
+                    ps += p[u][j];
+                }
+            pk[s2] = u32x4{pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3]),
+                           pack_bf16(p[1][0], p[1][1]), pack_bf16(p[1][2], p[1][3])};
+        }
+        l = fmaf(l, alpha, ps);
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+            for (int dt = 0; dt < P::DT; ++dt) o[dt] *= alpha;
+        }
+
+        // ---- V^T into LDS: keys 2m, 2m+1 share a dword of each V^T row ----------------
+        __syncthreads();               // the previous tile's V^T reads are done
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int slot = mq_slot(2 * (8 * p + kp));
+            const int g = slot >> 3, within = (slot & 7) * 2;
+#pragma unroll
+            for (int j = 0; j < P::VJ; ++j) {
+                const u32x4 x0 = vreg[p][0][j], x1 = vreg[p][1][j];
+                const uint32_t a0[4] = {x0.x, x0.y, x0.z, x0.w};
+                const uint32_t a1[4] = {x1.x, x1.y, x1.z, x1.w};
+                const int dbase = (c0 + 8 * j) * 8;
+#pragma unroll
+                for (int w2 = 0; w2 < 4; ++w2) {
+                    const int d = dbase + 2 * w2;
+                    *reinterpret_cast<uint32_t*>(lds_vt + mq_vt_off<D>(d, g) + within) =
+                        pair_lo(a0[w2], a1[w2]);
+                    *reinterpret_cast<uint32_t*>(lds_vt + mq_vt_off<D>(d + 1, g) + within) =
+                        pair_hi(a0[w2], a1[w2]);
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- O^T += V^T P^T ----------------------------------------------------------
+#pragma unroll
+        for (int dt = 0; dt < P::DT; ++dt)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const u32x4 va = *reinterpret_cast<const u32x4*>(
+                    lds_vt + mq_vt_off<D>(dt * 16 + n, 4 * s2 + q));
+                o[dt] = mfma16(va, pk[s2], o[dt]);
+            }
+    }
+#pragma unroll
+    for (int dt = 0; dt < P::DT; ++dt) st.o[dt] = o[dt];
+    st.m = m;
+    st.l = swap32_sum(swap16_sum(l));
+}
+
+// Normalised rows of a finished (s, h): lane 16q + n writes d = 16dt + 4q .. +3 of row n.
+template <int D, int G>
+__device__ __forceinline__ void write_mq_rows(const DecodeArgs& a, int s, int h, int nq,
+                                              const MqState<D>& st) {
+    using P = MqShape<D>;
+    const int lane = threadIdx.x;
+    const int n = lane & 15, q = lane >> 4;
+    if (n >= nq * G) return;
+    const int qi = n / G, hh = n - (n / G) * G;
+    const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
+    uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) +
+                    (((int64_t)s * nq + qi) * a.num_q_heads + h * G + hh) * D + q * 4;
+#pragma unroll
+    for (int dt = 0; dt < P::DT; ++dt)
+        *reinterpret_cast<u32x2*>(dst + dt * 16) =
+            u32x2{pack_bf16(st.o[dt][0] * inv, st.o[dt][1] * inv),
+                  pack_bf16(st.o[dt][2] * inv, st.o[dt][3] * inv)};
+}
+
+// Unnormalised state of row n into partial row prow0 + n.
+template <int D, int G>
+__device__ __forceinline__ void write_mq_partial(const DecodeArgs& a, int64_t prow0, int nq,
+                                                 const MqState<D>& st) {
+    using P = MqShape<D>;
+    const int lane = threadIdx.x;
+    const int n = lane & 15, q = lane >> 4;
+    if (n >= nq * G) return;
+    const int64_t prow = prow0 + n;
+    float* dst = a.part_o + prow * D + q * 4;
+#pragma unroll
+    for (int dt = 0; dt < P::DT; ++dt)
+        *reinterpret_cast<float4*>(dst + dt * 16) =
+            make_float4(st.o[dt][0], st.o[dt][1], st.o[dt][2], st.o[dt][3]);
+    if (q == 0) *reinterpret_cast<float2*>(a.part_ml + prow * 2) = make_float2(st.m, st.l);
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(64, 2) void decode_mq_kernel(DecodeArgs a, int nq) {
+    __shared__ __attribute__((aligned(16))) char lds_vt[D * MqShape<D>::VPITCH];
+    const int64_t w = blockIdx.x;
+    const int Hkv = a.g.num_kv_heads;
+    const int rows = nq * G;
+
+    int64_t tiles_all, unused;
+    count_tiles(a, 0, tiles_all, unused);
+    const int64_t T = tiles_all * Hkv;
+    const int64_t W = min((int64_t)a.num_waves, T);
+    if (w >= W) return;
+    const Split sp = make_split(a, T, W);
+    const int64_t b = range_begin(sp, w), e = range_begin(sp, w + 1);
+
+    int s = 0;
+    int64_t before = 0;
+    locate_unit(a, b, Hkv, s, before);
+    int nt_s = unit_tiles<false>(a, s);
+    const int64_t rel = b - before * Hkv;
+    int h = (int)(rel / nt_s);
+    int tile = (int)(rel - (int64_t)h * nt_s);
+    int64_t remaining = e - b;
+    bool first = true;
+    MqState<D> st;
+    while (remaining > 0) {
+        const int seg = (int)min((int64_t)(nt_s - tile), remaining);
+        const bool last = seg == remaining;
+        const int ctx = clamp_ctx(a, a.context_lens[s]);
+        attend_mq<D, G>(a, s, h, ctx, nq, tile * kTile, min(ctx, (tile + seg) * kTile), lds_vt,
+                        st);
+        if (tile == 0 && seg == nt_s) {
+            write_mq_rows<D, G>(a, s, h, nq, st);
+        } else {
+            if (first) write_mq_partial<D, G>(a, (w * 2 + 0) * rows, nq, st);
+            if (last) write_mq_partial<D, G>(a, (w * 2 + 1) * rows, nq, st);
+        }
+        remaining -= seg;
+        first = false;
+        if (remaining > 0) {
+            tile = 0;
+            if (++h == Hkv) {
+                h = 0;
+                do {
+                    ++s;
+                    nt_s = unit_tiles<false>(a, s);
+                } while (nt_s == 0);
+            }
+        }
+    }
+}
+
+// --------------------------------------------------------------------------------------
+// host side
+// --------------------------------------------------------------------------------------
+template <int D, int G>
+static int mq_waves_t() {
+    static std::mutex mu;
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cache[dev] == 0) {
+        int per_cu = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &per_cu, reinterpret_cast<const void*>(decode_mq_kernel<D, G>), 64, 0) !=
+                hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        cache[dev] = max(1, per_cu) * max(1, cus);
+    }
+    return cache[dev];
+}
+
+template <int D, int G>
+static hipError_t launch_mq_t(const DecodeArgs& a, int nq, hipStream_t st) {
+    hipLaunchKernelGGL((decode_mq_kernel<D, G>), dim3(a.num_waves), dim3(64), 0, st, a, nq);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_balanced_merge_mq(a, D, G, nq, st);
+}
+
+#define PKV_MQ_DISPATCH(FN, DD, group, ...)    \
+    switch (group) {                           \
+        case 1: return FN<DD, 1>(__VA_ARGS__); \
+        case 2: return FN<DD, 2>(__VA_ARGS__); \
+        case 3: return FN<DD, 3>(__VA_ARGS__); \
+        case 4: return FN<DD, 4>(__VA_ARGS__); \
+        case 5: return FN<DD, 5>(__VA_ARGS__); \
+        case 6: return FN<DD, 6>(__VA_ARGS__); \
+        case 7: return FN<DD, 7>(__VA_ARGS__); \
+        case 8: return FN<DD, 8>(__VA_ARGS__); \
+        default: break;                        \
+    }
+
+int decode_mq_waves(int head_dim, int group) {
+    if (head_dim == 128) { PKV_MQ_DISPATCH(mq_waves_t, 128, group) }
+    if (head_dim == 64) { PKV_MQ_DISPATCH(mq_waves_t, 64, group) }
+    return 0;
+}
+
+hipError_t launch_decode_mq(const DecodeArgs& a, int head_dim, int group, int nq, int num_seqs,
+                            hipStream_t st) {
+    if (num_seqs == 0) return hipSuccess;
+    if (nq < 1 || nq * group > MqShape<128>::ROWS) return hipErrorInvalidValue;
+    if (head_dim == 128) { PKV_MQ_DISPATCH(launch_mq_t, 128, group, a, nq, st) }
+    if (head_dim == 64) { PKV_MQ_DISPATCH(launch_mq_t, 64, group, a, nq, st) }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace pkv

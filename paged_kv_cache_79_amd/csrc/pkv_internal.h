@@ -156,5 +156,12 @@ hipError_t launch_decode_prefix(const DecodeArgs& a, int head_dim, int group, in
                                 hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int group, int num_chunks,
                           int max_q_len, hipStream_t st);
+// Multi-query decode (bf16): nq queries per sequence, nq * group <= 16, balanced split.
+int decode_mq_waves(int head_dim, int group);
+hipError_t launch_decode_mq(const DecodeArgs& a, int head_dim, int group, int nq, int num_seqs,
+                            hipStream_t st);
+// The balanced merge for nq queries per sequence (used by the multi-query decode).
+hipError_t launch_balanced_merge_mq(const DecodeArgs& a, int head_dim, int group, int nq,
+                                    hipStream_t st);
 
 }  // namespace pkv

@@ -175,6 +175,37 @@ def test_shared_prefix_workspace_sizes(lib):
     assert f(0, 8, 2, 128, 4096, 2032) == 0
 
 
+def mq(lib, dtype=1, nb=8, hkv=2, bs=16, d=128, mb=4, S=2, n=4, maxctx=64, hq=8, scale=0.1,
+       ws=P, wsb=1 << 30, ptr=P):
+    return lib.paged_attention_decode_multi_query(dtype, ptr, ptr, ptr, ptr, nb, hkv, bs, d, ptr,
+                                                  mb, ptr, S, n, maxctx, hq, scale, ws, wsb, None)
+
+
+@dummy_ptrs
+def test_multi_query_validation(lib):
+    assert mq(lib, dtype=7) == DTYPE
+    assert mq(lib, dtype=0) == UNSUP                   # bf16 only
+    assert mq(lib, d=96) == UNSUP
+    assert mq(lib, n=0) == SHAPE
+    assert mq(lib, hq=9) == SHAPE
+    assert mq(lib, n=5) == UNSUP                       # 5 queries x 4 heads > 16 rows
+    assert mq(lib, hq=36, hkv=2, n=1) == UNSUP         # group of 18 heads
+    assert mq(lib, scale=float("nan")) == SHAPE
+    assert mq(lib, ptr=None) == NULL
+    assert mq(lib, S=0, ptr=None) == OK
+    assert mq(lib, ws=None) == WS
+    need = lib.paged_attention_decode_multi_query_workspace_bytes(2, 4, 8, 2, 128)
+    assert mq(lib, wsb=need - 1) == WS
+
+
+def test_multi_query_workspace_sizes(lib):
+    f = lib.paged_attention_decode_multi_query_workspace_bytes
+    # two partial slots of n * G rows per resident wave; n = 1 is decode's size
+    assert f(2, 1, 8, 2, 128) == lib.paged_attention_decode_workspace_bytes(2, 8, 2, 128, 4096, 0)
+    assert f(2, 4, 8, 2, 128) == 4 * f(2, 1, 8, 2, 128)
+    assert f(0, 4, 8, 2, 128) == 0 and f(2, 0, 8, 2, 128) == 0
+
+
 @dummy_ptrs
 def test_prefill_validation(lib):
     f = lib.paged_attention_prefill_chunk
