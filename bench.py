@@ -63,17 +63,19 @@ def prefill_flops(pre) -> int:
 
 
 def recorded_traffic(workload_name):
-    """Counter-derived HBM bytes per decode call, as recorded under profiles/ with the
-    hash of the decode source they were measured on; None when absent or stale."""
+    """Counter-derived HBM bytes per call of the timed kernels, as recorded under profiles/
+    with the hashes of the sources they were measured on; None when absent or stale."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"decode_{workload_name.replace('_decode', '')}_traffic.json")
-    src = os.path.join(ROOT, "paged_kv_cache_79_amd", "csrc", "pkv_decode.hip")
     try:
         rec = json.load(open(path))
-        cur = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    except (OSError, ValueError):
+        for name, sha in rec["sources_sha256"].items():
+            src = os.path.join(ROOT, "paged_kv_cache_79_amd", "csrc", name)
+            if hashlib.sha256(open(src, "rb").read()).hexdigest() != sha:
+                return None
+    except (OSError, ValueError, KeyError):
         return None
-    return rec["traffic_bytes_per_call"] if rec.get("decode_source_sha256") == cur else None
+    return rec["traffic_bytes_per_call"]
 
 
 def log(msg):
@@ -233,7 +235,8 @@ def run_spec(args):
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "kv_bytes_per_step": byts,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic("spec") if mq and pre.block_size == 16 else None,
                      "kernel": ("paged_attention_decode_multi_query (attention kernel + merge "
                                 "kernel)" if mq else
                                 "paged_attention_prefill_chunk with k + 1 queries per sequence"),

@@ -428,11 +428,9 @@ __global__ __launch_bounds__(64, (BF16 ? 2 : 1)) void decode_balanced_kernel(Dec
     int h = (int)(rel / nt_s);
     int tile = (int)(rel - (int64_t)h * nt_s);
     int64_t remaining = e - b;
-    bool first = true;
     SegState<BF16, D, G> st;
     while (remaining > 0) {
         const int seg = (int)min((int64_t)(nt_s - tile), remaining);
-        const bool last = seg == remaining;
         const int ctx = clamp_ctx(a, a.context_lens[s]);
         const int t_first = seq_start<PREFIX>(a, s, ctx);    // 0 unless in the prefix mode
         attend_segment<BF16, D, G, CONTIG>(a, s, h, ctx, t_first + tile * kTile,
@@ -444,11 +442,12 @@ __global__ __launch_bounds__(64, (BF16 ? 2 : 1)) void decode_balanced_kernel(Dec
             }
             write_rows<BF16, D, G>(a, s, h, st);
         } else {
-            if (first) write_partial<BF16, D, G>(a, (w * 2 + 0) * G, 1, st);
-            if (last) write_partial<BF16, D, G>(a, (w * 2 + 1) * G, 1, st);
+            // the merge reads the piece of the wave holding the unit's first tile from
+            // slot 1 and every later wave's from slot 0: a piece that starts the unit can
+            // only be this wave's last segment, one that starts inside it only the first
+            write_partial<BF16, D, G>(a, (w * 2 + (tile == 0 ? 1 : 0)) * G, 1, st);
         }
         remaining -= seg;
-        first = false;
         if (remaining > 0) {
             tile = 0;
             if (++h == Hkv) {

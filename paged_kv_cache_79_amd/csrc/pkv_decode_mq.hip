@@ -283,22 +283,20 @@ __global__ __launch_bounds__(64, 2) void decode_mq_kernel(DecodeArgs a, int nq) 
     int h = (int)(rel / nt_s);
     int tile = (int)(rel - (int64_t)h * nt_s);
     int64_t remaining = e - b;
-    bool first = true;
     MqState<D> st;
     while (remaining > 0) {
         const int seg = (int)min((int64_t)(nt_s - tile), remaining);
-        const bool last = seg == remaining;
         const int ctx = clamp_ctx(a, a.context_lens[s]);
         attend_mq<D, G>(a, s, h, ctx, nq, tile * kTile, min(ctx, (tile + seg) * kTile), lds_vt,
                         st);
         if (tile == 0 && seg == nt_s) {
             write_mq_rows<D, G>(a, s, h, nq, st);
         } else {
-            if (first) write_mq_partial<D, G>(a, (w * 2 + 0) * rows, nq, st);
-            if (last) write_mq_partial<D, G>(a, (w * 2 + 1) * rows, nq, st);
+            // slot 1 for a piece that starts the unit, slot 0 for one that starts inside
+            // it (the merge's reading order, as for decode)
+            write_mq_partial<D, G>(a, (w * 2 + (tile == 0 ? 1 : 0)) * rows, nq, st);
         }
         remaining -= seg;
-        first = false;
         if (remaining > 0) {
             tile = 0;
             if (++h == Hkv) {

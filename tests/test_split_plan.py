@@ -6,9 +6,10 @@ W'/2 waves share the first F = floor(T f / 1024) tiles evenly and the others the
 remaining T - F (when both classes get at least one tile per wave), otherwise all
 W' waves share the T tiles evenly.  Each wave walks its range in (sequence, kv
 head, tile) order, finishes a (sequence, head) that lies inside its range, and
-otherwise leaves a partial in slot 0 (its first segment) and/or slot 1 (its last
-segment); the merge takes the first covering wave's slot 1 and every later
-covering wave's slot 0, locating the owner of a tile by the same split.  This test
+otherwise leaves one partial: in slot 1 if the piece starts the (sequence, head)
+(only a wave's last segment can), in slot 0 if it starts inside it (only a wave's
+first segment can); the merge takes the first covering wave's slot 1 and every
+later covering wave's slot 0, locating the owner of a tile by the same split.  This test
 replays that arithmetic on random mixes of lengths and checks that every tile is
 processed exactly once and that the merge reads exactly the slots that were written
 for that (sequence, head)."""
@@ -62,10 +63,10 @@ def plan(ctx, hkv, W, lead_q10):
                 assert (s, h) not in finished
                 finished[(s, h)] = w
             else:
-                if first:
-                    written[(w, 0)] = (s, h)
-                if last:
-                    written[(w, 1)] = (s, h)
+                slot = 1 if tile == 0 else 0
+                assert (w, slot) not in written
+                assert (slot == 1 and last) or (slot == 0 and first)
+                written[(w, slot)] = (s, h)
             rem -= seg
             first = False
             if rem > 0:
