@@ -12,6 +12,8 @@ namespace pkv {
 constexpr int kRowsPerWg = 128;   // packed (query, head) rows per workgroup
 constexpr int kKeyTile = 64;      // keys per tile
 constexpr int kXcds = 8;          // MI355X: workgroups are dealt round-robin to 8 XCDs
+// Slack of the lazily updated softmax maximum (log2 units): a factor of 256.
+constexpr float kLazyMax = 8.f;
 
 template <int D>
 struct PrefillShape {
@@ -61,65 +63,79 @@ struct TileIds {
     int v[2];
 };
 
-// Block ids for the tile starting at t0.  Rows past the context are clamped to its
-// last token (their data is replaced by zeros when loaded), so every table read
-// stays inside the sequence's used blocks.
+// Byte offsets, inside a (block, kv head) run, of the K rows one thread loads.  Tiles
+// start at multiples of 64 >= block_size, so they are the same for every tile.
 template <int D>
-__device__ __forceinline__ void load_ids(TileIds<D>& ids, const int32_t* table, int log2_bs,
-                                         int ctx, int t0, int tid) {
+struct TileOffs {
+    uint32_t k[PrefillShape<D>::KLOADS];
+};
+
+template <int D>
+__device__ __forceinline__ void tile_offsets(TileOffs<D>& o, int block_size, int tid) {
     using P = PrefillShape<D>;
 #pragma unroll
     for (int i = 0; i < P::KLOADS; ++i)
-        ids.k[i] = table[min(t0 + k_row<D>(i, tid), ctx - 1) >> log2_bs];
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-        ids.v[r] = table[min(t0 + 2 * (tid >> 3) + r, ctx - 1) >> log2_bs];
+        o.k[i] = (uint32_t)((k_row<D>(i, tid) & (block_size - 1)) * P::RB + (tid % P::CPR) * 16);
 }
 
+// Block ids for the tile starting at t0 (validated where they are used: checking
+// them here would wait for these table reads, and with them for every global load
+// issued before, at the top of each tile).  Keys past the context (only in a sequence's last tile):
+//   K rows read the block of the last token at their own offset -- inside the pool,
+//      but stale data, whose scores the softmax replaces by -inf;
+//   V rows read the last token's row itself -- finite data, which the zero
+//      probability of a hidden key then multiplies to exactly zero.
 template <int D>
-__device__ __forceinline__ const u32x4* row_chunk(const char* base, int pb, int tok, int chunk,
-                                                  const PoolGeom& g) {
-    const uint32_t ub = ((unsigned)pb < (unsigned)g.num_blocks) ? pb : 0;   // never a bad id
-    return reinterpret_cast<const u32x4*>(
-        base + (uint64_t)ub * (uint32_t)g.block_stride_bytes +
-        (uint32_t)((tok & (g.block_size - 1)) * PrefillShape<D>::RB + chunk * 16));
-}
-
-// Global loads of the 64-key tile starting at t0; keys >= ctx read as zero.
-template <int D>
-__device__ __forceinline__ void load_tile(KvStage<D>& st, const TileIds<D>& ids,
-                                          const PoolGeom& g, const char* kb, const char* vb,
-                                          int ctx, int t0, int tid) {
+__device__ __forceinline__ void load_ids(TileIds<D>& ids, const int32_t* table, const PoolGeom& g,
+                                         int ctx, int t0, int tid) {
     using P = PrefillShape<D>;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < P::KLOADS; ++i) {
-        const int tok = t0 + k_row<D>(i, tid);
-        const u32x4 x = __builtin_nontemporal_load(
-            row_chunk<D>(kb, ids.k[i], min(tok, ctx - 1), tid % P::CPR, g));
-        st.k[i] = tok < ctx ? x : zero;
+        ids.k[i] = table[(uint32_t)min(t0 + k_row<D>(i, tid), ctx - 1) >> g.log2_bs];
     }
-    const int kp = tid >> 3, c0 = tid & 7;
 #pragma unroll
-    for (int j = 0; j < P::VLOADS; ++j)
+    for (int r = 0; r < 2; ++r)
+        ids.v[r] = table[(uint32_t)min(t0 + 2 * (tid >> 3) + r, ctx - 1) >> g.log2_bs];
+}
+
+// Row address in the pool; an id outside the pool reads block 0 instead.
+__device__ __forceinline__ const u32x4* pool_row(const char* base, int id, uint32_t num_blocks,
+                                                 uint32_t stride, uint32_t off) {
+    const uint32_t ub = (uint32_t)id < num_blocks ? (uint32_t)id : 0u;
+    return reinterpret_cast<const u32x4*>(base + ((uint64_t)ub * stride + off));
+}
+
+// Global loads of the 64-key tile starting at t0 (K and V are read once: nontemporal).
+template <int D>
+__device__ __forceinline__ void load_tile(KvStage<D>& st, const TileIds<D>& ids,
+                                          const TileOffs<D>& offs, const PoolGeom& g,
+                                          const char* kb, const char* vb, int ctx, int t0,
+                                          int tid) {
+    using P = PrefillShape<D>;
+    const uint32_t stride = (uint32_t)g.block_stride_bytes, nb = (uint32_t)g.num_blocks;
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const int tok = t0 + 2 * kp + r;
-            const u32x4 x = __builtin_nontemporal_load(
-                row_chunk<D>(vb, ids.v[r], min(tok, ctx - 1), c0 + 8 * j, g));
-            st.v[2 * j + r] = tok < ctx ? x : zero;
-        }
+    for (int i = 0; i < P::KLOADS; ++i)
+        st.k[i] = __builtin_nontemporal_load(pool_row(kb, ids.k[i], nb, stride, offs.k[i]));
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const uint32_t tok = (uint32_t)min(t0 + 2 * (tid >> 3) + r, ctx - 1);
+        const uint32_t off = (tok & (uint32_t)(g.block_size - 1)) * P::RB + (uint32_t)(tid & 7) * 16;
+#pragma unroll
+        for (int j = 0; j < P::VLOADS; ++j)
+            st.v[2 * j + r] =
+                __builtin_nontemporal_load(pool_row(vb, ids.v[r], nb, stride, off + 128 * j));
+    }
 }
 
 // Staged tile -> LDS: K rows as they are, V transposed (pairs of keys per dword).
 template <int D>
 __device__ __forceinline__ void store_tile(const KvStage<D>& st, char* lds_k, char* lds_vt, int tid) {
     using P = PrefillShape<D>;
+    const int kp = tid >> 3, c0 = tid & 7;
 #pragma unroll
     for (int i = 0; i < P::KLOADS; ++i)
         *reinterpret_cast<u32x4*>(lds_k + k_row<D>(i, tid) * P::KPITCH + (tid % P::CPR) * 16) =
             st.k[i];
-    const int kp = tid >> 3, c0 = tid & 7;
     const int slot = vt_slot(2 * kp);           // even: keys 2kp, 2kp+1 share one dword
     const int g = slot >> 3, within = (slot & 7) * 2;
 #pragma unroll
@@ -135,6 +151,16 @@ __device__ __forceinline__ void store_tile(const KvStage<D>& st, char* lds_k, ch
             *reinterpret_cast<uint32_t*>(lds_vt + vt_off<D>(d + 1, g) + within) = pair_hi(a0[q], a1[q]);
         }
     }
+}
+
+// Sum of the 8 bf16 probabilities packed in p, added to acc: the row sums then count
+// the same rounded values that the P V product multiplies.
+__device__ __forceinline__ float sum_bf16x8(u32x4 p, float acc) {
+    constexpr uint32_t kOnes = 0x3F803F80u;      // (1.0, 1.0) in bf16
+    acc = dot2_bf16(p.x, kOnes, acc);
+    acc = dot2_bf16(p.y, kOnes, acc);
+    acc = dot2_bf16(p.z, kOnes, acc);
+    return dot2_bf16(p.w, kOnes, acc);
 }
 
 }  // namespace pkv

@@ -19,14 +19,16 @@
 //                     which the C registers of S^T hold them), B = bf16 P^T
 //                     straight from those registers.
 // Software pipeline: while the matrix cores work on tile j from LDS, the K/V
-// global loads of tile j+1 are in flight (their block ids were fetched during
-// tile j-1) and the block ids of tile j+2 are being fetched; tile j+1 lands in
-// LDS after tile j's products.  V is written transposed with a 16-byte XOR
+// global loads of tiles j+1 and j+2 are in flight in two register stages (tile
+// j+2's issued at the top of tile j, after the table reads of tile j+3: the
+// in-order load counter then lets each wait cover only what it needs); tile j+1
+// goes into the second LDS buffer after tile j's products, with one barrier per tile.  V is written transposed with a 16-byte XOR
 // swizzle so that the transposing writes meet fewer LDS bank conflicts while the
 // operand reads stay conflict-free.  Workgroups are ordered so that all query
 // tiles of one (chunk, kv head) run on the same XCD and share its L2.
-// Keys past the context are zero in LDS and masked to -inf, so stale or NaN
-// slots never reach the matrix cores.
+// Keys past the context get -inf scores by selection (whatever stale data their K
+// rows hold) and their V rows repeat the last token's row, so stale or NaN slots
+// never reach the output.
 #include "pkv_attn_tiles.h"
 
 namespace pkv {
@@ -36,8 +38,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, int num_
                                                          int num_items) {
     using P = PrefillShape<D>;
     constexpr int QP = kRowsPerWg / G;           // query positions per workgroup
-    __shared__ __attribute__((aligned(16))) char lds_k[kKeyTile * P::KPITCH];
-    __shared__ __attribute__((aligned(16))) char lds_vt[D * P::VPITCH];
+    // two LDS tile buffers: tile j is read from buffer j % 2 while tile j+1 is
+    // written into the other one, so one barrier per tile suffices
+    __shared__ __attribute__((aligned(16))) char lds_k[2][kKeyTile * P::KPITCH];
+    __shared__ __attribute__((aligned(16))) char lds_vt[2][D * P::VPITCH];
 
     // XCD-aware order: consecutive work items (the query tiles of one (chunk, kv head))
     // get workgroup ids that are equal modulo the XCD count.
@@ -101,21 +105,33 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, int num_
     // keys any row of this workgroup may see
     const int t_stop = ctx - nq + min(nq, (qt + 1) * QP);
 
-    KvStage<D> stage;
-    TileIds<D> ids;
-    load_ids<D>(ids, table, a.g.log2_bs, ctx, 0, tid);
-    load_tile<D>(stage, ids, a.g, kb, vb, ctx, 0, tid);
-    load_ids<D>(ids, table, a.g.log2_bs, ctx, kKeyTile, tid);
-    store_tile<D>(stage, lds_k, lds_vt, tid);
+    // Two K/V stages in registers and two sets of block ids, alternating with the
+    // parity of the tile: at tile j, the table reads of tile j+3 go out first, then the
+    // K/V reads of tile j+2 (with ids read during tile j-1), so each wait of the
+    // in-order load counter covers only what it needs.
+    KvStage<D> st0, st1;
+    TileIds<D> ids0, ids1;
+    TileOffs<D> offs;
+    tile_offsets<D>(offs, bs, tid);
+    load_ids<D>(ids0, table, a.g, ctx, 0, tid);
+    load_tile<D>(st0, ids0, offs, a.g, kb, vb, ctx, 0, tid);
+    load_ids<D>(ids1, table, a.g, ctx, kKeyTile, tid);
+    if (kKeyTile < t_stop) load_tile<D>(st1, ids1, offs, a.g, kb, vb, ctx, kKeyTile, tid);
+    load_ids<D>(ids0, table, a.g, ctx, 2 * kKeyTile, tid);
+    store_tile<D>(st0, lds_k[0], lds_vt[0], tid);
     __syncthreads();
 
-    for (int t0 = 0; t0 < t_stop; t0 += kKeyTile) {
-        const bool more = t0 + kKeyTile < t_stop;
-        if (more) {
-            load_tile<D>(stage, ids, a.g, kb, vb, ctx, t0 + kKeyTile, tid);
-            load_ids<D>(ids, table, a.g.log2_bs, ctx, t0 + 2 * kKeyTile, tid);
+    // one tile: prefetch tile t0 + 128 into `next2` (ids in `use`; the ids of tile
+    // t0 + 192 into `load`), attend tile t0 from LDS, then move tile t0 + 64 (in
+    // `next1`) into LDS
+    auto step = [&](int t0, int buf, KvStage<D>& next2, const KvStage<D>& next1,
+                    const TileIds<D>& use, TileIds<D>& load) {
+        const char* tk = lds_k[buf];
+        const char* tv = lds_vt[buf];
+        if (t0 + 2 * kKeyTile < t_stop) {
+            load_ids<D>(load, table, a.g, ctx, t0 + 3 * kKeyTile, tid);
+            load_tile<D>(next2, use, offs, a.g, kb, vb, ctx, t0 + 2 * kKeyTile, tid);
         }
-
         // ---- S^T = K Q^T ----------------------------------------------------------
         floatx16_t sacc[2];
 #pragma unroll
@@ -125,7 +141,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, int num_
 #pragma unroll
             for (int ks = 0; ks < P::KSTEPS; ++ks) {
                 const u32x4 ka = *reinterpret_cast<const u32x4*>(
-                    lds_k + (mt * 32 + n) * P::KPITCH + ks * 32 + half * 16);
+                    tk + (mt * 32 + n) * P::KPITCH + ks * 32 + half * 16);
                 sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     __builtin_bit_cast(bf16x8_t, ka), __builtin_bit_cast(bf16x8_t, qreg[ks]),
                     sacc[mt], 0, 0, 0);
@@ -152,32 +168,31 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, int num_
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, sacc[mt][e]);
-        const float mn = fmaxf(m, swap32_max(mloc) * mul);
-        // rescale the output only when some row of the wave raised its maximum
-        if (__builtin_amdgcn_ballot_w64(mn > m)) {
-            const float alpha = fast_exp2(m - mn);
+        // The reference maximum m moves only when some row of the wave outgrew it by
+        // more than kLazyMax (log2 units): probabilities stay below 2^kLazyMax, far
+        // inside the bf16 and fp32 ranges, and the rescales of O become rare.
+        const float mx = fmaxf(m, swap32_max(mloc) * mul);
+        if (__builtin_amdgcn_ballot_w64(mx > m + kLazyMax)) {
+            const float alpha = fast_exp2(m - mx);
             l *= alpha;
 #pragma unroll
             for (int dt = 0; dt < P::DT; ++dt)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
+            m = mx;
         }
-        m = mn;
-        float psum = 0.f;
+        const float mn = m;
         u32x4 pk[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int mt = u >> 1, e0 = (u & 1) * 8;
             float p[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                p[j] = fast_exp2(__builtin_fmaf(sacc[mt][e0 + j], mul, -mn));
-                psum += p[j];
-            }
+            for (int j = 0; j < 8; ++j) p[j] = fast_exp2(__builtin_fmaf(sacc[mt][e0 + j], mul, -mn));
             pk[u] = u32x4{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
                           pack_bf16(p[6], p[7])};
+            l = sum_bf16x8(pk[u], l);
         }
-        l += psum;
 
         // ---- O^T += V^T P^T ---------------------------------------------------------
 #pragma unroll
@@ -185,16 +200,21 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, int num_
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const u32x4 va = *reinterpret_cast<const u32x4*>(
-                    lds_vt + vt_off<D>(dt * 32 + n, 2 * u + half));
+                    tv + vt_off<D>(dt * 32 + n, 2 * u + half));
                 oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     __builtin_bit_cast(bf16x8_t, va), __builtin_bit_cast(bf16x8_t, pk[u]),
                     oacc[dt], 0, 0, 0);
             }
-        __syncthreads();                 // every wave is done with this tile's LDS
-        if (more) {
-            store_tile<D>(stage, lds_k, lds_vt, tid);
-            __syncthreads();
-        }
+
+        // the other buffer held tile j-1, which every wave finished before the last
+        // barrier; the barrier below publishes tile j+1 and frees this buffer
+        if (t0 + kKeyTile < t_stop) store_tile<D>(next1, lds_k[buf ^ 1], lds_vt[buf ^ 1], tid);
+        __syncthreads();
+    };
+    for (int t0 = 0; t0 < t_stop; t0 += 2 * kKeyTile) {
+        step(t0, 0, st0, st1, ids0, ids1);
+        if (t0 + kKeyTile >= t_stop) break;
+        step(t0 + kKeyTile, 1, st1, st0, ids1, ids0);
     }
 
     // ---- normalise and store: lane holds d = 32dt + 8(e/4) + 4half + e%4 ------------

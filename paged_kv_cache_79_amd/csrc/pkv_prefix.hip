@@ -83,20 +83,22 @@ __global__ __launch_bounds__(256, 2) void prefix_kernel(PrefixArgs a, int num_ro
     float m = kNoMax, l = 0.f;           // running max (log2 units) and sum of the row
     const float sl2 = a.scale_log2;
 
-    // keys [k0, k1): load_tile zeroes keys >= k1, masking below removes them
+    // keys [k0, k1): keys >= k1 of the last tile are masked below (see load_ids)
     KvStage<D> stage;
     TileIds<D> ids;
-    load_ids<D>(ids, table, a.g.log2_bs, k1, k0, tid);
-    load_tile<D>(stage, ids, a.g, kb, vb, k1, k0, tid);
-    load_ids<D>(ids, table, a.g.log2_bs, k1, k0 + kKeyTile, tid);
+    TileOffs<D> offs;
+    tile_offsets<D>(offs, a.g.block_size, tid);
+    load_ids<D>(ids, table, a.g, k1, k0, tid);
+    load_tile<D>(stage, ids, offs, a.g, kb, vb, k1, k0, tid);
+    load_ids<D>(ids, table, a.g, k1, k0 + kKeyTile, tid);
     store_tile<D>(stage, lds_k, lds_vt, tid);
     __syncthreads();
 
     for (int t0 = k0; t0 < k1; t0 += kKeyTile) {
         const bool more = t0 + kKeyTile < k1;
         if (more) {
-            load_tile<D>(stage, ids, a.g, kb, vb, k1, t0 + kKeyTile, tid);
-            load_ids<D>(ids, table, a.g.log2_bs, k1, t0 + 2 * kKeyTile, tid);
+            load_tile<D>(stage, ids, offs, a.g, kb, vb, k1, t0 + kKeyTile, tid);
+            load_ids<D>(ids, table, a.g, k1, t0 + 2 * kKeyTile, tid);
         }
 
         // ---- S^T = K Q^T ----------------------------------------------------------
@@ -134,31 +136,31 @@ __global__ __launch_bounds__(256, 2) void prefix_kernel(PrefixArgs a, int num_ro
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, sacc[mt][e]);
-        const float mn = fmaxf(m, swap32_max(mloc) * mul);
-        if (__builtin_amdgcn_ballot_w64(mn > m)) {
-            const float alpha = fast_exp2(m - mn);
+        // The reference maximum m moves only when some row of the wave outgrew it by
+        // more than kLazyMax (log2 units): probabilities stay below 2^kLazyMax, far
+        // inside the bf16 and fp32 ranges, and the rescales of O become rare.
+        const float mx = fmaxf(m, swap32_max(mloc) * mul);
+        if (__builtin_amdgcn_ballot_w64(mx > m + kLazyMax)) {
+            const float alpha = fast_exp2(m - mx);
             l *= alpha;
 #pragma unroll
             for (int dt = 0; dt < P::DT; ++dt)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
+            m = mx;
         }
-        m = mn;
-        float psum = 0.f;
+        const float mn = m;
         u32x4 pk[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int mt = u >> 1, e0 = (u & 1) * 8;
             float p[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                p[j] = fast_exp2(__builtin_fmaf(sacc[mt][e0 + j], mul, -mn));
-                psum += p[j];
-            }
+            for (int j = 0; j < 8; ++j) p[j] = fast_exp2(__builtin_fmaf(sacc[mt][e0 + j], mul, -mn));
             pk[u] = u32x4{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
                           pack_bf16(p[6], p[7])};
+            l = sum_bf16x8(pk[u], l);
         }
-        l += psum;
 
         // ---- O^T += V^T P^T ---------------------------------------------------------
 #pragma unroll
