@@ -93,8 +93,10 @@ int32_t prefix_splits(int32_t max_prefix_len) {
 }
 size_t prefix_state_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                           int32_t max_prefix_len) {
-    return (size_t)num_seqs * num_q_heads * prefix_splits(max_prefix_len) *
-           (size_t)(head_dim + 2) * sizeof(float);
+    // one slot per split, plus the decode's own-token state of the row
+    const int32_t ns = prefix_splits(max_prefix_len);
+    if (ns == 0) return 0;
+    return (size_t)num_seqs * num_q_heads * (ns + 1) * (size_t)(head_dim + 2) * sizeof(float);
 }
 
 // Balanced split over the resident waves (`resident`, from the kernel's occupancy):
@@ -496,7 +498,7 @@ pkv_status paged_attention_decode_shared_prefix(
                                         max_context_len, 0);
     float* pre_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + dec);
     const int32_t nsplit = prefix_splits(max_prefix_len);
-    float* pre_ml = pre_o + (size_t)num_seqs * num_q_heads * nsplit * head_dim;
+    float* pre_ml = pre_o + (size_t)num_seqs * num_q_heads * (nsplit + 1) * head_dim;
 
     // 1. every group's members against their shared prefix (matrix cores)
     PrefixArgs pa;
@@ -514,6 +516,7 @@ pkv_status paged_attention_decode_shared_prefix(
     pa.num_q_heads = num_q_heads;
     pa.max_blocks_per_seq = max_blocks_per_seq;
     pa.num_splits = nsplit;
+    pa.state_stride = nsplit + 1;
     pa.split_tokens = prefix_split_tokens(max_prefix_len);
     pa.scale_log2 = scale * 1.4426950408889634f;
     const hipError_t e1 = launch_prefix(pa, head_dim, group, num_groups, max_group_seqs, stream);

@@ -35,11 +35,13 @@ __device__ __forceinline__ int vt_slot(int k) {
     return (k & ~0xC) | ((k & 4) << 1) | ((k & 8) >> 1);
 }
 
-// Byte offset of 16-byte group g (8 key slots) of V^T row d: groups are XOR-swizzled
-// by d / 8 so that rows 8 apart never share banks.
+// Byte offset of 16-byte group g (8 key slots) of V^T row d.  Groups are XOR-swizzled
+// by 2 * (d / 16): the transposing writes (rows 8 apart, in pairs of keys) then spread
+// over all 64 banks, and the operand reads (16 consecutive rows, 36 dwords apart) stay
+// on distinct banks.
 template <int D>
 __device__ __forceinline__ int vt_off(int d, int g) {
-    return d * PrefillShape<D>::VPITCH + ((g ^ ((d >> 3) & 7)) << 4);
+    return d * PrefillShape<D>::VPITCH + ((g ^ ((d >> 3) & 6)) << 4);
 }
 
 // Thread t loads K rows t / CPR + (256 / CPR) i (whole rows per wave) and the V

@@ -278,11 +278,11 @@ __device__ __forceinline__ void write_rows(const DecodeArgs& a, int s, int h,
     }
 }
 
-// Unnormalised partial state of head hh into row prow0 + hh * prow_step of the
-// workspace (o: D floats per row; (max, sum): 2 floats per row).
+// Unnormalised partial state of head hh into row prow0 + hh * prow_step of the state
+// arrays o_base (D floats per row) and ml_base ((max, sum): 2 floats per row).
 template <bool BF16, int D, int G>
-__device__ __forceinline__ void write_partial(const DecodeArgs& a, int64_t prow0, int64_t prow_step,
-                                              const SegState<BF16, D, G>& st) {
+__device__ __forceinline__ void write_state(float* o_base, float* ml_base, int64_t prow0,
+                                            int64_t prow_step, const SegState<BF16, D, G>& st) {
     using S = DecodeShape<BF16, D>;
     const int lane = threadIdx.x;
     const int ra = lane / S::CPR, rc = lane - (lane / S::CPR) * S::CPR;
@@ -290,15 +290,21 @@ __device__ __forceinline__ void write_partial(const DecodeArgs& a, int64_t prow0
     for (int hh = 0; hh < G; ++hh) {
         const int64_t prow = prow0 + hh * prow_step;
         if (ra == 0) {
-            float* dst = a.part_o + prow * D + rc * S::EPC;
+            float* dst = o_base + prow * D + rc * S::EPC;
 #pragma unroll
             for (int e = 0; e < S::EPC; e += 4)
                 *reinterpret_cast<float4*>(dst + e) =
                     make_float4(st.o[hh][e], st.o[hh][e + 1], st.o[hh][e + 2], st.o[hh][e + 3]);
         }
         if (lane == 0)
-            *reinterpret_cast<float2*>(a.part_ml + prow * 2) = make_float2(st.m[hh], st.l[hh]);
+            *reinterpret_cast<float2*>(ml_base + prow * 2) = make_float2(st.m[hh], st.l[hh]);
     }
+}
+// ... into the balanced split's slots of the workspace.
+template <bool BF16, int D, int G>
+__device__ __forceinline__ void write_partial(const DecodeArgs& a, int64_t prow0, int64_t prow_step,
+                                              const SegState<BF16, D, G>& st) {
+    write_state<BF16, D, G>(a.part_o, a.part_ml, prow0, prow_step, st);
 }
 
 template <bool BF16, int D, int G>
@@ -311,91 +317,6 @@ __device__ __forceinline__ void zero_rows(const DecodeArgs& a, int s, int h) {
     } else {
         float* o = reinterpret_cast<float*>(a.out) + row0;
         for (int e = lane; e < G * D; e += 64) o[e] = 0.f;
-    }
-}
-
-// Shared-prefix mode: combine the prefix pass's partial states of (s, h) (one per key
-// split) with the decode's own state, by log-sum-exp, before the rows are written.
-// All loads are issued before any of them is used: lane hh*K + k reads the (max, sum)
-// of head hh, split k; row group r of the wave reads the o rows of splits r, r + R, ...
-template <bool BF16, int D, int G>
-__device__ __forceinline__ void fold_prefix(const DecodeArgs& a, int s, int h, int start,
-                                            SegState<BF16, D, G>& st) {
-    using S = DecodeShape<BF16, D>;
-    constexpr int K = kMaxPreSplits;
-    constexpr int J = (K + S::R - 1) / S::R;          // splits per row group
-    constexpr int HB = G <= 4 ? G : 1;                // heads whose rows are loaded together
-    static_assert(G * K <= 64, "one lane per (head, split)");
-    const int lane = threadIdx.x;
-    const int ra = lane / S::CPR, rc = lane - ra * S::CPR;
-    // never past the splits the workspace holds, whatever the device lengths say
-    const int ns = min((start + a.pre_split_tokens - 1) / a.pre_split_tokens, a.pre_splits);
-    if (ns <= 0) return;
-    const int ps = a.pre_splits;
-    const int64_t row0 = ((int64_t)s * a.num_q_heads + h * G) * ps;   // (hh, k): row0 + hh*ps + k
-
-    const int lh = lane / K, lk = lane - (lane / K) * K;
-    float2 ml = make_float2(-INFINITY, 0.f);
-    if (lh < G && lk < ns)
-        ml = *reinterpret_cast<const float2*>(a.pre_ml + (row0 + (int64_t)lh * ps + lk) * 2);
-
-    // new max per head: the decode's and the prefix splits' (8-lane groups)
-    float gm = ml.x;
-#pragma unroll
-    for (int d = 1; d < K; d <<= 1) gm = fmaxf(gm, __shfl_xor(gm, d));
-    float Mh[G], c[G];
-    float Ml = 0.f;
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-        Mh[hh] = fmaxf(st.m[hh], u2f(__builtin_amdgcn_readlane(f2u(gm), hh * K)));
-        c[hh] = fast_exp2(st.m[hh] - Mh[hh]);
-        if (lh == hh) Ml = Mh[hh];
-    }
-    const float wl = (lh < G && lk < ns) ? fast_exp2(ml.x - Ml) : 0.f;
-    float ls = wl * ml.y;
-#pragma unroll
-    for (int d = 1; d < K; d <<= 1) ls += __shfl_xor(ls, d);
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-        st.l[hh] = fmaf(st.l[hh], c[hh], u2f(__builtin_amdgcn_readlane(f2u(ls), hh * K)));
-        st.m[hh] = Mh[hh];
-    }
-
-#pragma unroll
-    for (int h0 = 0; h0 < G; h0 += HB) {
-        float v[HB][J][S::EPC];
-#pragma unroll
-        for (int i = 0; i < HB; ++i)
-#pragma unroll
-            for (int j = 0; j < J; ++j) {
-                const int k = min(ra + j * S::R, ns - 1);   // splits past ns get weight 0
-                const float4* src = reinterpret_cast<const float4*>(
-                    a.pre_o + (row0 + (int64_t)(h0 + i) * ps + k) * D + rc * S::EPC);
-#pragma unroll
-                for (int e4 = 0; e4 < S::EPC / 4; ++e4) {
-                    const float4 x = src[e4];
-                    v[i][j][4 * e4 + 0] = x.x;
-                    v[i][j][4 * e4 + 1] = x.y;
-                    v[i][j][4 * e4 + 2] = x.z;
-                    v[i][j][4 * e4 + 3] = x.w;
-                }
-            }
-#pragma unroll
-        for (int i = 0; i < HB; ++i) {
-            float acc[S::EPC];
-#pragma unroll
-            for (int e = 0; e < S::EPC; ++e) acc[e] = 0.f;
-#pragma unroll
-            for (int j = 0; j < J; ++j) {
-                const int k = ra + j * S::R;
-                const float wk = k < K ? __shfl(wl, (h0 + i) * K + min(k, K - 1)) : 0.f;
-#pragma unroll
-                for (int e = 0; e < S::EPC; ++e) acc[e] = fmaf(wk, v[i][j][e], acc[e]);
-            }
-#pragma unroll
-            for (int e = 0; e < S::EPC; ++e)
-                st.o[h0 + i][e] = fmaf(st.o[h0 + i][e], c[h0 + i], group_sum<S::R>(acc[e]));
-        }
     }
 }
 
@@ -437,10 +358,19 @@ __global__ __launch_bounds__(64, (BF16 ? 2 : 1)) void decode_balanced_kernel(Dec
                                            min(ctx, t_first + (tile + seg) * kTile), lds_k, lds_p,
                                            lds_q, st);
         if (tile == 0 && seg == nt_s) {
-            if constexpr (PREFIX) {
-                if (t_first > 0) fold_prefix<BF16, D, G>(a, s, h, t_first, st);
+            bool own = false;
+            if constexpr (PREFIX) own = t_first > 0;
+            if (own) {
+                // the row's state of its own tokens goes to the last slot of its prefix
+                // states; the merge combines them (all loads at once, every row in parallel)
+                const int64_t stride = a.pre_splits + 1;
+                write_state<BF16, D, G>(a.pre_o, a.pre_ml,
+                                        ((int64_t)s * a.num_q_heads + h * G) * stride +
+                                            a.pre_splits,
+                                        stride, st);
+            } else {
+                write_rows<BF16, D, G>(a, s, h, st);
             }
-            write_rows<BF16, D, G>(a, s, h, st);
         } else {
             // the merge reads the piece of the wave holding the unit's first tile from
             // slot 1 and every later wave's from slot 0: a piece that starts the unit can
@@ -464,8 +394,9 @@ __global__ __launch_bounds__(64, (BF16 ? 2 : 1)) void decode_balanced_kernel(Dec
 // Merge the pieces of each (sequence, kv head) that straddles waves, one wave per
 // query head; write zero rows for empty contexts.  The first covering wave holds
 // its piece in its last slot, every later covering wave in its first slot.  In the
-// shared-prefix mode the prefix pass's states of the row are merged in as well (a
-// row with no token after its prefix is the prefix states alone).
+// shared-prefix mode the prefix pass's states of the row are merged in as well,
+// together with the row's own-token state when one wave finished its (sequence, kv
+// head) (a row with no token after its prefix is the prefix states alone).
 // With nq queries per sequence (multi-query decode) the output row blockIdx.x is
 // (s * nq + i) * Hq + hq, and a (sequence, kv head) has nq * G partial rows.
 template <bool BF16, int D, int G, bool PREFIX = false>
@@ -485,33 +416,40 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(DecodeArgs a,
     const int nt = ntiles_of(ctx - start);
     const int ns =
         PREFIX ? min((start + a.pre_split_tokens - 1) / a.pre_split_tokens, a.pre_splits) : 0;
-    const int64_t pre_row0 = ((int64_t)s * a.num_q_heads + hq) * a.pre_splits;
+    const int64_t pre_row0 = ((int64_t)s * a.num_q_heads + hq) * (a.pre_splits + 1);
     const int64_t o = (int64_t)blockIdx.x * D + lane * PER;
     int64_t w0 = 0;
-    int npieces = 0;
+    int npieces = 0, own = 0;
     if (nt > 0) {
         const int64_t T = tiles_all * Hkv, W = min((int64_t)a.num_waves, T);
         const int64_t u0 = before * Hkv + (int64_t)h * nt;
         const Split sp = make_split(a, T, W);
         w0 = unit_owner(sp, u0);
         const int64_t w1 = unit_owner(sp, u0 + nt - 1);
-        if (w0 == w1) return;  // finished by one wave (prefix states folded in there)
-        npieces = (int)(w1 - w0 + 1);
+        if (w0 == w1) {
+            if (ns == 0) return;               // finished and written by one wave
+            own = 1;                           // its state is in the row's last slot
+        } else {
+            npieces = (int)(w1 - w0 + 1);
+        }
     }
-    // the prefix states of the row, all loads in flight together (clamped to ns)
-    constexpr int KP = PREFIX ? kMaxPreSplits : 1;
+    // the prefix states of the row (and its own-token state), all loads in flight
+    // together, clamped to the valid count: state k < ns is split k, state ns the own one
+    constexpr int KP = PREFIX ? kMaxPreSplits + 1 : 1;
+    const int nst = ns + own;
     float2 pml[KP];
     float pv[KP][PER];
-    if (ns > 0) {
+    if (nst > 0) {
 #pragma unroll
         for (int k = 0; k < KP; ++k) {
-            const int64_t r = pre_row0 + min(k, ns - 1);
+            const int kc = min(k, nst - 1);
+            const int64_t r = pre_row0 + (kc < ns ? kc : a.pre_splits);
             pml[k] = *reinterpret_cast<const float2*>(a.pre_ml + r * 2);
 #pragma unroll
             for (int e = 0; e < PER; ++e) pv[k][e] = a.pre_o[r * D + lane * PER + e];
         }
     }
-    if (npieces == 0 && ns == 0) {
+    if (npieces == 0 && nst == 0) {
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
             if constexpr (BF16)
@@ -559,18 +497,18 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(DecodeArgs a,
         }
     }
     L = wave_sum(L);
-    if (ns > 0) {                           // prefix states: (max, sum) the same for every lane
+    if (nst > 0) {                          // prefix states: (max, sum) the same for every lane
         float Mp = M;
 #pragma unroll
         for (int k = 0; k < KP; ++k)
-            if (k < ns) Mp = fmaxf(Mp, pml[k].x);
+            if (k < nst) Mp = fmaxf(Mp, pml[k].x);
         const float c = fast_exp2(M - Mp);
         L *= c;
 #pragma unroll
         for (int e = 0; e < PER; ++e) acc[e] *= c;
 #pragma unroll
         for (int k = 0; k < KP; ++k) {
-            if (k < ns) {
+            if (k < nst) {
                 const float wk = fast_exp2(pml[k].x - Mp);
                 L = fmaf(wk, pml[k].y, L);
 #pragma unroll

@@ -50,7 +50,7 @@ struct SwapArgs {
 };
 
 // Most key splits of a shared prefix (the prefix pass writes one partial state per
-// split; the decode folds them in with all loads in flight at once).
+// split; the merge reads them with all loads in flight at once).
 constexpr int kMaxPreSplits = 8;
 
 struct DecodeArgs {
@@ -79,12 +79,13 @@ struct DecodeArgs {
     int64_t contig_seq_stride;
     int32_t contig_row_stride;
     // Shared-prefix mode: the first seq_prefix[s] tokens of sequence s were attended by
-    // the prefix pass, whose partial states are pre_o [S][Hq][pre_splits][D] and pre_ml
-    // [S][Hq][pre_splits][2] (splits of pre_split_tokens keys); the decode covers the
-    // rest of the context and merges them.  seq_prefix == nullptr: no prefix.
+    // the prefix pass, whose partial states are pre_o [S][Hq][pre_splits + 1][D] and
+    // pre_ml [S][Hq][pre_splits + 1][2] (splits of pre_split_tokens keys; the last slot
+    // of a row takes the decode's state of its own tokens when one wave finishes them);
+    // the merge combines them.  seq_prefix == nullptr: no prefix.
     const int32_t* seq_prefix;
-    const float* pre_o;
-    const float* pre_ml;
+    float* pre_o;
+    float* pre_ml;
     int32_t pre_splits;
     int32_t pre_split_tokens;
     float scale_log2;      // scale * log2(e)
@@ -119,6 +120,7 @@ struct PrefixArgs {
     int32_t num_q_heads;
     int32_t max_blocks_per_seq;
     int32_t num_splits;      // key splits per group prefix
+    int32_t state_stride;    // state slots per row (num_splits + 1)
     int32_t split_tokens;    // keys per split (a multiple of 64)
     float scale_log2;
 };

@@ -22,10 +22,11 @@
 // global loads of tiles j+1 and j+2 are in flight in two register stages (tile
 // j+2's issued at the top of tile j, after the table reads of tile j+3: the
 // in-order load counter then lets each wait cover only what it needs); tile j+1
-// goes into the second LDS buffer after tile j's products, with one barrier per tile.  V is written transposed with a 16-byte XOR
-// swizzle so that the transposing writes meet fewer LDS bank conflicts while the
-// operand reads stay conflict-free.  Workgroups are ordered so that all query
-// tiles of one (chunk, kv head) run on the same XCD and share its L2.
+// goes into the second LDS buffer after tile j's products, with one barrier per
+// tile.  V is written transposed with a 16-byte XOR swizzle that keeps both the
+// transposing writes and the operand reads free of bank conflicts.  Workgroups are
+// ordered so that all query tiles of one (chunk, kv head) run on the same XCD and
+// share its L2.
 // Keys past the context get -inf scores by selection (whatever stale data their K
 // rows hold) and their V rows repeat the last token's row, so stale or NaN slots
 // never reach the output.

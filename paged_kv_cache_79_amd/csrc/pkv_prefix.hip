@@ -25,8 +25,8 @@ __global__ __launch_bounds__(256, 2) void prefix_kernel(PrefixArgs a, int num_ro
                                                         int num_items) {
     using P = PrefillShape<D>;
     constexpr int QP = kRowsPerWg / G;           // members per workgroup
-    __shared__ __attribute__((aligned(16))) char lds_k[kKeyTile * P::KPITCH];
-    __shared__ __attribute__((aligned(16))) char lds_vt[D * P::VPITCH];
+    __shared__ __attribute__((aligned(16))) char lds_k[2][kKeyTile * P::KPITCH];
+    __shared__ __attribute__((aligned(16))) char lds_vt[2][D * P::VPITCH];
 
     const int nwg = gridDim.x;
     const int item = (blockIdx.x % kXcds) * (nwg / kXcds) + blockIdx.x / kXcds;
@@ -83,24 +83,29 @@ __global__ __launch_bounds__(256, 2) void prefix_kernel(PrefixArgs a, int num_ro
     float m = kNoMax, l = 0.f;           // running max (log2 units) and sum of the row
     const float sl2 = a.scale_log2;
 
-    // keys [k0, k1): keys >= k1 of the last tile are masked below (see load_ids)
-    KvStage<D> stage;
-    TileIds<D> ids;
+    // keys [k0, k1): keys >= k1 of the last tile are masked below (see load_ids).
+    // The same pipeline as chunked prefill: two K/V register stages and two id sets
+    // alternating with the tile parity, two LDS buffers, one barrier per tile.
+    KvStage<D> st0, st1;
+    TileIds<D> ids0, ids1;
     TileOffs<D> offs;
     tile_offsets<D>(offs, a.g.block_size, tid);
-    load_ids<D>(ids, table, a.g, k1, k0, tid);
-    load_tile<D>(stage, ids, offs, a.g, kb, vb, k1, k0, tid);
-    load_ids<D>(ids, table, a.g, k1, k0 + kKeyTile, tid);
-    store_tile<D>(stage, lds_k, lds_vt, tid);
+    load_ids<D>(ids0, table, a.g, k1, k0, tid);
+    load_tile<D>(st0, ids0, offs, a.g, kb, vb, k1, k0, tid);
+    load_ids<D>(ids1, table, a.g, k1, k0 + kKeyTile, tid);
+    if (k0 + kKeyTile < k1) load_tile<D>(st1, ids1, offs, a.g, kb, vb, k1, k0 + kKeyTile, tid);
+    load_ids<D>(ids0, table, a.g, k1, k0 + 2 * kKeyTile, tid);
+    store_tile<D>(st0, lds_k[0], lds_vt[0], tid);
     __syncthreads();
 
-    for (int t0 = k0; t0 < k1; t0 += kKeyTile) {
-        const bool more = t0 + kKeyTile < k1;
-        if (more) {
-            load_tile<D>(stage, ids, offs, a.g, kb, vb, k1, t0 + kKeyTile, tid);
-            load_ids<D>(ids, table, a.g, k1, t0 + 2 * kKeyTile, tid);
+    auto step = [&](int t0, int buf, KvStage<D>& next2, const KvStage<D>& next1,
+                    const TileIds<D>& use, TileIds<D>& load) {
+        const char* tk = lds_k[buf];
+        const char* tv = lds_vt[buf];
+        if (t0 + 2 * kKeyTile < k1) {
+            load_ids<D>(load, table, a.g, k1, t0 + 3 * kKeyTile, tid);
+            load_tile<D>(next2, use, offs, a.g, kb, vb, k1, t0 + 2 * kKeyTile, tid);
         }
-
         // ---- S^T = K Q^T ----------------------------------------------------------
         floatx16_t sacc[2];
 #pragma unroll
@@ -110,7 +115,7 @@ __global__ __launch_bounds__(256, 2) void prefix_kernel(PrefixArgs a, int num_ro
 #pragma unroll
             for (int ks = 0; ks < P::KSTEPS; ++ks) {
                 const u32x4 ka = *reinterpret_cast<const u32x4*>(
-                    lds_k + (mt * 32 + n) * P::KPITCH + ks * 32 + half * 16);
+                    tk + (mt * 32 + n) * P::KPITCH + ks * 32 + half * 16);
                 sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     __builtin_bit_cast(bf16x8_t, ka), __builtin_bit_cast(bf16x8_t, qreg[ks]),
                     sacc[mt], 0, 0, 0);
@@ -168,22 +173,24 @@ __global__ __launch_bounds__(256, 2) void prefix_kernel(PrefixArgs a, int num_ro
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const u32x4 va = *reinterpret_cast<const u32x4*>(
-                    lds_vt + vt_off<D>(dt * 32 + n, 2 * u + half));
+                    tv + vt_off<D>(dt * 32 + n, 2 * u + half));
                 oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     __builtin_bit_cast(bf16x8_t, va), __builtin_bit_cast(bf16x8_t, pk[u]),
                     oacc[dt], 0, 0, 0);
             }
-        __syncthreads();                 // every wave is done with this tile's LDS
-        if (more) {
-            store_tile<D>(stage, lds_k, lds_vt, tid);
-            __syncthreads();
-        }
+        if (t0 + kKeyTile < k1) store_tile<D>(next1, lds_k[buf ^ 1], lds_vt[buf ^ 1], tid);
+        __syncthreads();
+    };
+    for (int t0 = k0; t0 < k1; t0 += 2 * kKeyTile) {
+        step(t0, 0, st0, st1, ids0, ids1);
+        if (t0 + kKeyTile >= k1) break;
+        step(t0 + kKeyTile, 1, st1, st0, ids1, ids0);
     }
 
     // ---- partial state of the row: lane holds d = 32dt + 8(e/4) + 4half + e%4 -------
     const float lt = swap32_sum(l);
     if (!row_valid) return;
-    const int64_t prow = (seq * Hq + (int64_t)h * G + hh) * a.num_splits + split;
+    const int64_t prow = (seq * Hq + (int64_t)h * G + hh) * a.state_stride + split;
     float* po = a.pre_o + prow * D;
 #pragma unroll
     for (int dt = 0; dt < P::DT; ++dt)
