@@ -111,15 +111,21 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, int s, int h
         // loads then take the scalar base + 32-bit lane offset form
         uint32_t loff = lane_off;
         asm volatile("" : "+v"(loff));
+        // Only a sequence's last tile can be partial: its groups of rows past the context
+        // re-read the last group inside it (a cache hit, no HBM traffic); their scores
+        // and V rows are masked below.
+        const int last_row = __builtin_amdgcn_readfirstlane(min(t_end - t0 - 1, kTile - 1)) &
+                             ~(S::R - 1);
 #pragma unroll
         for (int i = 0; i < S::NL; ++i) {
+            const int row = min(i * S::R, last_row);    // uniform
             uint64_t base;
             if constexpr (CONTIG) {
-                // row t0 + i*R of the sequence's slab (the slab holds a whole number of tiles)
-                const uint32_t ur = (uint32_t)(t0 + i * S::R);
+                // row t0 + row of the sequence's slab (the slab holds a whole number of tiles)
+                const uint32_t ur = (uint32_t)(t0 + row);
                 base = ((uint64_t)__umulhi(ur, row_stride) << 32) | (uint64_t)(ur * row_stride);
             } else {
-                const int rel = (i * S::R) >> a.g.log2_bs;   // block of this load inside the tile
+                const int rel = row >> a.g.log2_bs;   // block of this load inside the tile
                 int pb = __builtin_amdgcn_readlane(tab, rel);
                 pb = ((unsigned)pb < (unsigned)a.g.num_blocks) ? pb : 0;   // never a bad id
                 // scalar base: block, head and first row of this load; per-lane part is
@@ -127,7 +133,7 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, int s, int h
                 // on the scalar unit.
                 const uint32_t ub = (uint32_t)pb, us = (uint32_t)a.g.block_stride_bytes;
                 base = (((uint64_t)__umulhi(ub, us) << 32) | (uint64_t)(ub * us)) +
-                       (uint64_t)(((i * S::R) & (bs - 1)) * S::RB);
+                       (uint64_t)((row & (bs - 1)) * S::RB);
             }
             // K and V are read exactly once: nontemporal loads keep them from
             // displacing reusable lines (tables, q, partials) in the caches
@@ -334,7 +340,8 @@ __global__ __launch_bounds__(64, (BF16 ? 2 : 1)) void decode_balanced_kernel(Dec
     // units = 64-token tiles, ordered by (sequence, kv head, tile); with W <= T every
     // wave's range [wT/W, (w+1)T/W) is non-empty
     int64_t tiles_all, unused;
-    count_tiles<PREFIX>(a, 0, tiles_all, unused);
+    int first[4];
+    count_tiles<PREFIX>(a, 0, tiles_all, unused, first);
     const int64_t T = tiles_all * Hkv;
     const int64_t W = min((int64_t)a.num_waves, T);
     if (w >= W) return;
@@ -343,7 +350,7 @@ __global__ __launch_bounds__(64, (BF16 ? 2 : 1)) void decode_balanced_kernel(Dec
 
     int s = 0;
     int64_t before = 0;
-    locate_unit<PREFIX>(a, b, Hkv, s, before);
+    locate_unit<PREFIX>(a, b, Hkv, first, s, before);
     int nt_s = unit_tiles<PREFIX>(a, s);
     const int64_t rel = b - before * Hkv;
     int h = (int)(rel / nt_s);

@@ -268,7 +268,8 @@ __global__ __launch_bounds__(64, 2) void decode_mq_kernel(DecodeArgs a, int nq) 
     const int rows = nq * G;
 
     int64_t tiles_all, unused;
-    count_tiles(a, 0, tiles_all, unused);
+    int first[4];
+    count_tiles(a, 0, tiles_all, unused, first);
     const int64_t T = tiles_all * Hkv;
     const int64_t W = min((int64_t)a.num_waves, T);
     if (w >= W) return;
@@ -277,7 +278,7 @@ __global__ __launch_bounds__(64, 2) void decode_mq_kernel(DecodeArgs a, int nq) 
 
     int s = 0;
     int64_t before = 0;
-    locate_unit(a, b, Hkv, s, before);
+    locate_unit(a, b, Hkv, first, s, before);
     int nt_s = unit_tiles<false>(a, s);
     const int64_t rel = b - before * Hkv;
     int h = (int)(rel / nt_s);

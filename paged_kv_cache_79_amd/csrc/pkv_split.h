@@ -55,10 +55,11 @@ __device__ __forceinline__ int unit_tiles(const DecodeArgs& a, int s) {
 }
 
 // Tiles of the whole batch (all sequences, one kv head) and tiles before sequence `upto`.
-// Four chunks of 64 sequences per pass, their loads issued together.
+// Four chunks of 64 sequences per pass, their loads issued together; the counts of
+// the first 256 sequences stay in first[q] (sequence 64q + lane) for locate_unit.
 template <bool PREFIX = false>
 __device__ __forceinline__ void count_tiles(const DecodeArgs& a, int upto, int64_t& total,
-                                            int64_t& before) {
+                                            int64_t& before, int (&first)[4]) {
     const int lane = threadIdx.x;
     total = 0;
     before = 0;
@@ -69,6 +70,10 @@ __device__ __forceinline__ void count_tiles(const DecodeArgs& a, int upto, int64
             const int sl = c0 + q * 64 + lane;
             nt[q] = sl < a.num_seqs ? unit_tiles<PREFIX>(a, sl) : 0;
         }
+        if (c0 == 0) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) first[q] = nt[q];
+        }
         int t = 0, u = 0;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -78,6 +83,12 @@ __device__ __forceinline__ void count_tiles(const DecodeArgs& a, int upto, int64
         total += wave_sum_int(t);
         before += wave_sum_int(u);
     }
+}
+template <bool PREFIX = false>
+__device__ __forceinline__ void count_tiles(const DecodeArgs& a, int upto, int64_t& total,
+                                            int64_t& before) {
+    int first[4];
+    count_tiles<PREFIX>(a, upto, total, before, first);
 }
 
 // The split of T tiles over W waves: the first Wl waves share the first F tiles
@@ -107,17 +118,24 @@ __device__ __forceinline__ int64_t unit_owner(const Split& p, int64_t u) {
 }
 
 // Sequence holding unit b (the first s with Hkv * (tiles up to s) > b) and the tiles
-// of all sequences before it; one wave-wide inclusive scan per 64 sequences.
+// of all sequences before it; one wave-wide inclusive scan per 64 sequences, over the
+// counts count_tiles kept for the first 256 (no reload) and reloaded beyond.
 template <bool PREFIX = false>
-__device__ __forceinline__ void locate_unit(const DecodeArgs& a, int64_t b, int Hkv, int& s,
-                                            int64_t& before) {
+__device__ __forceinline__ void locate_unit(const DecodeArgs& a, int64_t b, int Hkv,
+                                            const int (&first)[4], int& s, int64_t& before) {
     const int lane = threadIdx.x;
     s = 0;
     before = 0;
     int64_t carry = 0;
     for (int c0 = 0; c0 < a.num_seqs; c0 += 64) {
         const int sl = c0 + lane;
-        const int nt = sl < a.num_seqs ? unit_tiles<PREFIX>(a, sl) : 0;
+        int nt;
+        if (c0 < 256) {
+            const int q = c0 >> 6;                 // uniform
+            nt = q == 0 ? first[0] : q == 1 ? first[1] : q == 2 ? first[2] : first[3];
+        } else {
+            nt = sl < a.num_seqs ? unit_tiles<PREFIX>(a, sl) : 0;
+        }
         int incl = nt;
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
