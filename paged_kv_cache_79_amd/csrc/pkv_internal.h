@@ -93,10 +93,10 @@ struct DecodeArgs {
 
 // Share of the tiles (in 1/1024) that the balanced split gives the first half of its
 // waves when two waves share each SIMD: the first-dispatched wave of a SIMD wins
-// issue arbitration and streams ~1.3x faster while its partner is active, so an
-// even split leaves the second half as the critical path (measured on MI355X: 584
-// shortens the long-context decode by ~3% and leaves the GQA decode unchanged).
-constexpr int kLeadShareQ10 = 584;
+// issue arbitration and streams faster while its partner is active, so an even
+// split leaves the second half as the critical path.  Measured on MI355X (sweep of
+// 512..704): 624 is best for both the long-context and the GQA decode.
+constexpr int kLeadShareQ10 = 624;
 
 // Persistent waves the balanced decode launches on the current device.
 int decode_balanced_waves(bool is_bf16, int head_dim, int group);

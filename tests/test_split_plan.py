@@ -118,21 +118,21 @@ def test_balanced_split_covers_and_merges(seed):
     else:
         ctx = rng.integers(60, 70, S)                    # around one tile
     W = int(rng.choice([1, 3, 7, 64, 2048]))
-    lead = int(rng.choice([512, 584, 700, 1000]))
+    lead = int(rng.choice([512, 584, 624, 700, 1000]))
     nt, T, Weff, (F, Wl), written, finished, seen = plan(ctx, hkv, W, lead)
     check(ctx, hkv, nt, T, Weff, F, Wl, written, finished, seen)
 
 
 @pytest.mark.parametrize("shape", ["gqa", "long"])
 def test_skewed_split_at_benchmark_shapes(shape):
-    """The split the bf16 kernels take on a 256-CU device: 2048 waves, lead share 584."""
+    """The split the bf16 kernels take on a 256-CU device: 2048 waves, lead share 624."""
     rng = np.random.Generator(np.random.PCG64(7))
     if shape == "gqa":
         ctx, hkv = rng.integers(128, 4096, 64, endpoint=True), 8
     else:
         ctx, hkv = rng.integers(32768, 200000, 8, endpoint=True), 4
-    nt, T, Weff, (F, Wl), written, finished, seen = plan(ctx, hkv, 2048, 584)
-    assert Wl == 1024 and F == T * 584 // 1024          # the skewed path is taken
+    nt, T, Weff, (F, Wl), written, finished, seen = plan(ctx, hkv, 2048, 624)
+    assert Wl == 1024 and F == T * 624 // 1024          # the skewed path is taken
     check(ctx, hkv, nt, T, Weff, F, Wl, written, finished, seen)
-    # lead waves hold ~1.33x the tiles of the others
-    assert 1.3 < (F / Wl) / ((T - F) / (Weff - Wl)) < 1.36
+    # lead waves hold ~1.56x the tiles of the others
+    assert 1.53 < (F / Wl) / ((T - F) / (Weff - Wl)) < 1.59
