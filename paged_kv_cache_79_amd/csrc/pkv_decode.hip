@@ -440,23 +440,12 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(DecodeArgs a,
             npieces = (int)(w1 - w0 + 1);
         }
     }
-    // the prefix states of the row (and its own-token state), all loads in flight
-    // together, clamped to the valid count: state k < ns is split k, state ns the own one
-    constexpr int KP = PREFIX ? kMaxPreSplits + 1 : 1;
-    const int nst = ns + own;
-    float2 pml[KP];
-    float pv[KP][PER];
-    if (nst > 0) {
-#pragma unroll
-        for (int k = 0; k < KP; ++k) {
-            const int kc = min(k, nst - 1);
-            const int64_t r = pre_row0 + (kc < ns ? kc : a.pre_splits);
-            pml[k] = *reinterpret_cast<const float2*>(a.pre_ml + r * 2);
-#pragma unroll
-            for (int e = 0; e < PER; ++e) pv[k][e] = a.pre_o[r * D + lane * PER + e];
-        }
-    }
-    if (npieces == 0 && nst == 0) {
+    // The states of the row: in the shared-prefix mode its ns prefix splits and, when
+    // one wave finished the (sequence, kv head), the own-token state in the row's last
+    // slot; then the pieces of the covering waves.
+    const int npre = ns + own;
+    const int nst = npre + npieces;
+    if (nst == 0) {
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
             if constexpr (BF16)
@@ -466,9 +455,21 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(DecodeArgs a,
         }
         return;
     }
-    auto slot_row = [&](int p) -> int64_t { return ((w0 + p) * 2 + (p == 0 ? 1 : 0)) * rows + r; };
-    // pieces in batches of kBatch, each batch one round of loads: lane j holds the
-    // (max, sum) of piece c0 + j while every lane loads its part of all the batch's
+    auto state = [&](int k, const float*& so, const float*& sml) {
+        if (PREFIX && k < npre) {
+            const int64_t rr = pre_row0 + (k < ns ? k : a.pre_splits);
+            so = a.pre_o + rr * D;
+            sml = a.pre_ml + rr * 2;
+        } else {
+            // the first covering wave holds its piece in slot 1, later ones in slot 0
+            const int p = k - npre;
+            const int64_t rr = ((w0 + p) * 2 + (p == 0 ? 1 : 0)) * rows + r;
+            so = a.part_o + rr * D;
+            sml = a.part_ml + rr * 2;
+        }
+    };
+    // states in batches of kBatch, each batch one round of loads: lane j holds the
+    // (max, sum) of state c0 + j while every lane loads its part of all the batch's
     // output rows (unconditionally, clamped to the batch); a running maximum rescales
     // what earlier batches accumulated, as in the online softmax
     constexpr int kBatch = 16;
@@ -476,16 +477,21 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(DecodeArgs a,
     float acc[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) acc[k] = 0.f;
-    for (int c0 = 0; c0 < npieces; c0 += kBatch) {
-        const int cnt = min(kBatch, npieces - c0);
+    for (int c0 = 0; c0 < nst; c0 += kBatch) {
+        const int cnt = min(kBatch, nst - c0);
         float2 ml = make_float2(-INFINITY, 0.f);
-        if (lane < cnt) ml = *reinterpret_cast<const float2*>(a.part_ml + slot_row(c0 + lane) * 2);
+        if (lane < cnt) {
+            const float *so, *sml;
+            state(c0 + lane, so, sml);
+            ml = *reinterpret_cast<const float2*>(sml);
+        }
         float v[kBatch][PER];
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
-            const float* src = a.part_o + slot_row(c0 + min(j, cnt - 1)) * D + lane * PER;
+            const float *so, *sml;
+            state(c0 + min(j, cnt - 1), so, sml);
 #pragma unroll
-            for (int k = 0; k < PER; ++k) v[j][k] = src[k];
+            for (int k = 0; k < PER; ++k) v[j][k] = so[lane * PER + k];
         }
         const float Mn = fmaxf(M, wave_max(ml.x));
         const float c = fast_exp2(M - Mn);
@@ -504,25 +510,6 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(DecodeArgs a,
         }
     }
     L = wave_sum(L);
-    if (nst > 0) {                          // prefix states: (max, sum) the same for every lane
-        float Mp = M;
-#pragma unroll
-        for (int k = 0; k < KP; ++k)
-            if (k < nst) Mp = fmaxf(Mp, pml[k].x);
-        const float c = fast_exp2(M - Mp);
-        L *= c;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] *= c;
-#pragma unroll
-        for (int k = 0; k < KP; ++k) {
-            if (k < nst) {
-                const float wk = fast_exp2(pml[k].x - Mp);
-                L = fmaf(wk, pml[k].y, L);
-#pragma unroll
-                for (int e = 0; e < PER; ++e) acc[e] = fmaf(wk, pv[k][e], acc[e]);
-            }
-        }
-    }
     const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
