@@ -62,7 +62,8 @@ typedef enum pkv_status {
     PKV_ERR_UNSUPPORTED = 4,   /* valid but not implemented (head_dim, block_size, group size, dtype) */
     PKV_ERR_WORKSPACE = 5,     /* workspace missing or smaller than required */
     PKV_ERR_LAUNCH = 6,        /* the HIP runtime refused a launch or copy */
-    PKV_ERR_NO_BLOCKS = 7      /* block pool: not enough free blocks (nothing was taken) */
+    PKV_ERR_NO_BLOCKS = 7,     /* block pool: not enough free blocks (nothing was taken) */
+    PKV_ERR_VALIDATION = 8     /* pkv_validate found violated preconditions (binding-level) */
 } pkv_status;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -239,6 +240,31 @@ pkv_status paged_attention_decode_shared_prefix(
     const int32_t* seq_prefix_lens, const int32_t* group_first_seq, const int32_t* group_num_seqs,
     const int32_t* group_prefix_lens, int32_t num_groups, int32_t max_group_seqs,
     int32_t max_prefix_len, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * pkv_validate -- device-side check of the device-content preconditions that the other
+ * calls trust and do not check ("2.1 PagedAttention", section 3: token t of sequence s
+ * lives in block block_tables[s][t / block_size], and a write puts token i at slot
+ * block * block_size + offset; section 6: copy-on-write copies whole blocks).
+ * Enqueues kernels that write counts[4] (int32, device memory owned by the caller):
+ *   counts[0]  table entries a context reaches (j < min(ceil(ctx / block_size),
+ *              max_blocks_per_seq)) outside [0, num_blocks)
+ *   counts[1]  sequences with context_lens[s] < 0 or > max_blocks_per_seq * block_size
+ *   counts[2]  tokens whose slot is >= num_blocks * block_size, or equals an earlier
+ *              token's slot (negative slots are padding)
+ *   counts[3]  copy pairs with an id outside [0, num_blocks), a destination written by
+ *              an earlier pair, or a destination that some pair reads
+ * Each part is skipped when its count (num_seqs, num_tokens, num_pairs) is 0.  The
+ * call does not wait: synchronise the stream, then read counts (all zero = valid).
+ * Cost is O(n^2) in num_tokens and num_pairs: a debugging aid, not for every step.
+ * Errors: PKV_ERR_NULL / PKV_ERR_SHAPE for missing pointers or negative sizes (nothing
+ * enqueued); PKV_ERR_LAUNCH if a launch fails.
+ */
+pkv_status pkv_validate(int32_t num_blocks, int32_t block_size, const int32_t* block_tables,
+                        int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                        const int64_t* slot_mapping, int32_t num_tokens,
+                        const int64_t* block_mapping, int32_t num_pairs, int32_t* counts,
+                        hipStream_t stream);
 
 /*
  * paged_attention_prefill_chunk -- causal attention of prefill query chunks over

@@ -22,6 +22,7 @@ from .paged import (  # noqa: F401
     lse_merge, kv_size_bytes,
     blocks_needed, tail_waste,
 )
+from .preconditions import validate  # noqa: F401
 
 # function -> what pins it (see tests/test_oracle_pins.py)
 PINS = {
@@ -38,6 +39,8 @@ PINS = {
     "copy_blocks": "snapshot semantics on hand-built pairs; CoW divergence scenario",
     "swap_blocks": "bit copies between two pools on hand-built pairs; a round trip restores "
                    "the original blocks",
+    "validate": "hand-built tables, lengths, slots and pairs with a known number of "
+                "violations of each rule; clean workloads count zero",
     "block_pool.BlockPoolModel/block_hash": "the pages' pool rules as scenarios and published "
                                             "FNV-1a vectors (tests/test_block_pool.py)",
     "partition_partials/lse_merge": "merge over any partition equals the unsplit result",

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 # every symbol include/pagedkv.h declares
 EXPORTS = (
     "pkv_status_string",
+    "pkv_validate",
     "paged_kv_write",
     "copy_blocks",
     "paged_attention_decode_workspace_bytes",
@@ -45,6 +46,7 @@ EXPORTS = (
 
 PKV_F32, PKV_BF16 = 0, 1
 PKV_ERR_NO_BLOCKS = 7
+PKV_ERR_VALIDATION = 8
 
 _lib = None
 
@@ -99,6 +101,8 @@ def load_library(path: Optional[str] = None):
     U64 = ctypes.c_uint64
     lib.swap_blocks.argtypes = [ctypes.c_int, VP, VP, I32, VP, VP, I32, I32, I32, I32, VP, I32, VP]
     lib.swap_blocks.restype = ctypes.c_int
+    lib.pkv_validate.argtypes = [I32, I32, VP, I32, VP, I32, VP, I32, VP, I32, VP, VP]
+    lib.pkv_validate.restype = ctypes.c_int
     lib.pkv_pool_create.argtypes = [I32]
     lib.pkv_pool_create.restype = VP
     lib.pkv_pool_destroy.argtypes = [VP]
@@ -424,6 +428,47 @@ def swap_blocks(dst_k, dst_v, src_k, src_v, block_mapping, stream=None) -> None:
         _dtype_code(src_k), _ptr(dst_k), _ptr(dst_v), int(dst_k.shape[0]), _ptr(src_k), _ptr(src_v),
         int(src_k.shape[0]), hkv, bs, d, m.ctypes.data if m.size else None, int(m.shape[0]),
         _stream(stream)))
+
+
+def validate(num_blocks: int, block_size: int, block_tables=None, context_lens=None,
+             slot_mapping=None, block_mapping=None, stream=None) -> dict:
+    """Device-side check of the preconditions the other calls trust (pkv_validate):
+    returns the violation counts after synchronising the stream."""
+    import torch
+    dev_t = None
+    for n, t, dt in (("block_tables", block_tables, torch.int32),
+                     ("context_lens", context_lens, torch.int32),
+                     ("slot_mapping", slot_mapping, torch.int64),
+                     ("block_mapping", block_mapping, torch.int64)):
+        if t is not None:
+            _dev(t, n, dt)
+            dev_t = t
+    if dev_t is None:
+        raise ValueError("nothing to validate")
+    S = 0 if context_lens is None else int(context_lens.numel())
+    if S and (block_tables is None or block_tables.dim() != 2 or block_tables.shape[0] != S):
+        raise ValueError("block_tables must be [num_seqs][max_blocks] with context_lens [num_seqs]")
+    mb = int(block_tables.shape[1]) if block_tables is not None and block_tables.dim() == 2 else 0
+    T = 0 if slot_mapping is None else int(slot_mapping.numel())
+    n = 0 if block_mapping is None else int(block_mapping.numel()) // 2
+    counts = torch.empty(4, dtype=torch.int32, device=dev_t.device)
+    _check("pkv_validate", load_library().pkv_validate(
+        int(num_blocks), int(block_size), _ptr(block_tables), mb, _ptr(context_lens), S,
+        _ptr(slot_mapping), T, _ptr(block_mapping), n, _ptr(counts), _stream(stream)))
+    if stream is None:
+        torch.cuda.current_stream(dev_t.device).synchronize()
+    else:
+        stream.synchronize()
+    c = counts.cpu().tolist()
+    return {"bad_table_entries": c[0], "bad_context_lens": c[1], "bad_slots": c[2],
+            "bad_copy_pairs": c[3]}
+
+
+def check_preconditions(num_blocks: int, block_size: int, **kw) -> None:
+    """validate(), raising PagedKVError (PKV_ERR_VALIDATION) if anything is violated."""
+    c = validate(num_blocks, block_size, **kw)
+    if any(c.values()):
+        raise PagedKVError("pkv_validate", PKV_ERR_VALIDATION, str(c))
 
 
 def block_hash(parent: int, tokens) -> int:

@@ -21,7 +21,8 @@ LIB = os.path.join(PKG, "libpagedkv.so")
 ARCH = "gfx950"
 
 SOURCES = ["pkv_api.hip", "pkv_write_copy.hip", "pkv_decode.hip", "pkv_prefill.hip",
-           "pkv_prefix.hip", "pkv_decode_mq.hip", "pkv_block_pool.cpp"]
+           "pkv_prefix.hip", "pkv_decode_mq.hip", "pkv_validate.hip",
+           "pkv_block_pool.cpp"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

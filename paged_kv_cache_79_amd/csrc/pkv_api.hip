@@ -130,6 +130,7 @@ const char* pkv_status_string(pkv_status s) {
         case PKV_ERR_WORKSPACE: return "PKV_ERR_WORKSPACE: workspace missing or too small";
         case PKV_ERR_LAUNCH: return "PKV_ERR_LAUNCH: kernel launch or copy failed";
         case PKV_ERR_NO_BLOCKS: return "PKV_ERR_NO_BLOCKS: not enough free blocks in the pool";
+        case PKV_ERR_VALIDATION: return "PKV_ERR_VALIDATION: device contents violate a precondition";
     }
     return "PKV_ERR_UNKNOWN";
 }
@@ -171,6 +172,33 @@ pkv_status copy_blocks(pkv_dtype dtype, void* k_pool, void* v_pool, int32_t num_
     a.num_pairs = num_pairs;
     a.g = g;
     return launch_status(launch_copy_blocks(a, stream));
+}
+
+pkv_status pkv_validate(int32_t num_blocks, int32_t block_size, const int32_t* block_tables,
+                        int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                        const int64_t* slot_mapping, int32_t num_tokens,
+                        const int64_t* block_mapping, int32_t num_pairs, int32_t* counts,
+                        hipStream_t stream) {
+    if (num_blocks <= 0 || block_size <= 0 || max_blocks_per_seq < 0 || num_seqs < 0 ||
+        num_tokens < 0 || num_pairs < 0)
+        return PKV_ERR_SHAPE;
+    if (!counts) return PKV_ERR_NULL;
+    if (num_seqs > 0 && (!block_tables || !context_lens)) return PKV_ERR_NULL;
+    if (num_tokens > 0 && !slot_mapping) return PKV_ERR_NULL;
+    if (num_pairs > 0 && !block_mapping) return PKV_ERR_NULL;
+    ValidateArgs v;
+    v.block_tables = block_tables;
+    v.context_lens = context_lens;
+    v.slot_mapping = slot_mapping;
+    v.block_mapping = block_mapping;
+    v.counts = counts;
+    v.num_blocks = num_blocks;
+    v.block_size = block_size;
+    v.max_blocks_per_seq = max_blocks_per_seq;
+    v.num_seqs = num_seqs;
+    v.num_tokens = num_tokens;
+    v.num_pairs = num_pairs;
+    return launch_status(launch_validate(v, stream));
 }
 
 size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,

@@ -142,6 +142,22 @@ struct PrefillArgs {
     float scale_log2;
 };
 
+// Device-side precondition check (pkv_validate): counts [4] in device memory.
+struct ValidateArgs {
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    const int64_t* slot_mapping;
+    const int64_t* block_mapping;
+    int32_t* counts;
+    int32_t num_blocks;
+    int32_t block_size;
+    int32_t max_blocks_per_seq;
+    int32_t num_seqs;
+    int32_t num_tokens;
+    int32_t num_pairs;
+};
+
+hipError_t launch_validate(const ValidateArgs& v, hipStream_t st);
 hipError_t launch_kv_write(const WriteArgs& a, hipStream_t st);
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t st);
 hipError_t launch_swap(const SwapArgs& a, hipStream_t st);

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in range(8):
+    for code in range(9):
         assert pkv.status_string(code).startswith("PKV_")
     assert "UNKNOWN" in pkv.status_string(99)
 
@@ -205,6 +205,17 @@ def test_multi_query_workspace_sizes(lib):
     assert f(2, 1, 8, 2, 128) == lib.paged_attention_decode_workspace_bytes(2, 8, 2, 128, 4096, 0)
     assert f(2, 4, 8, 2, 128) == 4 * f(2, 1, 8, 2, 128)
     assert f(0, 4, 8, 2, 128) == 0 and f(2, 0, 8, 2, 128) == 0
+
+
+@dummy_ptrs
+def test_validate_validation(lib):
+    f = lib.pkv_validate
+    assert f(0, 16, P, 4, P, 2, None, 0, None, 0, P, None) == SHAPE       # no blocks
+    assert f(8, 16, P, 4, P, -1, None, 0, None, 0, P, None) == SHAPE      # negative count
+    assert f(8, 16, P, 4, P, 2, None, 0, None, 0, None, None) == NULL     # no counts
+    assert f(8, 16, None, 4, P, 2, None, 0, None, 0, P, None) == NULL     # tables missing
+    assert f(8, 16, None, 0, None, 0, None, 3, None, 0, P, None) == NULL  # slots missing
+    assert f(8, 16, None, 0, None, 0, None, 0, None, 2, P, None) == NULL  # pairs missing
 
 
 @dummy_ptrs
