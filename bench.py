@@ -3,6 +3,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gqa|long|prefix_cow|mixed|spec|swap]
                     [--layout paged|contiguous] [--block-size 8|16|32] [--shared-prefix]
+                    [--spec-path multi_query|prefill] [--no-cpu-baseline] [--no-read-ceiling]
 
 One step is one pass of the path over one synthetic batch: the step's cache
 write (paged_kv_write) followed by paged decode attention (split-context
@@ -15,7 +16,9 @@ Infinity Cache.
 Prints ONE JSON line: metric/value = decode KV GB/s of the whole step
 (algorithmic KV bytes: K and V of every valid token, read once per
 (sequence, kv head)), plus seqs/s, a roofline object for the decode kernels
-(HIP events on the launch stream) and the CPU oracle timed on this host.
+(HIP events on the launch stream; also per-call p10/p50/p90 and the fraction of
+the measured streaming-read ceiling of a 4 GiB buffer), the device time of the
+step's write and block-copy calls, and the CPU oracle timed on this host.
 """
 from __future__ import annotations
 
@@ -133,6 +136,74 @@ def cpu_baseline(b, target_s=12.0):
 # ----------------------------------------------------------------------------
 # GPU
 # ----------------------------------------------------------------------------
+def read_ceiling(buffer_bytes=4 << 30, waves=8192, reps=5):
+    """Measured streaming-read ceiling: pkv_bench_read (libpkvbench.so) over a buffer
+    16x the 256 MB Infinity Cache; median GB/s of 3 runs of `reps` passes."""
+    import ctypes
+    import torch
+    import paged_kv_cache_79_amd as pkv
+    path = os.path.join(os.path.dirname(pkv.LIB_PATH), "libpkvbench.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"{path} is missing: run __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
+    lib.pkv_bench_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                   ctypes.c_int32, ctypes.c_void_p]
+    lib.pkv_bench_read.restype = ctypes.c_int
+    buf = torch.ones(buffer_bytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.empty(waves * 64, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def once():
+        rc = lib.pkv_bench_read(buf.data_ptr(), buffer_bytes, sink.data_ptr(), waves,
+                                stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"pkv_bench_read failed: {rc}")
+
+    once()
+    runs = []
+    for _ in range(3):
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for _ in range(reps):
+            once()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        runs.append(buffer_bytes * reps / (t0.elapsed_time(t1) * 1e-3) / 1e9)
+    del buf, sink
+    return sorted(runs)[1]
+
+
+def device_us(fn, n, busy, stream):
+    """Device time per call of a short call: the n calls are enqueued while the stream
+    is still busy with `busy` (long work issued first), so the events measure the
+    device, not the host's call rate."""
+    import torch
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    busy()
+    t0.record(stream)
+    for i in range(n):
+        fn(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) * 1e3 / n
+
+
+def per_call_us(fn, n, stream):
+    """Each of n calls bracketed by its own pair of events: (p10, p50, p90) in us."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        fn(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    return [round(float(x), 2) for x in np.percentile(t, [10, 50, 90])]
+
 def _dev(a):
     import torch
     a = np.ascontiguousarray(a)
@@ -392,6 +463,25 @@ def run(args):
     # the decode kernels alone, same inputs and pool rotation, for the roofline
     dec_runs = [timed(decode, args.steps) for _ in range(3)]
     dec_avg = sorted(dec_runs)[1]
+    dec_pct = per_call_us(decode, args.steps, stream)
+    # the step's other calls alone
+    # the step's other calls alone (device time: enqueued behind 8 decode calls)
+    parts = {}
+    if not contig:
+        def busy():
+            for i in range(8):
+                decode(i)
+
+        def write(i):
+            kp, vp = pools[i % copies]
+            pkv.paged_kv_write(kp, vp, k_new, v_new, slots)
+        parts["paged_kv_write_us"] = round(device_us(write, 10, busy, stream), 2)
+        if cow_map is not None:
+            def copy(i):
+                kp, vp = pools[i % copies]
+                pkv.copy_blocks(kp, vp, cow_map)
+            parts["copy_blocks_us"] = round(device_us(copy, 10, busy, stream), 2)
+    ceiling = read_ceiling() if not args.no_read_ceiling else None
     byts = kv_bytes(b.context_lens, b.num_kv_heads, b.head_dim, elem)
     value = byts / (ms_step * 1e-3) / 1e9
     # the roofline counts what the path has to read: with a shared prefix its K/V once
@@ -435,7 +525,12 @@ def run(args):
                                 "paged_attention_decode (attention kernel + merge kernel)"),
                      "algorithmic_bytes": unique,
                      "avg_us": round(dec_avg * 1e3, 2),
-                     "runs_us": [round(x * 1e3, 2) for x in dec_runs]},
+                     "runs_us": [round(x * 1e3, 2) for x in dec_runs],
+                     "per_call_us_p10_p50_p90": dec_pct,
+                     "read_ceiling_GBs": None if ceiling is None else round(ceiling, 1),
+                     "frac_of_read_ceiling": None if ceiling is None
+                                             else round(achieved / ceiling, 4)},
+        **parts,
     }
     if pre is not None:
         # prefill alone, same inputs and pool rotation
@@ -474,6 +569,8 @@ def main():
     ap.add_argument("--spec-path", default="multi_query", choices=["multi_query", "prefill"],
                     help="spec: attention through the multi-query decode or chunked prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-read-ceiling", action="store_true",
+                    help="skip the streaming-read ceiling measurement (4 GiB buffer)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",

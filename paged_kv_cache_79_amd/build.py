@@ -18,6 +18,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
+# the benchmark's streaming-read ceiling kernel, kept out of libpagedkv's interface
+BENCH_LIB = os.path.join(PKG, "libpkvbench.so")
+BENCH_SOURCES = ["pkv_read_ceiling.hip"]
 ARCH = "gfx950"
 
 SOURCES = ["pkv_api.hip", "pkv_write_copy.hip", "pkv_decode.hip", "pkv_prefill.hip",
@@ -49,19 +52,27 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build_library(verbose: bool = False) -> str:
-    """Compile every HIP source and link libpagedkv.so; returns the library path."""
-    os.makedirs(OBJDIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build_library(verbose: bool = False) -> str:
+    """Compile every HIP source, link libpagedkv.so (and the benchmark's
+    libpkvbench.so); returns the libpagedkv path."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    srcs = SOURCES + BENCH_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], BENCH_LIB)
     if verbose:
         print(f"built {LIB}")
+        print(f"built {BENCH_LIB}")
     return LIB
 
 
