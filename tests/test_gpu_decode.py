@@ -193,3 +193,54 @@ def test_full_mixed_decode_part():
     seqs = sorted(rng.choice(b.num_seqs, 24, replace=False).tolist())
     want = oracle_decode(b, k, v, seqs=seqs)
     assert rownorm_err(got, want) <= TOL["bf16"]
+
+
+def sample_seqs(S, n, seed):
+    """Sequences checked against the oracle: both ends, the 256-sequence boundaries the
+    split's counting passes step over, and a seeded random draw."""
+    fixed = {0, 1, S - 1, S - 2} | {c + d for c in range(256, S, 256) for d in (-1, 0)}
+    rng = np.random.Generator(np.random.PCG64(seed))
+    draw = rng.choice(S, min(n, S), replace=False).tolist()
+    return sorted({s for s in fixed | set(draw) if 0 <= s < S})
+
+
+def test_many_sequences():
+    """1500 short sequences: the balanced split counts tiles in passes of 256 sequences
+    and locates units past the first 256 by re-reading the lengths. Sampled rows
+    against the oracle; every row of the balanced path against the partitioned one."""
+    rng = np.random.Generator(np.random.PCG64(41))
+    ctx = rng.integers(1, 300, size=1500, endpoint=True)
+    b = batch("bf16", 128, 16, 8, 2, ctx, seed=41)
+    got = check_sampled(b, sample_seqs(b.num_seqs, 24, 42))
+    r = DecodeRun(b)
+    r.write()
+    part = O.widen(r.decode(256), "bf16")
+    assert rownorm_err(got, part) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("hkv,hq,d", [(4, 16, 64), (2, 16, 128)])
+def test_most_sequences_the_grid_allows(hkv, hq, d):
+    """num_seqs * num_kv_heads at the 65535 limit of the partitioned grid, contexts of
+    1..48 tokens; the balanced path on the same batch, every row compared."""
+    S = 65535 // hkv
+    rng = np.random.Generator(np.random.PCG64(43 + hkv))
+    ctx = rng.integers(1, 48, size=S, endpoint=True)
+    b = batch("bf16", d, 16, hq, hkv, ctx, seed=43 + hkv)
+    bal = check_sampled(b, sample_seqs(S, 16, 44))
+    r = DecodeRun(b)
+    r.write()
+    part = O.widen(r.decode(64), "bf16")
+    assert rownorm_err(bal, part) <= TOL["bf16"]
+
+
+def check_sampled(b, seqs, partition_tokens=0):
+    print(f"decode {b.name} S={b.num_seqs} Hq={b.num_q_heads} Hkv={b.num_kv_heads} "
+          f"D={b.head_dim} max_ctx={b.max_context_len} part={partition_tokens} "
+          f"sampled={len(seqs)}", flush=True)
+    r = DecodeRun(b)
+    r.write()
+    got = O.widen(r.decode(partition_tokens), b.dtype)
+    k, v = oracle_after_write(b)
+    err = rownorm_err(got, oracle_decode(b, k, v, seqs=seqs))
+    assert err <= TOL[b.dtype], f"row-normalised error {err:.3e}"
+    return got

@@ -164,3 +164,17 @@ def test_prefix_cow_full_size():
                        np.array([0], np.int32), np.array([S], np.int32),
                        np.array([shared_tokens + b.block_size], np.int32))
     assert rownorm_err(widen_out(whole, b.dtype), want) <= TOL[b.dtype]
+
+
+def test_many_sequences():
+    """470 sequences in three groups and a run of unshared ones: the own-token decode
+    counts and locates past the first 256 sequences. Sampled rows against the oracle,
+    every row against plain decode."""
+    pg = W.prefix_groups(306, [(150, 3), (200, 0), (120, 5)], suffix_range=(1, 150))
+    S = pg.batch.num_seqs
+    seqs = [0, 149, 150, 255, 256, 349, 350, 469]
+    rng = np.random.Generator(np.random.PCG64(307))
+    seqs = sorted(set(seqs) | set(rng.choice(S, 12, replace=False).tolist()))
+    r, got = check_groups(pg, seqs=seqs)
+    b = pg.batch
+    assert rownorm_err(widen_out(got, b.dtype), widen_out(r.decode(0), b.dtype)) <= TOL[b.dtype]

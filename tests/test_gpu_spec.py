@@ -105,3 +105,17 @@ def test_full_sampled(path):
     sb = W.spec_decode()
     rng = np.random.Generator(np.random.PCG64(4))
     run(sb, sorted(rng.choice(sb.prefill.num_chunks, 10, replace=False).tolist()), path)
+
+
+def test_many_sequences():
+    """700 sequences of up to 300 tokens: the balanced split counts and locates past the
+    first 256 sequences. Sampled rows against the oracle; every row against the prefill
+    path."""
+    sb = W.spec_decode(seed=33, num_seqs=700, draft=3, ctx_range=(4, 300), num_q_heads=8,
+                       num_kv_heads=2)
+    seqs = [0, 1, 255, 256, 257, 511, 512, 699]
+    rng = np.random.Generator(np.random.PCG64(34))
+    seqs = sorted(set(seqs) | set(rng.choice(700, 12, replace=False).tolist()))
+    raw, k, v = run(sb, seqs)
+    other = attend("prefill", sb.prefill, 4, k, v)
+    assert rownorm_err(O.widen(raw, "bf16"), O.widen(other, "bf16")) <= TOL["bf16"]
