@@ -398,21 +398,28 @@ __global__ __launch_bounds__(64, (BF16 ? 2 : 1)) void decode_balanced_kernel(Dec
     }
 }
 
+// Output rows (one wave each) per workgroup of the balanced merge.
+constexpr int kMergeRows = 4;
+
 // Merge the pieces of each (sequence, kv head) that straddles waves, one wave per
 // query head; write zero rows for empty contexts.  The first covering wave holds
 // its piece in its last slot, every later covering wave in its first slot.  In the
 // shared-prefix mode the prefix pass's states of the row are merged in as well,
 // together with the row's own-token state when one wave finished its (sequence, kv
 // head) (a row with no token after its prefix is the prefix states alone).
-// With nq queries per sequence (multi-query decode) the output row blockIdx.x is
+// With nq queries per sequence (multi-query decode) the output row is
 // (s * nq + i) * Hq + hq, and a (sequence, kv head) has nq * G partial rows.
 template <bool BF16, int D, int G, bool PREFIX = false>
-__global__ __launch_bounds__(64) void decode_balanced_merge_kernel(DecodeArgs a, int nq) {
+__global__ __launch_bounds__(64 * kMergeRows) void decode_balanced_merge_kernel(DecodeArgs a,
+                                                                               int nq) {
     constexpr int PER = D / 64;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
     const int Hkv = a.g.num_kv_heads;
-    const int sq = blockIdx.x / a.num_q_heads;
-    const int hq = blockIdx.x - sq * a.num_q_heads;
+    // kMergeRows rows per workgroup: the grid then starts 4x fewer workgroups
+    const int row = blockIdx.x * kMergeRows + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (row >= a.num_seqs * nq * a.num_q_heads) return;
+    const int sq = row / a.num_q_heads;
+    const int hq = row - sq * a.num_q_heads;
     const int s = sq / nq;
     const int h = hq / G;
     const int rows = nq * G, r = (sq - s * nq) * G + (hq - h * G);
@@ -424,7 +431,7 @@ __global__ __launch_bounds__(64) void decode_balanced_merge_kernel(DecodeArgs a,
     const int ns =
         PREFIX ? min((start + a.pre_split_tokens - 1) / a.pre_split_tokens, a.pre_splits) : 0;
     const int64_t pre_row0 = ((int64_t)s * a.num_q_heads + hq) * (a.pre_splits + 1);
-    const int64_t o = (int64_t)blockIdx.x * D + lane * PER;
+    const int64_t o = (int64_t)row * D + lane * PER;
     int64_t w0 = 0;
     int npieces = 0, own = 0;
     if (nt > 0) {
@@ -593,6 +600,9 @@ __global__ __launch_bounds__(64) void decode_partition_merge_kernel(DecodeArgs a
 // --------------------------------------------------------------------------------------
 // host side
 // --------------------------------------------------------------------------------------
+// Workgroups of the balanced merge for `rows` output rows.
+static dim3 merge_grid(int64_t rows) { return dim3((unsigned)((rows + kMergeRows - 1) / kMergeRows)); }
+
 template <bool BF16, int D, int G, bool CONTIG = false, bool PREFIX = false>
 static int balanced_waves_t() {
     // resident waves of the balanced kernel on the current device, cached per device
@@ -626,8 +636,8 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
     } else {
         hipLaunchKernelGGL((decode_balanced_kernel<BF16, D, G>), dim3(a.num_waves), dim3(64), 0, st,
                            a);
-        hipLaunchKernelGGL((decode_balanced_merge_kernel<BF16, D, G>), dim3(S * a.num_q_heads),
-                           dim3(64), 0, st, a, 1);
+        hipLaunchKernelGGL((decode_balanced_merge_kernel<BF16, D, G>),
+                           merge_grid(S * a.num_q_heads), dim3(64 * kMergeRows), 0, st, a, 1);
     }
     return hipGetLastError();
 }
@@ -650,8 +660,8 @@ template <bool BF16, int D, int G>
 static hipError_t launch_contig_t(const DecodeArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((decode_balanced_kernel<true, D, G, true>), dim3(a.num_waves), dim3(64), 0,
                        st, a);
-    hipLaunchKernelGGL((decode_balanced_merge_kernel<true, D, G>), dim3(a.num_seqs * a.num_q_heads),
-                       dim3(64), 0, st, a, 1);
+    hipLaunchKernelGGL((decode_balanced_merge_kernel<true, D, G>),
+                       merge_grid(a.num_seqs * a.num_q_heads), dim3(64 * kMergeRows), 0, st, a, 1);
     return hipGetLastError();
 }
 template <bool BF16, int D, int G>
@@ -665,7 +675,7 @@ static hipError_t launch_prefix_decode_t(const DecodeArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((decode_balanced_kernel<true, D, G, false, true>), dim3(a.num_waves),
                        dim3(64), 0, st, a);
     hipLaunchKernelGGL((decode_balanced_merge_kernel<true, D, G, true>),
-                       dim3(a.num_seqs * a.num_q_heads), dim3(64), 0, st, a, 1);
+                       merge_grid(a.num_seqs * a.num_q_heads), dim3(64 * kMergeRows), 0, st, a, 1);
     return hipGetLastError();
 }
 template <bool BF16, int D, int G>
@@ -677,7 +687,8 @@ static int prefix_waves_t() {
 template <bool BF16, int D, int G>
 static hipError_t launch_merge_mq_t(const DecodeArgs& a, int nq, hipStream_t st) {
     hipLaunchKernelGGL((decode_balanced_merge_kernel<true, D, G>),
-                       dim3(a.num_seqs * nq * a.num_q_heads), dim3(64), 0, st, a, nq);
+                       merge_grid(a.num_seqs * nq * a.num_q_heads), dim3(64 * kMergeRows), 0, st, a,
+                       nq);
     return hipGetLastError();
 }
 

@@ -60,7 +60,7 @@ __device__ __forceinline__ int unit_tiles(const DecodeArgs& a, int s) {
 template <bool PREFIX = false>
 __device__ __forceinline__ void count_tiles(const DecodeArgs& a, int upto, int64_t& total,
                                             int64_t& before, int (&first)[4]) {
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;   // lane of the wave (the merge runs several per workgroup)
     total = 0;
     before = 0;
     for (int c0 = 0; c0 < a.num_seqs; c0 += 256) {
@@ -123,7 +123,7 @@ __device__ __forceinline__ int64_t unit_owner(const Split& p, int64_t u) {
 template <bool PREFIX = false>
 __device__ __forceinline__ void locate_unit(const DecodeArgs& a, int64_t b, int Hkv,
                                             const int (&first)[4], int& s, int64_t& before) {
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;   // lane of the wave (the merge runs several per workgroup)
     s = 0;
     before = 0;
     int64_t carry = 0;
