@@ -1,0 +1,131 @@
+"""Decode and prefill steps captured in a HIP graph (torch.cuda.CUDAGraph) and replayed.
+The library only launches kernels on the caller's stream -- no allocation, memset or
+host synchronisation inside a call when the caller passes the workspace -- so a
+captured step replays with new inputs copied into its static buffers.  Every replay
+is compared bit for bit with the same calls run eagerly on copies of the same pools,
+with eager work and synchronisations between the replays; one replay is also checked
+against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_79_amd as pkv
+import workloads as W
+from oracle import paged as O
+from tests.gpu_helpers import TOL, dev, host, rownorm_err
+
+pytestmark = pytest.mark.gpu
+
+
+def bf16_normal(rng, shape):
+    x = rng.standard_normal(shape, dtype=np.float32)
+    return dev((x.view(np.uint32) + 0x8000 >> 16).astype(np.uint16))
+
+
+def capture(step):
+    """Warm up once eagerly (library load, occupancy queries), then capture step()."""
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    return g
+
+
+@pytest.mark.parametrize("partition_tokens", [0, 256])
+def test_decode_step_replays(partition_tokens):
+    rng = np.random.Generator(np.random.PCG64(71))
+    ctx = rng.integers(1, 1500, size=12, endpoint=True)
+    b = W.build_decode_batch(name="graph_decode", dtype="bf16", context_lens=ctx, num_q_heads=8,
+                             num_kv_heads=2, head_dim=128, block_size=16, seed=71)
+    print(f"graph decode S={b.num_seqs} part={partition_tokens}", flush=True)
+    k, v = dev(b.k_pool), dev(b.v_pool)
+    q, kn, vn, slots = dev(b.q), dev(b.k_new), dev(b.v_new), dev(b.slot_mapping)
+    tables, ctxd = dev(b.block_tables), dev(b.context_lens)
+    out = torch.empty_like(q)
+    need = pkv.paged_attention_decode_workspace_bytes(b.num_seqs, b.num_q_heads, b.num_kv_heads,
+                                                      b.head_dim, b.max_context_len,
+                                                      partition_tokens)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+
+    def step(kp, vp, o):
+        pkv.paged_kv_write(kp, vp, kn, vn, slots)
+        pkv.paged_attention_decode(o, q, kp, vp, tables, ctxd, b.max_context_len, b.scale,
+                                   partition_tokens=partition_tokens, workspace=ws)
+
+    k0, v0 = k.clone(), v.clone()
+    step(k0, v0, torch.empty_like(q))
+    g = capture(lambda: step(k, v, out))
+    for r in range(4):
+        # new inputs for this replay, and the eager reference on copies of the pools
+        q.copy_(bf16_normal(rng, tuple(q.shape)))
+        kn.copy_(bf16_normal(rng, tuple(kn.shape)))
+        vn.copy_(bf16_normal(rng, tuple(vn.shape)))
+        ke, ve, oe = k.clone(), v.clone(), torch.empty_like(q)
+        step(ke, ve, oe)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), oe.view(torch.int16)), f"replay {r}: output"
+        assert torch.equal(k.view(torch.int16), ke.view(torch.int16)), f"replay {r}: k pool"
+        assert torch.equal(v.view(torch.int16), ve.view(torch.int16)), f"replay {r}: v pool"
+        if r == 1:
+            kh, vh = host(k), host(v)
+            want = O.decode(host(q), kh, vh, b.block_tables, b.context_lens, b.scale, "bf16",
+                            b.num_kv_heads)
+            assert rownorm_err(O.widen(host(out), "bf16"), want) <= TOL["bf16"]
+
+
+def test_multi_query_and_prefill_replays():
+    """A speculative-verification step (write of k + 1 tokens, multi-query decode) and a
+    chunked-prefill call in one graph."""
+    rng = np.random.Generator(np.random.PCG64(72))
+    sb = W.spec_decode(seed=72, num_seqs=6, draft=3, ctx_range=(4, 900), num_q_heads=8,
+                       num_kv_heads=2)
+    pre = sb.prefill
+    nq = sb.draft + 1
+    pf, kp_pf, vp_pf, _ = W.prefill_only(seed=73, chunk_lens=[70, 129], contexts=[300, 129],
+                                         num_q_heads=8, num_kv_heads=2, head_dim=128,
+                                         block_size=16)
+    print(f"graph spec S={pre.num_chunks} k+1={nq}; prefill chunks={pf.num_chunks}", flush=True)
+    k, v = dev(sb.k_pool), dev(sb.v_pool)
+    q, kn, vn, slots = dev(pre.q), dev(sb.k_new), dev(sb.v_new), dev(sb.slot_mapping)
+    tables, ctxd = dev(pre.block_tables), dev(pre.context_lens)
+    out = torch.empty_like(q)
+    need = pkv.paged_attention_decode_multi_query_workspace_bytes(
+        pre.num_chunks, nq, pre.num_q_heads, pre.num_kv_heads, pre.head_dim)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    kpf, vpf = dev(kp_pf), dev(vp_pf)
+    qpf, cupf = dev(pf.q), dev(pf.cu_q_lens)
+    tpf, cpf = dev(pf.block_tables), dev(pf.context_lens)
+    opf = torch.empty_like(qpf)
+
+    def step(kp, vp, o, o2):
+        pkv.paged_kv_write(kp, vp, kn, vn, slots)
+        pkv.paged_attention_decode_multi_query(o, q, kp, vp, tables, ctxd, nq,
+                                               pre.max_context_len, pre.scale, workspace=ws)
+        pkv.paged_attention_prefill_chunk(o2, qpf, cupf, kpf, vpf, tpf, cpf, pf.max_q_len,
+                                          pf.max_context_len, pf.scale)
+
+    k0, v0 = k.clone(), v.clone()
+    step(k0, v0, torch.empty_like(q), torch.empty_like(qpf))
+    g = capture(lambda: step(k, v, out, opf))
+    for r in range(4):
+        q.copy_(bf16_normal(rng, tuple(q.shape)))
+        kn.copy_(bf16_normal(rng, tuple(kn.shape)))
+        vn.copy_(bf16_normal(rng, tuple(vn.shape)))
+        qpf.copy_(bf16_normal(rng, tuple(qpf.shape)))
+        ke, ve = k.clone(), v.clone()
+        oe, oe2 = torch.empty_like(q), torch.empty_like(qpf)
+        step(ke, ve, oe, oe2)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), oe.view(torch.int16)), f"replay {r}: decode"
+        assert torch.equal(opf.view(torch.int16), oe2.view(torch.int16)), f"replay {r}: prefill"
+        assert torch.equal(k.view(torch.int16), ke.view(torch.int16)), f"replay {r}: k pool"
+        if r == 2:
+            got = O.widen(host(opf), "bf16")
+            want = O.prefill_chunk(host(qpf), pf.cu_q_lens, kp_pf, vp_pf, pf.block_tables,
+                                   pf.context_lens, pf.scale, "bf16", pf.num_kv_heads)
+            assert rownorm_err(got, want) <= TOL["bf16"]
