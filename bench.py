@@ -573,7 +573,7 @@ def main():
                     help="skip the streaming-read ceiling measurement (4 GiB buffer)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+        print("bench.py measures one GPU: the library has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
     runners = {"spec": run_spec, "swap": run_swap}
