@@ -2,7 +2,8 @@
 batch is built on a compact host pool, then its blocks are placed at ids spread over
 a 5.4 GB device pool (most of them past 4 GiB); the results must equal the oracle
 on the compact pool (same contents, relabelled ids) -- decode (balanced and
-partitioned), multi-query decode, chunked prefill, the cache write and block copy."""
+partitioned), shared-prefix decode, multi-query decode, chunked prefill, the cache
+write and block copy."""
 import numpy as np
 import pytest
 import torch
@@ -114,3 +115,28 @@ def test_multi_query_and_prefill():
         torch.cuda.synchronize()
         err = rownorm_err(O.widen(host(out), "bf16"), want)
         assert err <= TOL["bf16"], f"{path}: row-normalised error {err:.3e}"
+
+
+def test_shared_prefix():
+    rng = np.random.Generator(np.random.PCG64(1203))
+    pg = W.prefix_groups(1203, [(5, 9), (2, 0), (4, 3)], num_q_heads=32, num_kv_heads=8)
+    b = pg.batch
+    ids = big_ids(rng, b.k_pool.shape[0])
+    print(f"large pool shared prefix: max id {ids.max()}", flush=True)
+    k, v = place(b.k_pool, ids), place(b.v_pool, ids)
+    tables = dev(relabel_tables(b.block_tables, ids))
+    pkv.paged_kv_write(k, v, dev(b.k_new), dev(b.v_new),
+                       dev(relabel_slots(b.slot_mapping, ids, b.block_size)))
+    q = dev(b.q)
+    out = torch.empty_like(q)
+    gnum, gpre = pg.group_num_seqs, pg.group_prefix_lens
+    pkv.paged_attention_decode_shared_prefix(
+        out, q, k, v, tables, dev(b.context_lens), b.max_context_len, b.scale,
+        dev(pg.seq_prefix_lens), dev(pg.group_first_seq), dev(gnum), dev(gpre),
+        int(gnum.max()), int(gpre.max()))
+    torch.cuda.synchronize()
+    kw = O.kv_write(b.k_pool, b.k_new, b.slot_mapping)
+    vw = O.kv_write(b.v_pool, b.v_new, b.slot_mapping)
+    want = O.decode(b.q, kw, vw, b.block_tables, b.context_lens, b.scale, "bf16", b.num_kv_heads)
+    err = rownorm_err(O.widen(host(out), "bf16"), want)
+    assert err <= TOL["bf16"], f"row-normalised error {err:.3e}"
