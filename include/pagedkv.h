@@ -37,6 +37,9 @@
  *    and slots are skipped by the kernels (never dereferenced), which keeps
  *    a bad table from faulting the GPU but yields unspecified output.
  *  - No entry point blocks or aborts; errors are status codes.
+ *  - Apart from swap_blocks (host memory) every entry point only launches
+ *    kernels on the given stream -- no memset, copy or host wait -- so a
+ *    sequence of calls can be captured into a HIP graph and replayed.
  */
 #ifndef PAGEDKV_H
 #define PAGEDKV_H
