@@ -107,7 +107,10 @@ __device__ __forceinline__ const u32x4* pool_row(const char* base, int id, uint3
     return reinterpret_cast<const u32x4*>(base + ((uint64_t)ub * stride + off));
 }
 
-// Global loads of the 64-key tile starting at t0 (K and V are read once: nontemporal).
+// Global loads of the 64-key tile starting at t0.  Ordinary (cached) loads: every
+// query tile of a (chunk, kv head) reads the same K/V tiles at about the same time,
+// and L2 serves the repeats (nontemporal loads, which suit decode's read-once
+// stream, cost the prefill 10-14% here).
 template <int D>
 __device__ __forceinline__ void load_tile(KvStage<D>& st, const TileIds<D>& ids,
                                           const TileOffs<D>& offs, const PoolGeom& g,
@@ -117,15 +120,14 @@ __device__ __forceinline__ void load_tile(KvStage<D>& st, const TileIds<D>& ids,
     const uint32_t stride = (uint32_t)g.block_stride_bytes, nb = (uint32_t)g.num_blocks;
 #pragma unroll
     for (int i = 0; i < P::KLOADS; ++i)
-        st.k[i] = __builtin_nontemporal_load(pool_row(kb, ids.k[i], nb, stride, offs.k[i]));
+        st.k[i] = *pool_row(kb, ids.k[i], nb, stride, offs.k[i]);
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
         const uint32_t tok = (uint32_t)min(t0 + 2 * (tid >> 3) + r, ctx - 1);
         const uint32_t off = (tok & (uint32_t)(g.block_size - 1)) * P::RB + (uint32_t)(tid & 7) * 16;
 #pragma unroll
         for (int j = 0; j < P::VLOADS; ++j)
-            st.v[2 * j + r] =
-                __builtin_nontemporal_load(pool_row(vb, ids.v[r], nb, stride, off + 128 * j));
+            st.v[2 * j + r] = *pool_row(vb, ids.v[r], nb, stride, off + 128 * j);
     }
 }
 
