@@ -254,6 +254,10 @@ def run_spec(args):
     stream = torch.cuda.current_stream()
 
     mq = args.spec_path == "multi_query"
+    pws = None
+    if not mq:
+        pws = torch.empty(max(1, pkv.paged_attention_prefill_chunk_workspace_bytes(
+            pre.num_q_heads, pre.num_kv_heads, pre.head_dim)), dtype=torch.uint8, device="cuda")
     if mq:
         ws = pkv.decode_workspace(pkv.paged_attention_decode_multi_query_workspace_bytes(
             pre.num_chunks, nq, pre.num_q_heads, pre.num_kv_heads, pre.head_dim), q.device)
@@ -265,7 +269,7 @@ def run_spec(args):
                                                    pre.max_context_len, pre.scale, workspace=ws)
         else:
             pkv.paged_attention_prefill_chunk(out, q, cu, kp, vp, tab, ctx, nq,
-                                              pre.max_context_len, pre.scale)
+                                              pre.max_context_len, pre.scale, workspace=pws)
 
     def step(i):
         kp, vp = pools[i % copies]
@@ -413,6 +417,11 @@ def run(args):
         pq, pcu = _dev(pre.q), _dev(pre.cu_q_lens)
         ptab, pctx = _dev(pre.block_tables), _dev(pre.context_lens)
         pout = torch.empty_like(pq)
+        # the prefill's workspace lets it split uneven chunks over keys (--no-prefill-split: none)
+        pws = None
+        if not args.no_prefill_split:
+            pws = torch.empty(max(1, pkv.paged_attention_prefill_chunk_workspace_bytes(
+                pre.num_q_heads, pre.num_kv_heads, pre.head_dim)), dtype=torch.uint8, device="cuda")
 
     stream = torch.cuda.current_stream()
 
@@ -441,7 +450,8 @@ def run(args):
         pkv.paged_kv_write(kp, vp, k_new, v_new, slots)
         if pre is not None:
             pkv.paged_attention_prefill_chunk(pout, pq, pcu, kp, vp, ptab, pctx, pre.max_q_len,
-                                              pre.max_context_len, pre.scale)
+                                              pre.max_context_len, pre.scale, workspace=pws,
+                                              split=pws is not None)
         decode(i)
 
     def timed(fn, n):
@@ -537,10 +547,12 @@ def run(args):
         def prefill(i):
             kp, vp = pools[i % copies]
             pkv.paged_attention_prefill_chunk(pout, pq, pcu, kp, vp, ptab, pctx, pre.max_q_len,
-                                              pre.max_context_len, pre.scale)
+                                              pre.max_context_len, pre.scale, workspace=pws,
+                                              split=pws is not None)
         p_ms = timed(prefill, max(5, args.steps // 4))
         fl = prefill_flops(pre)
         rec["prefill"] = {"avg_us": round(p_ms * 1e3, 2), "flops": fl,
+                          "key_split_allowed": pws is not None,
                           "tflops": round(fl / (p_ms * 1e-3) / 1e12, 2),
                           "mfma_frac": round(fl / (p_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
     log(f"GPU: {ms_step * 1e3:.1f} us/step, decode {dec_avg * 1e3:.1f} us")
@@ -568,6 +580,8 @@ def main():
                     help="prefix_cow: decode through the shared-prefix path (prefix read once)")
     ap.add_argument("--spec-path", default="multi_query", choices=["multi_query", "prefill"],
                     help="spec: attention through the multi-query decode or chunked prefill")
+    ap.add_argument("--no-prefill-split", action="store_true",
+                    help="mixed: chunked prefill without a workspace (one workgroup per query tile)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-read-ceiling", action="store_true",
                     help="skip the streaming-read ceiling measurement (4 GiB buffer)")

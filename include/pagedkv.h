@@ -282,8 +282,16 @@ pkv_status pkv_validate(int32_t num_blocks, int32_t block_size, const int32_t* b
  *   context_lens  int32 [num_chunks], including the chunk; chunk c's queries are the
  *                 last n_q positions, query i at p = ctx - n_q + i, seeing keys t <= p.
  *                 n_q must not exceed ctx.
+ *   workspace     NULL, or device scratch of at least
+ *                 paged_attention_prefill_chunk_workspace_bytes() (no initialisation
+ *                 needed; garbage afterwards; calls sharing it must not overlap).
+ *                 With it, a batch whose query tiles fit in one round of resident
+ *                 workgroups but whose chunks differ in length is split over keys into
+ *                 equal ranges and merged by log-sum-exp (the result is the same up to
+ *                 rounding); without it every query tile is one workgroup.
  * The chunk's own K/V must already be in the cache (paged_kv_write earlier on the
  * stream).  bf16 only (PKV_ERR_UNSUPPORTED for fp32); runs on the matrix cores.
+ * PKV_ERR_WORKSPACE if a workspace is given and is too small.
  */
 pkv_status paged_attention_prefill_chunk(pkv_dtype dtype, void* out, const void* q,
                                          const int32_t* cu_q_lens, int32_t num_chunks,
@@ -293,7 +301,16 @@ pkv_status paged_attention_prefill_chunk(pkv_dtype dtype, void* out, const void*
                                          int32_t head_dim, const int32_t* block_tables,
                                          int32_t max_blocks_per_seq, const int32_t* context_lens,
                                          int32_t max_context_len, int32_t num_q_heads, float scale,
+                                         void* workspace, size_t workspace_bytes,
                                          hipStream_t stream);
+
+/*
+ * paged_attention_prefill_chunk_workspace_bytes: bytes of the optional workspace of
+ * paged_attention_prefill_chunk for this head layout on the current device (two
+ * partial states of 128 rows per resident workgroup); 0 for an unsupported layout.
+ */
+size_t paged_attention_prefill_chunk_workspace_bytes(int32_t num_q_heads, int32_t num_kv_heads,
+                                                     int32_t head_dim);
 
 /*
  * swap_blocks -- preemption by swapping ("2.1 PagedAttention", section 7: a

@@ -28,6 +28,7 @@ EXPORTS = (
     "paged_attention_decode_shared_prefix",
     "paged_attention_decode_multi_query_workspace_bytes",
     "paged_attention_decode_multi_query",
+    "paged_attention_prefill_chunk_workspace_bytes",
     "paged_attention_prefill_chunk",
     "swap_blocks",
     "pkv_pool_create",
@@ -95,8 +96,10 @@ def load_library(path: Optional[str] = None):
         ctypes.c_int, VP, VP, VP, VP, I32, I32, I32, I32, VP, I32, VP, I32, I32, I32, I32, F, VP,
         SZ, VP]
     lib.paged_attention_decode_multi_query.restype = ctypes.c_int
+    lib.paged_attention_prefill_chunk_workspace_bytes.argtypes = [I32, I32, I32]
+    lib.paged_attention_prefill_chunk_workspace_bytes.restype = SZ
     lib.paged_attention_prefill_chunk.argtypes = [ctypes.c_int, VP, VP, VP, I32, I32, VP, VP, I32, I32,
-                                                  I32, I32, VP, I32, VP, I32, I32, F, VP]
+                                                  I32, I32, VP, I32, VP, I32, I32, F, VP, SZ, VP]
     lib.paged_attention_prefill_chunk.restype = ctypes.c_int
     U64 = ctypes.c_uint64
     lib.swap_blocks.argtypes = [ctypes.c_int, VP, VP, I32, VP, VP, I32, I32, I32, I32, VP, I32, VP]
@@ -384,9 +387,20 @@ def paged_attention_decode_multi_query(out, q, k_pool, v_pool, block_tables, con
         int(max_context_len), hq, float(scale), _ptr(workspace), wbytes, _stream(stream)))
 
 
+def paged_attention_prefill_chunk_workspace_bytes(num_q_heads: int, num_kv_heads: int,
+                                                  head_dim: int) -> int:
+    return int(load_library().paged_attention_prefill_chunk_workspace_bytes(
+        num_q_heads, num_kv_heads, head_dim))
+
+
 def paged_attention_prefill_chunk(out, q, cu_q_lens, k_pool, v_pool, block_tables, context_lens,
-                                  max_q_len: int, max_context_len: int, scale: float, stream=None) -> None:
-    """Causal attention of prefill chunks (the last n_q positions of each context)."""
+                                  max_q_len: int, max_context_len: int, scale: float,
+                                  workspace=None, split: bool = True, stream=None) -> None:
+    """Causal attention of prefill chunks (the last n_q positions of each context).
+
+    With ``split`` (the default) the call gets a workspace (``workspace``, or a fresh
+    one), so the library may balance uneven chunks by splitting their keys; with
+    ``split=False`` it passes none and every query tile is one workgroup."""
     import torch
     for n, t in (("out", out), ("q", q), ("k_pool", k_pool), ("v_pool", v_pool)):
         _dev(t, n)
@@ -400,10 +414,20 @@ def paged_attention_prefill_chunk(out, q, cu_q_lens, k_pool, v_pool, block_table
     if cu_q_lens.shape != (nc + 1,) or block_tables.dim() != 2 or block_tables.shape[0] != nc:
         raise ValueError("cu_q_lens must be [chunks + 1], block_tables [chunks][max_blocks]")
     lib = load_library()
+    if not split:
+        workspace = None
+    elif workspace is None:
+        need = paged_attention_prefill_chunk_workspace_bytes(int(q.shape[1]), hkv, d)
+        if need > 0:
+            workspace = decode_workspace(need, q.device)
+    if workspace is not None:
+        _dev(workspace, "workspace")
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("paged_attention_prefill_chunk", lib.paged_attention_prefill_chunk(
         _dtype_code(q), _ptr(out), _ptr(q), _ptr(cu_q_lens), nc, int(max_q_len), _ptr(k_pool),
         _ptr(v_pool), nb, hkv, bs, d, _ptr(block_tables), int(block_tables.shape[1]),
-        _ptr(context_lens), int(max_context_len), int(q.shape[1]), float(scale), _stream(stream)))
+        _ptr(context_lens), int(max_context_len), int(q.shape[1]), float(scale), _ptr(workspace),
+        wbytes, _stream(stream)))
 
 
 # ----------------------------------------------------------------------------

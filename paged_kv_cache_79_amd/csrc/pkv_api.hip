@@ -586,7 +586,8 @@ pkv_status paged_attention_prefill_chunk(pkv_dtype dtype, void* out, const void*
                                          int32_t block_size, int32_t head_dim,
                                          const int32_t* block_tables, int32_t max_blocks_per_seq,
                                          const int32_t* context_lens, int32_t max_context_len,
-                                         int32_t num_q_heads, float scale, hipStream_t stream) {
+                                         int32_t num_q_heads, float scale, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream) {
     PoolGeom g;
     const pkv_status st = check_geom(dtype, num_blocks, num_kv_heads, block_size, head_dim, &g);
     if (st != PKV_OK) return st;
@@ -618,7 +619,37 @@ pkv_status paged_attention_prefill_chunk(pkv_dtype dtype, void* out, const void*
     a.max_blocks_per_seq = max_blocks_per_seq;
     a.max_context_len = max_context_len;
     a.scale_log2 = scale * 1.4426950408889634f;
+    a.part_o = nullptr;
+    a.part_ml = nullptr;
+    a.item_desc = nullptr;
+    a.num_wgs = 0;
+    if (workspace != nullptr) {
+        const size_t need = paged_attention_prefill_chunk_workspace_bytes(num_q_heads, num_kv_heads,
+                                                                          head_dim);
+        if (need == 0) return PKV_ERR_LAUNCH;
+        if (workspace_bytes < need) return PKV_ERR_WORKSPACE;
+        a.num_wgs = prefill_wgs(head_dim, group);
+        const size_t slots = (size_t)2 * a.num_wgs * 128;      // partial rows
+        char* ws = static_cast<char*>(workspace);
+        a.part_ml = reinterpret_cast<float*>(ws);
+        a.item_desc = reinterpret_cast<int32_t*>(ws + slots * 2 * sizeof(float));
+        a.part_o = reinterpret_cast<uint16_t*>(ws + slots * 2 * sizeof(float) +
+                                               (size_t)a.num_wgs * 2 * sizeof(int32_t));
+    }
     return launch_status(launch_prefill(a, head_dim, group, num_chunks, max_q_len, stream));
+}
+
+size_t paged_attention_prefill_chunk_workspace_bytes(int32_t num_q_heads, int32_t num_kv_heads,
+                                                     int32_t head_dim) {
+    if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads ||
+        num_q_heads / num_kv_heads > 8 || (head_dim != 64 && head_dim != 128))
+        return 0;
+    const int wgs = prefill_wgs(head_dim, num_q_heads / num_kv_heads);
+    if (wgs <= 0) return 0;
+    // two partial slots per workgroup, each 128 rows of (max, sum) in fp32 and head_dim
+    // bf16 outputs, and a descriptor of two int32 per work item (at most one per workgroup)
+    return (size_t)2 * wgs * 128 * (2 * sizeof(float) + (size_t)head_dim * 2) +
+           (size_t)wgs * 2 * sizeof(int32_t);
 }
 
 }  // extern "C"

@@ -140,6 +140,11 @@ struct PrefillArgs {
     int32_t max_blocks_per_seq;
     int32_t max_context_len;
     float scale_log2;
+    // balanced key split (null part_o: one workgroup per query tile, no split)
+    uint16_t* part_o;             // [2 * num_wgs][128 rows][D] bf16 partial outputs (normalised)
+    float* part_ml;               // [2 * num_wgs][128 rows][2] (max in log2 units, sum)
+    int32_t* item_desc;           // [num_wgs][2]: (first workgroup, pieces; 0 = not cut) per item
+    int32_t num_wgs;              // workgroups of the split: the device's resident count
 };
 
 // Device-side precondition check (pkv_validate): counts [4] in device memory.
@@ -172,6 +177,8 @@ hipError_t launch_prefix(const PrefixArgs& a, int head_dim, int group, int num_g
 // Decode over the tokens after each sequence's shared prefix, merging the prefix pass.
 hipError_t launch_decode_prefix(const DecodeArgs& a, int head_dim, int group, int num_seqs,
                                 hipStream_t st);
+// Resident workgroups of the prefill kernel (the balanced split's grid), 0 if unknown.
+int prefill_wgs(int head_dim, int group);
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int group, int num_chunks,
                           int max_q_len, hipStream_t st);
 // Multi-query decode (bf16): nq queries per sequence, nq * group <= 16, balanced split.

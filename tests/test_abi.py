@@ -228,8 +228,12 @@ def test_prefill_validation(lib):
         a = dict(args, **kw)
         return f(a["dtype"], a["out"], a["q"], a["cu"], a["nc"], a["mq"], a["k"], a["v"], a["nb"],
                  a["hkv"], a["bs"], a["d"], a["bt"], a["mb"], a["ctx"], a["mctx"], a["hq"], a["scale"],
-                 None)
+                 a.get("ws"), a.get("wsb", 0), None)
     assert call(dtype=0) == UNSUP                      # fp32 prefill is not offered
     assert call(hq=9) == SHAPE                         # not a multiple of the kv heads
     assert call(q=None) == NULL
     assert call(nc=0, q=None) == OK
+    # a workspace too small for the split (without a GPU the size query itself fails)
+    assert call(ws=P, wsb=1) in (WS, 6)                 # 6: PKV_ERR_LAUNCH
+    g = lib.paged_attention_prefill_chunk_workspace_bytes
+    assert g(9, 2, 128) == 0 and g(18, 2, 128) == 0 and g(8, 2, 96) == 0 and g(0, 1, 64) == 0

@@ -99,13 +99,15 @@ def test_multi_query_and_prefill_replays():
     qpf, cupf = dev(pf.q), dev(pf.cu_q_lens)
     tpf, cpf = dev(pf.block_tables), dev(pf.context_lens)
     opf = torch.empty_like(qpf)
+    pws = torch.empty(pkv.paged_attention_prefill_chunk_workspace_bytes(
+        pf.num_q_heads, pf.num_kv_heads, pf.head_dim), dtype=torch.uint8, device="cuda")
 
     def step(kp, vp, o, o2):
         pkv.paged_kv_write(kp, vp, kn, vn, slots)
         pkv.paged_attention_decode_multi_query(o, q, kp, vp, tables, ctxd, nq,
                                                pre.max_context_len, pre.scale, workspace=ws)
         pkv.paged_attention_prefill_chunk(o2, qpf, cupf, kpf, vpf, tpf, cpf, pf.max_q_len,
-                                          pf.max_context_len, pf.scale)
+                                          pf.max_context_len, pf.scale, workspace=pws)
 
     k0, v0 = k.clone(), v.clone()
     step(k0, v0, torch.empty_like(q), torch.empty_like(qpf))
