@@ -255,7 +255,7 @@ def run_spec(args):
 
     mq = args.spec_path == "multi_query"
     pws = None
-    if not mq:
+    if not mq and not args.no_prefill_split:
         pws = torch.empty(max(1, pkv.paged_attention_prefill_chunk_workspace_bytes(
             pre.num_q_heads, pre.num_kv_heads, pre.head_dim)), dtype=torch.uint8, device="cuda")
     if mq:
@@ -269,7 +269,8 @@ def run_spec(args):
                                                    pre.max_context_len, pre.scale, workspace=ws)
         else:
             pkv.paged_attention_prefill_chunk(out, q, cu, kp, vp, tab, ctx, nq,
-                                              pre.max_context_len, pre.scale, workspace=pws)
+                                              pre.max_context_len, pre.scale, workspace=pws,
+                                              split=pws is not None)
 
     def step(i):
         kp, vp = pools[i % copies]
@@ -581,7 +582,8 @@ def main():
     ap.add_argument("--spec-path", default="multi_query", choices=["multi_query", "prefill"],
                     help="spec: attention through the multi-query decode or chunked prefill")
     ap.add_argument("--no-prefill-split", action="store_true",
-                    help="mixed: chunked prefill without a workspace (one workgroup per query tile)")
+                    help="mixed, spec --spec-path prefill: chunked prefill without a workspace "
+                         "(one workgroup per query tile)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-read-ceiling", action="store_true",
                     help="skip the streaming-read ceiling measurement (4 GiB buffer)")

@@ -434,24 +434,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, int num_
         e = pf_tiles<QP>(k, qt);
     }
     PfChunk k = pf_chunk<QP>(a, c, num_q_tiles);
-    while (true) {
-        const int nt = pf_tiles<QP>(k, qt);
-        const int k1 = min(nt, k0 + (e - u));
-        // a cut item: the piece starting at its first tile goes to slot 1 of the
-        // workgroup, a piece continuing one from an earlier workgroup to slot 0
-        const int64_t slot = (k0 == 0 && k1 == nt) ? -1 : 2 * (int64_t)w + (k0 == 0 ? 1 : 0);
-        // the workgroup that starts an item tells the merge which workgroups hold its
-        // pieces (none when it finishes the item itself)
-        if (a.part_o != nullptr && k0 == 0 && threadIdx.x == 0) {
-            const int pieces =
-                k1 == nt ? 0 : (int)(unit_owner(Split{tiles, nw, tiles, nw}, (int64_t)u + nt - 1) - w + 1);
-            const int item = (c * Hkv + h) * num_q_tiles + qt;
-            *reinterpret_cast<int2*>(a.item_desc + 2 * item) = make_int2(w, pieces);
-        }
-        attend<D, G>(a, k, c, h, qt, k0, k1, slot, lds);
-        u += k1 - k0;
-        if (u >= e) break;
-        k0 = 0;
+    // the next item with work after (c, h, qt); there is one while tiles remain
+    auto next_item = [&]() {
         if (++qt == k.nqt) {
             qt = 0;
             if (++h == Hkv) {
@@ -462,7 +446,42 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, int num_
                 } while (k.nqt == 0);
             }
         }
+    };
+    // A range that starts inside an item continues a piece of an earlier workgroup: that
+    // piece (slot 0) is attended last, so every workgroup starts at the first key of an
+    // item and the query tiles of one (chunk, kv head) on an XCD walk the same keys at
+    // about the same time, which keeps their shared K/V tiles in its L2.
+    int dc = -1, dh = 0, dqt = 0, dk0 = 0, dk1 = 0;
+    if (k0 > 0) {
+        dc = c;
+        dh = h;
+        dqt = qt;
+        dk0 = k0;
+        dk1 = min(pf_tiles<QP>(k, qt), k0 + (e - u));
+        u += dk1 - k0;
+        k0 = 0;
+        if (u < e) next_item();
     }
+    while (u < e && c < num_chunks) {
+        const int nt = pf_tiles<QP>(k, qt);
+        const int k1 = min(nt, e - u);           // every piece here starts its item
+        // a cut item: the piece starting at its first tile goes to slot 1 of the
+        // workgroup (a piece continuing one from an earlier workgroup goes to slot 0)
+        const int64_t slot = k1 == nt ? -1 : 2 * (int64_t)w + 1;
+        // the workgroup that starts an item tells the merge which workgroups hold its
+        // pieces (none when it finishes the item itself)
+        if (a.part_o != nullptr && threadIdx.x == 0) {
+            const int pieces =
+                k1 == nt ? 0 : (int)(unit_owner(Split{tiles, nw, tiles, nw}, (int64_t)u + nt - 1) - w + 1);
+            const int item = (c * Hkv + h) * num_q_tiles + qt;
+            *reinterpret_cast<int2*>(a.item_desc + 2 * item) = make_int2(w, pieces);
+        }
+        attend<D, G>(a, k, c, h, qt, 0, k1, slot, lds);
+        u += k1;
+        if (u < e) next_item();
+    }
+    if (dc >= 0)
+        attend<D, G>(a, pf_chunk<QP>(a, dc, num_q_tiles), dc, dh, dqt, dk0, dk1, 2 * (int64_t)w, lds);
 }
 
 // One workgroup per work item; nothing to do unless the kernel cut the item.  Thread
