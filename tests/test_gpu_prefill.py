@@ -187,3 +187,14 @@ def test_split_workspace_too_small():
                                           dev(pre.block_tables), dev(pre.context_lens),
                                           pre.max_q_len, pre.max_context_len, pre.scale,
                                           workspace=ws)
+
+
+def test_split_at_one_round_of_items():
+    """500 chunks of 1..16 queries over 16..600 keys, 4 q / 1 kv head: 500 items (one per
+    chunk), just inside one round of 512 workgroups, so the plan scans 8 passes of 64
+    chunks and every workgroup locates its range among them."""
+    rng = np.random.default_rng(17)
+    nq = rng.integers(1, 17, 500)
+    ctx = nq + rng.integers(0, 585, 500)
+    ctx[::97] = 600                                   # a few long ones make the split pay
+    check_split(nq.tolist(), ctx.tolist(), 4, 1, seed=17)
