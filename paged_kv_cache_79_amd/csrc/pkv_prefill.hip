@@ -485,14 +485,18 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, int num_
 }
 
 // One workgroup per work item; nothing to do unless the kernel cut the item.  Thread
-// t combines half t % 2 of row t / 2 over the item's pieces (two per round of loads),
-// weighting each piece's normalised output by l 2^(m - M) with M the running maximum.
+// t combines quarter t % 4 of row t / 4 over the item's pieces (four per round of
+// loads), weighting each piece's normalised output by l 2^(m - M) with M the running
+// maximum.
+constexpr int kMergeThreads = 512;
 template <int D, int G>
-__global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a, int num_q_tiles,
-                                                            int num_items) {
+__global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(PrefillArgs a, int num_q_tiles,
+                                                                      int num_items) {
     constexpr int QP = kRowsPerWg / G;
-    constexpr int HALF = D / 2;                // elements per thread
-    constexpr int NV = HALF / 8;               // 16-byte vectors per thread and piece
+    constexpr int PARTS = kMergeThreads / kRowsPerWg;   // threads per row
+    constexpr int PART = D / PARTS;            // elements per thread
+    constexpr int NV = PART / 8;               // 16-byte vectors per thread and piece
+    constexpr int PB = 4;                      // pieces per round of loads
     const int item = blockIdx.x;
     if (item >= num_items) return;
     const int Hkv = a.g.num_kv_heads;
@@ -505,49 +509,60 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a, int n
     const int w0 = __builtin_amdgcn_readfirstlane(desc.x);
     const int np = __builtin_amdgcn_readfirstlane(desc.y);
     if (np <= 0) return;                       // finished in place
-    const int r = threadIdx.x >> 1, part = threadIdx.x & 1;
+    const int r = threadIdx.x / PARTS, part = threadIdx.x % PARTS;
     const int qi = r / G, hh = r - qi * G;
     if (r >= QP * G || qt * QP + qi >= k.nq) return;
     auto slot_of = [&](int j) -> int64_t { return j == 0 ? 2 * (int64_t)w0 + 1 : 2 * (int64_t)(w0 + j); };
     float M = kNoMax, L = 0.f;
-    float acc[HALF];
+    float acc[PART];
 #pragma unroll
-    for (int i = 0; i < HALF; ++i) acc[i] = 0.f;
-    for (int j0 = 0; j0 < np; j0 += 2) {
-        float2 ml[2];
-        u32x4 v[2][NV];
+    for (int i = 0; i < PART; ++i) acc[i] = 0.f;
+    for (int j0 = 0; j0 < np; j0 += PB) {
+        float2 ml[PB];
+        u32x4 v[PB][NV];
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const int64_t s = (slot_of(min(j0 + b, np - 1)) * kRowsPerWg + r);
+        for (int b = 0; b < PB; ++b) {
+            const int64_t s = slot_of(min(j0 + b, np - 1)) * kRowsPerWg + r;
             ml[b] = *reinterpret_cast<const float2*>(a.part_ml + s * 2);
-            const u32x4* src = reinterpret_cast<const u32x4*>(a.part_o + s * D + part * HALF);
+            const u32x4* src = reinterpret_cast<const u32x4*>(a.part_o + s * D + part * PART);
 #pragma unroll
             for (int i = 0; i < NV; ++i) v[b][i] = src[i];
         }
-        if (j0 + 1 >= np) ml[1] = make_float2(kNoMax, 0.f);   // the clamped repeat weighs 0
-        const float Mn = fmaxf(M, fmaxf(ml[0].x, ml[1].x));
+        float Mn = M;
+#pragma unroll
+        for (int b = 0; b < PB; ++b) {
+            if (j0 + b >= np) ml[b] = make_float2(kNoMax, 0.f);   // clamped repeats weigh 0
+            Mn = fmaxf(Mn, ml[b].x);
+        }
         const float sc = fast_exp2(M - Mn);
-        const float w0t = ml[0].y * fast_exp2(ml[0].x - Mn);
-        const float w1t = ml[1].y * fast_exp2(ml[1].x - Mn);
+        float wt[PB];
+        L *= sc;
+#pragma unroll
+        for (int b = 0; b < PB; ++b) {
+            wt[b] = ml[b].y * fast_exp2(ml[b].x - Mn);
+            L += wt[b];
+        }
         M = Mn;
-        L = L * sc + w0t + w1t;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            const uint32_t x0[4] = {v[0][i].x, v[0][i].y, v[0][i].z, v[0][i].w};
-            const uint32_t x1[4] = {v[1][i].x, v[1][i].y, v[1][i].z, v[1][i].w};
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                float& lo = acc[8 * i + 2 * q];
-                float& hi = acc[8 * i + 2 * q + 1];
-                lo = fmaf(w1t, bf16lo(x1[q]), fmaf(w0t, bf16lo(x0[q]), lo * sc));
-                hi = fmaf(w1t, bf16hi(x1[q]), fmaf(w0t, bf16hi(x0[q]), hi * sc));
+                float lo = acc[8 * i + 2 * q] * sc, hi = acc[8 * i + 2 * q + 1] * sc;
+#pragma unroll
+                for (int b = 0; b < PB; ++b) {
+                    const uint32_t x = v[b][i][q];
+                    lo = fmaf(wt[b], bf16lo(x), lo);
+                    hi = fmaf(wt[b], bf16hi(x), hi);
+                }
+                acc[8 * i + 2 * q] = lo;
+                acc[8 * i + 2 * q + 1] = hi;
             }
         }
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
     uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) +
                      (((int64_t)k.q0 + qt * QP + qi) * a.num_q_heads + (int64_t)h * G + hh) * D +
-                     part * HALF;
+                     part * PART;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         u32x4 o;
@@ -598,8 +613,8 @@ static hipError_t launch_prefill_t(const PrefillArgs& args, int num_chunks, int 
     hipLaunchKernelGGL((prefill_kernel<D, G>), dim3((uint32_t)nwg), dim3(256), 0, st, a, num_chunks,
                        nqt, (int)items);
     if (a.part_o != nullptr)
-        hipLaunchKernelGGL((prefill_merge_kernel<D, G>), dim3((uint32_t)items), dim3(256), 0, st,
-                           a, nqt, (int)items);
+        hipLaunchKernelGGL((prefill_merge_kernel<D, G>), dim3((uint32_t)items), dim3(kMergeThreads),
+                           0, st, a, nqt, (int)items);
     return hipGetLastError();
 }
 
