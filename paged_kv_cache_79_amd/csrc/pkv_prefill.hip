@@ -507,8 +507,12 @@ __global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(PrefillArg
     if (qt >= k.nqt) return;                   // no work item, no descriptor
     const int2 desc = *reinterpret_cast<const int2*>(a.item_desc + 2 * item);
     const int w0 = __builtin_amdgcn_readfirstlane(desc.x);
-    const int np = __builtin_amdgcn_readfirstlane(desc.y);
+    int np = __builtin_amdgcn_readfirstlane(desc.y);
     if (np <= 0) return;                       // finished in place
+    // the kernel writes a descriptor for every item with work; the bounds keep even a
+    // stale one inside the workspace's slots
+    if (w0 < 0 || w0 >= a.num_wgs) return;
+    np = min(np, a.num_wgs - w0);
     const int r = threadIdx.x / PARTS, part = threadIdx.x % PARTS;
     const int qi = r / G, hh = r - qi * G;
     if (r >= QP * G || qt * QP + qi >= k.nq) return;
