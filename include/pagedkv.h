@@ -150,6 +150,35 @@ pkv_status paged_attention_decode(pkv_dtype dtype, void* out, const void* q,
                                   size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * paged_attention_decode_noalloc -- paged_attention_decode for callers that cannot
+ * allocate device memory or pass a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments, semantics and
+ * results (identical bits) as paged_attention_decode without the workspace: the call
+ * uses a fixed scratch array in device memory that the library holds for the whole
+ * process (one per device, paged_attention_decode_noalloc_scratch_bytes() bytes,
+ * 20 MiB), and allocates nothing.
+ *   - PKV_ERR_WORKSPACE (nothing launched) when the call would need more workspace
+ *     than that (paged_attention_decode_workspace_bytes() > the scratch size): the
+ *     default split needs at most 2 * 8 * num_compute_units * G * (head_dim + 2) * 4
+ *     bytes (17 MB at G = 8, head_dim 128 on 256 compute units); fixed partitions
+ *     need num_seqs * num_q_heads * partitions * (head_dim + 2) * 4.
+ *   - Every call on a device shares that device's scratch: calls that overlap in
+ *     time on one device (other streams, other threads) race and give unspecified
+ *     output.  Calls ordered on one stream are fine.  The scratch keeps the last
+ *     call's contents; nothing in it needs initialisation.
+ *   - PKV_ERR_LAUNCH if the scratch's device address cannot be obtained.
+ */
+size_t paged_attention_decode_noalloc_scratch_bytes(void);
+pkv_status paged_attention_decode_noalloc(pkv_dtype dtype, void* out, const void* q,
+                                          const void* k_pool, const void* v_pool,
+                                          int32_t num_blocks, int32_t num_kv_heads,
+                                          int32_t block_size, int32_t head_dim,
+                                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                          const int32_t* context_lens, int32_t num_seqs,
+                                          int32_t max_context_len, int32_t num_q_heads, float scale,
+                                          int32_t partition_tokens, hipStream_t stream);
+
+/*
  * contiguous_attention_decode -- the unpaged baseline of paged_attention_decode:
  * the same attention over K/V stored contiguously per sequence, as a system that
  * reserves each request's whole maximum length up front would ("vAttention",

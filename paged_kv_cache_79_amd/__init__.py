@@ -23,6 +23,8 @@ EXPORTS = (
     "copy_blocks",
     "paged_attention_decode_workspace_bytes",
     "paged_attention_decode",
+    "paged_attention_decode_noalloc_scratch_bytes",
+    "paged_attention_decode_noalloc",
     "contiguous_attention_decode",
     "paged_attention_decode_shared_prefix_workspace_bytes",
     "paged_attention_decode_shared_prefix",
@@ -81,6 +83,11 @@ def load_library(path: Optional[str] = None):
     lib.paged_attention_decode.argtypes = [ctypes.c_int, VP, VP, VP, VP, I32, I32, I32, I32, VP, I32,
                                            VP, I32, I32, I32, F, I32, VP, SZ, VP]
     lib.paged_attention_decode.restype = ctypes.c_int
+    lib.paged_attention_decode_noalloc_scratch_bytes.argtypes = []
+    lib.paged_attention_decode_noalloc_scratch_bytes.restype = SZ
+    lib.paged_attention_decode_noalloc.argtypes = [ctypes.c_int, VP, VP, VP, VP, I32, I32, I32, I32,
+                                                   VP, I32, VP, I32, I32, I32, F, I32, VP]
+    lib.paged_attention_decode_noalloc.restype = ctypes.c_int
     lib.contiguous_attention_decode.argtypes = [ctypes.c_int, VP, VP, VP, VP, I32, I32, I32, I32, VP,
                                                 I32, I32, F, VP, SZ, VP]
     lib.contiguous_attention_decode.restype = ctypes.c_int
@@ -263,6 +270,34 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens, m
         _dtype_code(q), _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), nb, hkv, bs, d,
         _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), S, int(max_context_len),
         hq, float(scale), int(partition_tokens), _ptr(workspace), wbytes, _stream(stream)))
+
+
+def paged_attention_decode_noalloc_scratch_bytes() -> int:
+    return int(load_library().paged_attention_decode_noalloc_scratch_bytes())
+
+
+def paged_attention_decode_noalloc(out, q, k_pool, v_pool, block_tables, context_lens,
+                                   max_context_len: int, scale: float, partition_tokens: int = 0,
+                                   stream=None) -> None:
+    """paged_attention_decode through the library's fixed per-device scratch: nothing is
+    allocated (for graph capture and callers that cannot allocate).  Calls that overlap
+    in time on one device share that scratch and race."""
+    import torch
+    for n, t in (("out", out), ("q", q), ("k_pool", k_pool), ("v_pool", v_pool)):
+        _dev(t, n)
+    _dev(block_tables, "block_tables", torch.int32)
+    _dev(context_lens, "context_lens", torch.int32)
+    nb, hkv, bs, d = _pool_geom(k_pool, v_pool)
+    S, hq = int(q.shape[0]), int(q.shape[1])
+    if q.dim() != 3 or q.shape[2] != d or out.shape != q.shape or q.dtype != k_pool.dtype or out.dtype != q.dtype:
+        raise ValueError("q/out must be [num_seqs][num_q_heads][head_dim] of the pool dtype")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables must be [num_seqs][max_blocks], context_lens [num_seqs]")
+    lib = load_library()
+    _check("paged_attention_decode_noalloc", lib.paged_attention_decode_noalloc(
+        _dtype_code(q), _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), nb, hkv, bs, d,
+        _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), S, int(max_context_len),
+        hq, float(scale), int(partition_tokens), _stream(stream)))
 
 
 def contiguous_attention_decode(out, q, k_cache, v_cache, context_lens, max_context_len: int,

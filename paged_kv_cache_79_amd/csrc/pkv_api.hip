@@ -4,6 +4,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "pagedkv.h"
 #include "pkv_internal.h"
@@ -114,6 +115,33 @@ pkv_status setup_balanced(DecodeArgs& a, int64_t resident, int32_t num_seqs, int
     a.part_o = static_cast<float*>(workspace);
     a.part_ml = a.part_o + (size_t)waves * 2 * group * head_dim;
     return PKV_OK;
+}
+
+// Scratch of paged_attention_decode_noalloc: one copy per device, kept for the
+// process's lifetime.  Host code never uses the array's name as an address (on the
+// host it is only a stand-in for the symbol); the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kNoallocScratchBytes = (size_t)20 << 20;
+__device__ __align__(256) char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {nullptr};
+
+// Device address of the current device's scratch, or nullptr if it cannot be had.
+void* scratch_ptr() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
 }
 
 }  // namespace
@@ -353,6 +381,41 @@ pkv_status paged_attention_decode(pkv_dtype dtype, void* out, const void* q, con
         if (sb != PKV_OK) return sb;
     }
     return launch_status(launch_decode(a, dtype == PKV_BF16, head_dim, group, num_seqs, stream));
+}
+
+size_t paged_attention_decode_noalloc_scratch_bytes(void) { return kNoallocScratchBytes; }
+
+pkv_status paged_attention_decode_noalloc(pkv_dtype dtype, void* out, const void* q,
+                                          const void* k_pool, const void* v_pool,
+                                          int32_t num_blocks, int32_t num_kv_heads,
+                                          int32_t block_size, int32_t head_dim,
+                                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                          const int32_t* context_lens, int32_t num_seqs,
+                                          int32_t max_context_len, int32_t num_q_heads, float scale,
+                                          int32_t partition_tokens, hipStream_t stream) {
+    const size_t need = decode_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                         max_context_len, partition_tokens);
+    if (need > kNoallocScratchBytes) {
+        // more than the fixed scratch holds: run the usual argument checks with no
+        // workspace; they end in PKV_ERR_WORKSPACE at the latest, and nothing is launched
+        return paged_attention_decode(dtype, out, q, k_pool, v_pool, num_blocks, num_kv_heads,
+                                      block_size, head_dim, block_tables, max_blocks_per_seq,
+                                      context_lens, num_seqs, max_context_len, num_q_heads, scale,
+                                      partition_tokens, nullptr, 0, stream);
+    }
+    void* ws = need > 0 ? scratch_ptr() : nullptr;
+    if (need > 0 && ws == nullptr) {
+        // no device address for the scratch: argument errors still come first
+        const pkv_status s = paged_attention_decode(
+            dtype, out, q, k_pool, v_pool, num_blocks, num_kv_heads, block_size, head_dim,
+            block_tables, max_blocks_per_seq, context_lens, num_seqs, max_context_len, num_q_heads,
+            scale, partition_tokens, nullptr, 0, stream);
+        return s == PKV_ERR_WORKSPACE ? PKV_ERR_LAUNCH : s;
+    }
+    return paged_attention_decode(dtype, out, q, k_pool, v_pool, num_blocks, num_kv_heads,
+                                  block_size, head_dim, block_tables, max_blocks_per_seq,
+                                  context_lens, num_seqs, max_context_len, num_q_heads, scale,
+                                  partition_tokens, ws, ws ? kNoallocScratchBytes : 0, stream);
 }
 
 pkv_status contiguous_attention_decode(pkv_dtype dtype, void* out, const void* q,

@@ -104,6 +104,29 @@ def test_decode_validation(lib):
     assert decode(lib, maxctx=64, mb=4, pt=0) == WS
 
 
+def noalloc(lib, dtype=1, nb=8, hkv=2, bs=16, d=128, mb=4, S=2, maxctx=64, hq=8, scale=0.1,
+            pt=0, ptr=P):
+    return lib.paged_attention_decode_noalloc(dtype, ptr, ptr, ptr, ptr, nb, hkv, bs, d, ptr, mb, ptr,
+                                              S, maxctx, hq, scale, pt, None)
+
+
+@dummy_ptrs
+def test_decode_noalloc_validation(lib):
+    cap = lib.paged_attention_decode_noalloc_scratch_bytes()
+    assert cap == 20 << 20
+    # the default split fits the scratch on a 256-CU device at every group size
+    assert lib.paged_attention_decode_workspace_bytes(64, 64, 8, 128, 200000, 0) <= cap
+    # fixed partitions beyond the scratch: PKV_ERR_WORKSPACE before anything else happens
+    assert lib.paged_attention_decode_workspace_bytes(64, 32, 8, 128, 1 << 16, 64) > cap
+    assert noalloc(lib, S=64, hq=32, hkv=8, mb=4096, maxctx=1 << 16, pt=64) == WS
+    # argument errors as for paged_attention_decode
+    assert noalloc(lib, hq=9) == SHAPE
+    assert noalloc(lib, pt=100) == SHAPE
+    assert noalloc(lib, hq=36, hkv=2) == UNSUP
+    assert noalloc(lib, ptr=None) == NULL
+    assert noalloc(lib, S=0, ptr=None) == OK
+
+
 def test_workspace_sizes(lib):
     f = lib.paged_attention_decode_workspace_bytes
     # fixed partitions: S * Hq * parts * (D + 2) floats, none when one partition suffices
