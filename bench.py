@@ -65,11 +65,12 @@ def prefill_flops(pre) -> int:
     return int(4 * pre.head_dim * pre.num_q_heads * tot)
 
 
-def recorded_traffic(workload_name):
+def recorded_traffic(workload_name, prefix="decode_"):
     """Counter-derived HBM bytes per call of the timed kernels, as recorded under profiles/
     with the hashes of the sources they were measured on; None when absent or stale."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"decode_{workload_name.replace('_decode', '')}_traffic.json")
+    stem = prefix + workload_name.replace("_decode", "")
+    path = os.path.join(ROOT, "profiles", f"{stem}_traffic.json")
     try:
         rec = json.load(open(path))
         for name, sha in rec["sources_sha256"].items():
@@ -88,49 +89,64 @@ def log(msg):
 # ----------------------------------------------------------------------------
 # CPU oracle baseline (bounded sample, on this host's cores)
 # ----------------------------------------------------------------------------
-_ORACLE_BATCH = None
+# Batches the oracle workers read, by leg name: set before the worker pool is forked
+# (which happens before this process first touches the GPU), so every worker inherits
+# them and no worker inherits a GPU context.
+_ORACLE_BATCHES = {}
+# The box gives one GPU's job a share of 16 host cores, whatever the affinity mask shows.
+CPU_SHARE = 16
 
 
-def _oracle_unit(s):
+def _oracle_unit(task):
     from threadpoolctl import threadpool_limits
     from oracle import paged as O
-    b, k, v = _ORACLE_BATCH
+    name, s = task
+    b, k, v = _ORACLE_BATCHES[name]
     with threadpool_limits(1):
         O.decode(b.q, k, v, b.block_tables, b.context_lens, b.scale, b.dtype, b.num_kv_heads,
                  seqs=[s])
     return s
 
 
-def cpu_baseline(b, target_s=12.0):
-    """Time the oracle's decode of the batch (after the step's write) on this host's cores,
-    one process per core, one sequence per task; repeat passes until about target_s of CPU."""
-    import multiprocessing as mp
+def oracle_register(name, b):
+    """The oracle's view of a decode batch after the step's cache write."""
     from oracle import paged as O
-    global _ORACLE_BATCH
     k = O.kv_write(b.k_pool, b.k_new, b.slot_mapping)
     v = O.kv_write(b.v_pool, b.v_new, b.slot_mapping)
-    _ORACLE_BATCH = (b, k, v)
-    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    _ORACLE_BATCHES[name] = (b, k, v)
+
+
+def oracle_pool():
+    """Worker processes for the oracle baseline, one per core of this job's share."""
+    import multiprocessing as mp
+    avail = len(os.sched_getaffinity(0))
+    used = max(1, min(avail, CPU_SHARE))
+    return mp.get_context("fork").Pool(used), avail, used
+
+
+def cpu_baseline(pool, avail, used, name, target_s=8.0):
+    """Time the oracle's decode of the batch registered as `name` on this host: one
+    sequence per task over the worker pool, passes repeated until about target_s."""
+    b = _ORACLE_BATCHES[name][0]
     # one single-process pass over a few sequences estimates the per-sequence cost
     t0 = time.perf_counter()
-    probe = list(range(min(4, b.num_seqs)))
+    probe = list(range(min(2, b.num_seqs)))
     for s in probe:
-        _oracle_unit(s)
+        _oracle_unit((name, s))
     per_seq = (time.perf_counter() - t0) / len(probe)
-    passes = max(1, int(math.ceil(target_s / max(per_seq * b.num_seqs, 1e-3))))
-    passes = min(passes, 8)
-    ctx = mp.get_context("fork")
-    with ctx.Pool(cores) as pool:
-        t0 = time.perf_counter()
-        for _ in range(passes):
-            pool.map(_oracle_unit, range(b.num_seqs), chunksize=1)
-        wall = time.perf_counter() - t0
-    _ORACLE_BATCH = None
+    est_pass = per_seq * b.num_seqs / used
+    passes = max(1, min(8, int(math.ceil(target_s / max(est_pass, 1e-3)))))
+    t0 = time.perf_counter()
+    for _ in range(passes):
+        pool.map(_oracle_unit, [(name, s) for s in range(b.num_seqs)], chunksize=1)
+    wall = time.perf_counter() - t0
     byts = passes * kv_bytes(b.context_lens, b.num_kv_heads, b.head_dim, 2 if b.dtype == "bf16" else 4)
-    return {"value": round(byts / wall / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+    return {"value": round(byts / wall / 1e9, 4), "unit": "GB/s", "cores": used,
+            "cores_available": avail, "kind": "oracle",
             "seqs_per_s": round(passes * b.num_seqs / wall, 2), "wall_s": round(wall, 2),
             "sample": f"{passes} pass(es) of fp64 numpy decode over all {b.num_seqs} sequences of "
-                      f"the {b.name} batch, one process per core"}
+                      f"the {b.name} batch, one sequence per task on {used} worker processes "
+                      f"({avail} cores in the affinity mask, {CPU_SHARE} the job's share)"}
 
 
 # ----------------------------------------------------------------------------
@@ -367,28 +383,40 @@ def run_swap(args):
             "swap": res, "roofline": None, "cpu_baseline": None}
 
 
-def run(args):
+# The default run: the GQA batch (the headline line), the long-context shard and the
+# mixed chunked-prefill + decode batch, each a leg of the same JSON line.
+DEFAULT_LEGS = ("gqa", "long", "mixed")
+
+
+def prepare(name, args):
+    """Host-side workload of one leg (numpy only: nothing here touches the GPU)."""
+    log(f"building workload {name}")
+    contig = args.layout == "contiguous"
+    wl = make_workload(name, args.block_size, contig)
+    b = wl["batch"]
+    log(f"workload ready: {b.num_seqs} sequences, max context {b.max_context_len}")
+    return dict(name=name, wl=wl, contig=contig)
+
+
+def gpu_leg(prep, args, ceiling):
+    """Time one leg on the GPU: the whole step, the decode call alone (roofline), per-call
+    percentiles, the step's other calls and, for the mixed batch, the prefill call."""
     import torch
     import paged_kv_cache_79_amd as pkv
 
-    log(f"building workload {args.workload}")
-    contig = args.layout == "contiguous"
-    wl = make_workload(args.workload, args.block_size, contig)
+    wl, contig, name = prep["wl"], prep["contig"], prep["name"]
     b = wl["batch"]
-    log(f"workload ready: {b.num_seqs} sequences, max context {b.max_context_len}")
     elem = 2 if b.dtype == "bf16" else 4
     if contig:
         # the unpaged baseline: the same K/V values in [S][L][Hkv][D] slabs, already
         # holding the step's new token (no cache write is timed)
-        kc, vc = b.extra.pop("k_cache"), b.extra.pop("v_cache")
+        kc, vc = b.extra["k_cache"], b.extra["v_cache"]
         pool_bytes = 2 * kc.nbytes
     else:
         pool_bytes = 2 * b.k_pool.nbytes
     # enough pool copies that a rotation cycle spans well over 4x the 256 MB MALL
     copies = max(2, min(8, int(math.ceil(2.4e9 / max(pool_bytes, 1)))))
     k0, v0 = (_dev(kc), _dev(vc)) if contig else (_dev(b.k_pool), _dev(b.v_pool))
-    if contig:
-        del kc, vc
     pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(copies - 1)]
     q = _dev(b.q)
     tables = _dev(b.block_tables)
@@ -399,10 +427,10 @@ def run(args):
     ws_bytes = pkv.paged_attention_decode_workspace_bytes(b.num_seqs, b.num_q_heads, b.num_kv_heads,
                                                           b.head_dim, b.max_context_len, pt)
     extra = wl["extra"]
-    cow_map = _dev(extra.block_mapping) if args.workload == "prefix_cow" else None
+    cow_map = _dev(extra.block_mapping) if name == "prefix_cow" else None
     shared = None
     if args.shared_prefix:
-        if args.workload != "prefix_cow" or pt != 0:
+        if name != "prefix_cow" or pt != 0:
             raise SystemExit("--shared-prefix applies to the prefix_cow workload (balanced split)")
         # one group of every sequence; the blocks still shared after copy-on-write
         plen = (len(extra.prefix_blocks) - 1) * b.block_size
@@ -412,7 +440,7 @@ def run(args):
                       pre=_dev(np.array([plen], np.int32)))
         ws_bytes = pkv.paged_attention_decode_shared_prefix_workspace_bytes(
             b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim, b.max_context_len, plen)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     pre = wl["prefill"]
     if pre is not None:
         pq, pcu = _dev(pre.q), _dev(pre.cu_q_lens)
@@ -421,7 +449,7 @@ def run(args):
         # the prefill's workspace lets it split uneven chunks over keys (--no-prefill-split: none)
         pws = None
         if not args.no_prefill_split:
-            pws = torch.empty(max(1, pkv.paged_attention_prefill_chunk_workspace_bytes(
+            pws = torch.zeros(max(1, pkv.paged_attention_prefill_chunk_workspace_bytes(
                 pre.num_q_heads, pre.num_kv_heads, pre.head_dim)), dtype=torch.uint8, device="cuda")
 
     stream = torch.cuda.current_stream()
@@ -441,6 +469,12 @@ def run(args):
         pkv.paged_attention_decode(out, q, kp, vp, tables, ctx, b.max_context_len, b.scale,
                                    partition_tokens=pt, workspace=ws)
 
+    def prefill(i):
+        kp, vp = pools[i % copies]
+        pkv.paged_attention_prefill_chunk(pout, pq, pcu, kp, vp, ptab, pctx, pre.max_q_len,
+                                          pre.max_context_len, pre.scale, workspace=pws,
+                                          split=pws is not None)
+
     def step(i):
         if contig:
             decode(i)
@@ -450,9 +484,7 @@ def run(args):
             pkv.copy_blocks(kp, vp, cow_map)
         pkv.paged_kv_write(kp, vp, k_new, v_new, slots)
         if pre is not None:
-            pkv.paged_attention_prefill_chunk(pout, pq, pcu, kp, vp, ptab, pctx, pre.max_q_len,
-                                              pre.max_context_len, pre.scale, workspace=pws,
-                                              split=pws is not None)
+            prefill(i)
         decode(i)
 
     def timed(fn, n):
@@ -467,15 +499,14 @@ def run(args):
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) / n
 
-    log(f"{copies} pool copies on device; warmup {args.warmup}, timing {args.steps} steps")
+    log(f"{name}: {copies} pool copies on device; warmup {args.warmup}, timing {args.steps} steps")
     for i in range(args.warmup):
         step(i)
     ms_step = timed(step, args.steps)
-    # the decode kernels alone, same inputs and pool rotation, for the roofline
+    # the decode call alone, same inputs and pool rotation, for the roofline
     dec_runs = [timed(decode, args.steps) for _ in range(3)]
     dec_avg = sorted(dec_runs)[1]
     dec_pct = per_call_us(decode, args.steps, stream)
-    # the step's other calls alone
     # the step's other calls alone (device time: enqueued behind 8 decode calls)
     parts = {}
     if not contig:
@@ -492,7 +523,6 @@ def run(args):
                 kp, vp = pools[i % copies]
                 pkv.copy_blocks(kp, vp, cow_map)
             parts["copy_blocks_us"] = round(device_us(copy, 10, busy, stream), 2)
-    ceiling = read_ceiling() if not args.no_read_ceiling else None
     byts = kv_bytes(b.context_lens, b.num_kv_heads, b.head_dim, elem)
     value = byts / (ms_step * 1e-3) / 1e9
     # the roofline counts what the path has to read: with a shared prefix its K/V once
@@ -520,6 +550,11 @@ def run(args):
                    "split": "balanced" if pt == 0 else f"partitions of {pt}",
                    "layout": "contiguous [S][L][Hkv][D], no block table (step = decode only)"
                              if contig else "paged [NB][Hkv][bs][D]",
+                   "step": ("decode" if contig else
+                            " + ".join((["copy_blocks"] if cow_map is not None else []) +
+                                       ["paged_kv_write"] +
+                                       (["paged_attention_prefill_chunk"] if pre is not None else []) +
+                                       ["decode"])),
                    "pool_copies_rotated": copies,
                    **({"decode": f"shared prefix: one group of {b.num_seqs}, "
                                  f"{shared['plen']}-token prefix"} if shared else {})},
@@ -533,7 +568,7 @@ def run(args):
                      "kernel": ("contiguous_attention_decode" if contig else
                                 "paged_attention_decode_shared_prefix (prefix pass + "
                                 "attention kernel + merge kernel)" if shared else
-                                "paged_attention_decode (attention kernel + merge kernel)"),
+                                "paged_attention_decode (whole call)"),
                      "algorithmic_bytes": unique,
                      "avg_us": round(dec_avg * 1e3, 2),
                      "runs_us": [round(x * 1e3, 2) for x in dec_runs],
@@ -545,24 +580,57 @@ def run(args):
     }
     if pre is not None:
         # prefill alone, same inputs and pool rotation
-        def prefill(i):
-            kp, vp = pools[i % copies]
-            pkv.paged_attention_prefill_chunk(pout, pq, pcu, kp, vp, ptab, pctx, pre.max_q_len,
-                                              pre.max_context_len, pre.scale, workspace=pws,
-                                              split=pws is not None)
-        p_ms = timed(prefill, max(5, args.steps // 4))
+        p_runs = [timed(prefill, max(5, args.steps // 2)) for _ in range(3)]
+        p_ms = sorted(p_runs)[1]
         fl = prefill_flops(pre)
-        rec["prefill"] = {"avg_us": round(p_ms * 1e3, 2), "flops": fl,
-                          "key_split_allowed": pws is not None,
-                          "tflops": round(fl / (p_ms * 1e-3) / 1e12, 2),
-                          "mfma_frac": round(fl / (p_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
-    log(f"GPU: {ms_step * 1e3:.1f} us/step, decode {dec_avg * 1e3:.1f} us")
-    if not args.no_cpu_baseline and not contig:
-        log("timing the CPU oracle")
-        rec["cpu_baseline"] = cpu_baseline(b)
-    else:
-        rec["cpu_baseline"] = None
+        tf = fl / (p_ms * 1e-3) / 1e12
+        rec["prefill"] = {
+            "config": {"chunks": pre.num_chunks, "queries_per_chunk": pre.max_q_len,
+                       "max_context_len": pre.max_context_len, "causal": True},
+            "avg_us": round(p_ms * 1e3, 2), "runs_us": [round(x * 1e3, 2) for x in p_runs],
+            "flops": fl, "key_split_allowed": pws is not None,
+            "tflops": round(tf, 2), "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "traffic": recorded_traffic("prefill_mixed_bf16", prefix="")
+                                    if pws is not None else None,
+                         "kernel": "paged_attention_prefill_chunk (whole call)"}}
+    log(f"{name}: {ms_step * 1e3:.1f} us/step, decode {dec_avg * 1e3:.1f} us"
+        + (f", prefill {rec['prefill']['avg_us']:.1f} us" if pre is not None else ""))
+    del pools, k0, v0, ws
+    torch.cuda.empty_cache()
     return rec
+
+
+def run(args):
+    names = list(DEFAULT_LEGS) if args.workload == "all" else [args.workload]
+    if args.layout == "contiguous" and len(names) > 1:
+        raise SystemExit("--layout contiguous needs --workload gqa or long")
+    preps = [prepare(n, args) for n in names]
+    pool = None
+    want_cpu = not args.no_cpu_baseline and args.layout != "contiguous"
+    if want_cpu:
+        for p in preps:
+            oracle_register(p["name"], p["wl"]["batch"])
+        # forked before the first GPU call, so no worker inherits a GPU context
+        pool, avail, used = oracle_pool()
+    try:
+        ceiling = read_ceiling() if not args.no_read_ceiling else None
+        recs = [gpu_leg(p, args, ceiling) for p in preps]
+        for p, r in zip(preps, recs):
+            if want_cpu:
+                log(f"{p['name']}: timing the CPU oracle")
+                r["cpu_baseline"] = cpu_baseline(pool, avail, used, p["name"])
+            else:
+                r["cpu_baseline"] = None
+    finally:
+        if pool is not None:
+            pool.close()
+            pool.join()
+    top = recs[0]
+    if len(recs) > 1:
+        top["legs"] = {r["config"]["workload"]: r for r in recs[1:]}
+    return top
 
 
 def main():
@@ -570,8 +638,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="gqa", choices=["gqa", "long", "prefix_cow", "mixed", "spec",
-                                                             "swap"])
+    ap.add_argument("--workload", default="all",
+                    choices=["all", "gqa", "long", "prefix_cow", "mixed", "spec", "swap"],
+                    help="all (default): the gqa line with the long and mixed batches as legs")
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--layout", default="paged", choices=["paged", "contiguous"],
                     help="contiguous: the unpaged baseline on the same K/V values (gqa, long)")
