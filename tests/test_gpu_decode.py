@@ -166,6 +166,8 @@ def test_full_long_context():
 
 
 def test_full_prefix_cow():
+    """The copy-on-write batch at full size: every row against the oracle."""
+    from tests.oracle_pool import decode_all
     p = W.prefix_cow()
     b = p.batch
     print(f"decode prefix_cow full S={b.num_seqs}", flush=True)
@@ -173,15 +175,16 @@ def test_full_prefix_cow():
     pkv.copy_blocks(r.k, r.v, dev(p.block_mapping))
     r.write()
     got = O.widen(r.decode(0), "bf16")
-    rng = np.random.Generator(np.random.PCG64(1))
-    seqs = sorted(rng.choice(b.num_seqs, 24, replace=False).tolist())
     k = O.kv_write(O.copy_blocks(b.k_pool, p.block_mapping), b.k_new, b.slot_mapping)
     v = O.kv_write(O.copy_blocks(b.v_pool, p.block_mapping), b.v_new, b.slot_mapping)
-    want = oracle_decode(b, k, v, seqs=seqs)
+    want = decode_all(b.q, k, v, b.block_tables, b.context_lens, b.scale, "bf16", b.num_kv_heads)
+    assert not np.isnan(want).any()
     assert rownorm_err(got, want) <= TOL["bf16"]
 
 
 def test_full_mixed_decode_part():
+    """The decode sequences of the mixed batch at full size: every row against the oracle."""
+    from tests.oracle_pool import decode_all
     m = W.mixed()
     b = m.decode
     print(f"decode mixed full S={b.num_seqs}", flush=True)
@@ -189,9 +192,8 @@ def test_full_mixed_decode_part():
     r.write()
     got = O.widen(r.decode(0), "bf16")
     k, v = oracle_after_write(b)
-    rng = np.random.Generator(np.random.PCG64(2))
-    seqs = sorted(rng.choice(b.num_seqs, 24, replace=False).tolist())
-    want = oracle_decode(b, k, v, seqs=seqs)
+    want = decode_all(b.q, k, v, b.block_tables, b.context_lens, b.scale, "bf16", b.num_kv_heads)
+    assert not np.isnan(want).any()
     assert rownorm_err(got, want) <= TOL["bf16"]
 
 

@@ -98,9 +98,10 @@ def test_last_row_equals_decode():
     assert rownorm_err(got[-1:], dec) <= TOL["bf16"]
 
 
-def test_full_mixed_prefill_sampled():
-    """The mixed workload's 4 chunks of 512 queries; the oracle checks a sample of rows
-    (first, last and random (query, head) pairs of every chunk)."""
+def test_full_mixed_prefill():
+    """The mixed workload's 4 chunks of 512 queries, launched as the benchmark launches
+    them (with the key-split workspace): every (query, head) row against the oracle."""
+    from tests.oracle_pool import prefill_all
     m = W.mixed()
     b, pre = m.decode, m.prefill
     print("prefill mixed full", flush=True)
@@ -109,15 +110,9 @@ def test_full_mixed_prefill_sampled():
     got = run_prefill(pre, r.k, r.v)
     k = O.kv_write(b.k_pool, b.k_new, b.slot_mapping)
     v = O.kv_write(b.v_pool, b.v_new, b.slot_mapping)
-    rng = np.random.Generator(np.random.PCG64(3))
-    rows = []
-    for c in range(pre.num_chunks):
-        q0, q1 = int(pre.cu_q_lens[c]), int(pre.cu_q_lens[c + 1])
-        for i in [q0, q0 + 1, q1 - 1] + rng.integers(q0, q1, 6).tolist():
-            for hq in rng.choice(pre.num_q_heads, 3, replace=False):
-                rows.append((i, int(hq)))
-    want = O.prefill_chunk(pre.q, pre.cu_q_lens, k, v, pre.block_tables, pre.context_lens,
-                           pre.scale, "bf16", pre.num_kv_heads, rows=rows)
+    want = prefill_all(pre.q, pre.cu_q_lens, k, v, pre.block_tables, pre.context_lens, pre.scale,
+                       "bf16", pre.num_kv_heads)
+    assert not np.isnan(want).any()
     assert rownorm_err(got, want) <= TOL["bf16"]
 
 
