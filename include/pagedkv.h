@@ -54,7 +54,10 @@ extern "C" {
 
 typedef enum pkv_dtype {
     PKV_F32 = 0,
-    PKV_BF16 = 1
+    PKV_BF16 = 1,
+    /* not a type: widens the enum so that any non-negative int a foreign caller passes
+       is a value of it (the library then rejects it with PKV_ERR_DTYPE) */
+    PKV_DTYPE_INT32_ = 0x7fffffff
 } pkv_dtype;
 
 typedef enum pkv_status {
@@ -66,7 +69,10 @@ typedef enum pkv_status {
     PKV_ERR_WORKSPACE = 5,     /* workspace missing or smaller than required */
     PKV_ERR_LAUNCH = 6,        /* the HIP runtime refused a launch or copy */
     PKV_ERR_NO_BLOCKS = 7,     /* block pool: not enough free blocks (nothing was taken) */
-    PKV_ERR_VALIDATION = 8     /* pkv_validate found violated preconditions (binding-level) */
+    PKV_ERR_VALIDATION = 8,    /* pkv_validate found violated preconditions (binding-level) */
+    /* not a status: widens the enum so that any non-negative int is a value of it
+       (pkv_status_string answers such values with "PKV_ERR_UNKNOWN") */
+    PKV_STATUS_INT32_ = 0x7fffffff
 } pkv_status;
 
 /* Human-readable name of a status code (static string, never NULL). */

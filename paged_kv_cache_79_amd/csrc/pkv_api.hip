@@ -52,6 +52,12 @@ pkv_status launch_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_E
 
 int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// a * b for non-negative a, b, or limit + 1 when the product exceeds limit (no overflow)
+int64_t product_exceeds(int64_t a, int64_t b, int64_t limit) {
+    if (a > 0 && b > limit / a) return limit + 1;
+    return a * b;
+}
+
 int32_t num_partitions(int32_t max_context_len, int32_t pt) {
     return max_context_len <= 0 ? 1 : (int32_t)cdiv64(max_context_len, pt);
 }
@@ -159,6 +165,7 @@ const char* pkv_status_string(pkv_status s) {
         case PKV_ERR_LAUNCH: return "PKV_ERR_LAUNCH: kernel launch or copy failed";
         case PKV_ERR_NO_BLOCKS: return "PKV_ERR_NO_BLOCKS: not enough free blocks in the pool";
         case PKV_ERR_VALIDATION: return "PKV_ERR_VALIDATION: device contents violate a precondition";
+        default: break;
     }
     return "PKV_ERR_UNKNOWN";
 }
@@ -666,7 +673,8 @@ pkv_status paged_attention_prefill_chunk(pkv_dtype dtype, void* out, const void*
     if (!out || !q || !cu_q_lens || !k_pool || !v_pool || !block_tables || !context_lens)
         return PKV_ERR_NULL;
     // work items: query tiles (128 / group query positions each) x kv heads x chunks
-    if (cdiv64(max_q_len, 128 / group) * num_kv_heads * num_chunks > ((int64_t)1 << 30))
+    if (product_exceeds(product_exceeds(cdiv64(max_q_len, 128 / group), num_kv_heads, (int64_t)1 << 30),
+                        num_chunks, (int64_t)1 << 30) > ((int64_t)1 << 30))
         return PKV_ERR_UNSUPPORTED;
 
     PrefillArgs a;
