@@ -232,10 +232,18 @@ def copy_blocks(k_pool, v_pool, block_mapping, stream=None) -> None:
         _stream(stream)))
 
 
-def decode_workspace(num_bytes: int, device):
-    """Device scratch for a decode call (its contents need no initialisation)."""
+def decode_workspace(num_bytes: int, device, stream=None):
+    """Device scratch for a call (its contents need no initialisation).
+
+    The caching allocator ties a block to the stream it was allocated on and hands it
+    out again only in that stream's order, so a workspace for a call on ``stream`` is
+    allocated on ``stream``: when the binding drops it after enqueuing, no allocation
+    on another stream can reuse the memory while the kernels still write to it."""
     import torch
-    return torch.empty(max(int(num_bytes), 1), dtype=torch.uint8, device=device)
+    if stream is None:
+        return torch.empty(max(int(num_bytes), 1), dtype=torch.uint8, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(max(int(num_bytes), 1), dtype=torch.uint8, device=device)
 
 
 def paged_attention_decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int,
@@ -261,7 +269,7 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens, m
         raise ValueError("block_tables must be [num_seqs][max_blocks], context_lens [num_seqs]")
     need = paged_attention_decode_workspace_bytes(S, hq, hkv, d, max_context_len, partition_tokens)
     if workspace is None and need > 0:
-        workspace = decode_workspace(need, q.device)
+        workspace = decode_workspace(need, q.device, stream)
     if workspace is not None:
         _dev(workspace, "workspace")
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -318,7 +326,7 @@ def contiguous_attention_decode(out, q, k_cache, v_cache, context_lens, max_cont
         raise ValueError("q/out must be [num_seqs][num_q_heads][head_dim] of the cache dtype")
     need = paged_attention_decode_workspace_bytes(S, hq, hkv, d, max_context_len, 0)
     if workspace is None and need > 0:
-        workspace = decode_workspace(need, q.device)
+        workspace = decode_workspace(need, q.device, stream)
     if workspace is not None:
         _dev(workspace, "workspace")
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -368,7 +376,7 @@ def paged_attention_decode_shared_prefix(out, q, k_pool, v_pool, block_tables, c
     need = paged_attention_decode_shared_prefix_workspace_bytes(S, hq, hkv, d, max_context_len,
                                                                 max_prefix_len)
     if workspace is None and need > 0:
-        workspace = decode_workspace(need, q.device)
+        workspace = decode_workspace(need, q.device, stream)
     if workspace is not None:
         _dev(workspace, "workspace")
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -411,7 +419,7 @@ def paged_attention_decode_multi_query(out, q, k_pool, v_pool, block_tables, con
         raise ValueError("block_tables must be [num_seqs][max_blocks]")
     need = paged_attention_decode_multi_query_workspace_bytes(S, n, hq, hkv, d)
     if workspace is None and need > 0:
-        workspace = decode_workspace(need, q.device)
+        workspace = decode_workspace(need, q.device, stream)
     if workspace is not None:
         _dev(workspace, "workspace")
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -454,7 +462,7 @@ def paged_attention_prefill_chunk(out, q, cu_q_lens, k_pool, v_pool, block_table
     elif workspace is None:
         need = paged_attention_prefill_chunk_workspace_bytes(int(q.shape[1]), hkv, d)
         if need > 0:
-            workspace = decode_workspace(need, q.device)
+            workspace = decode_workspace(need, q.device, stream)
     if workspace is not None:
         _dev(workspace, "workspace")
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -510,7 +518,11 @@ def validate(num_blocks: int, block_size: int, block_tables=None, context_lens=N
     mb = int(block_tables.shape[1]) if block_tables is not None and block_tables.dim() == 2 else 0
     T = 0 if slot_mapping is None else int(slot_mapping.numel())
     n = 0 if block_mapping is None else int(block_mapping.numel()) // 2
-    counts = torch.empty(4, dtype=torch.int32, device=dev_t.device)
+    if stream is None:
+        counts = torch.empty(4, dtype=torch.int32, device=dev_t.device)
+    else:
+        with torch.cuda.stream(stream):
+            counts = torch.empty(4, dtype=torch.int32, device=dev_t.device)
     _check("pkv_validate", load_library().pkv_validate(
         int(num_blocks), int(block_size), _ptr(block_tables), mb, _ptr(context_lens), S,
         _ptr(slot_mapping), T, _ptr(block_mapping), n, _ptr(counts), _stream(stream)))
