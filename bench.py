@@ -228,7 +228,7 @@ def _dev(a):
     return torch.from_numpy(a).cuda()
 
 
-def make_workload(name, block_size=16, contiguous=False):
+def make_workload(name, block_size=16, contiguous=False, num_seqs=4096):
     import workloads as W
     if contiguous and name not in ("gqa", "long"):
         raise SystemExit("--layout contiguous applies to the gqa and long workloads")
@@ -246,6 +246,15 @@ def make_workload(name, block_size=16, contiguous=False):
     if name == "mixed":
         m = W.mixed(poison=False)
         return dict(batch=m.decode, extra=m, prefill=m.prefill)
+    if name == "many":
+        # the GQA geometry with many short sequences (U[64, 512] tokens): the merge's
+        # cost per output row, independent of the number of sequences
+        rng = np.random.Generator(np.random.PCG64(79010 + num_seqs))
+        ctx = rng.integers(64, 512, size=num_seqs, endpoint=True)
+        b = W.build_decode_batch(name=f"many_{num_seqs}_bf16", dtype="bf16", context_lens=ctx,
+                                 num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                                 seed=79010 + num_seqs, poison=False)
+        return dict(batch=b, extra=None, prefill=None)
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -392,7 +401,7 @@ def prepare(name, args):
     """Host-side workload of one leg (numpy only: nothing here touches the GPU)."""
     log(f"building workload {name}")
     contig = args.layout == "contiguous"
-    wl = make_workload(name, args.block_size, contig)
+    wl = make_workload(name, args.block_size, contig, args.num_seqs)
     b = wl["batch"]
     log(f"workload ready: {b.num_seqs} sequences, max context {b.max_context_len}")
     return dict(name=name, wl=wl, contig=contig)
@@ -639,9 +648,11 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="all",
-                    choices=["all", "gqa", "long", "prefix_cow", "mixed", "spec", "swap"],
+                    choices=["all", "gqa", "long", "prefix_cow", "mixed", "spec", "swap", "many"],
                     help="all (default): the gqa line with the long and mixed batches as legs")
     ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--num-seqs", type=int, default=4096,
+                    help="many: number of sequences of U[64, 512] tokens")
     ap.add_argument("--layout", default="paged", choices=["paged", "contiguous"],
                     help="contiguous: the unpaged baseline on the same K/V values (gqa, long)")
     ap.add_argument("--block-size", type=int, default=16, choices=[8, 16, 32],

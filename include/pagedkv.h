@@ -28,9 +28,11 @@
  *    beyond ceil(context_len / block_size) are never read.
  *  - A context length counts every token visible to the step's queries,
  *    including the ones written in this step.
- *  - Supported: head_dim in {64, 128}; block_size in {4, 8, 16, 32} with
- *    block_size * head_dim * element size >= 1024 bytes; one pool block
- *    (all kv heads) smaller than 2 GiB; num_q_heads / num_kv_heads in 1..8.
+ *  - Supported: head_dim in {64, 128}; block_size in {4, 8, 16, 32}; one pool
+ *    block (all kv heads) smaller than 2 GiB; num_q_heads / num_kv_heads in 1..8.
+ *    The matrix-core paths (multi-query decode, shared-prefix decode, chunked
+ *    prefill) also need block_size * head_dim * element size >= 1024 bytes, which
+ *    excludes bf16 with head_dim 64 and block_size 4 there (PKV_ERR_UNSUPPORTED).
  *  - Host-checkable arguments are validated before anything is enqueued; a
  *    non-zero status means nothing was launched.  Device-resident contents
  *    (block ids, slots, lengths) are not validated; out-of-range block ids
@@ -68,8 +70,9 @@ typedef enum pkv_status {
     PKV_ERR_UNSUPPORTED = 4,   /* valid but not implemented (head_dim, block_size, group size, dtype) */
     PKV_ERR_WORKSPACE = 5,     /* workspace missing or smaller than required */
     PKV_ERR_LAUNCH = 6,        /* the HIP runtime refused a launch or copy */
-    PKV_ERR_NO_BLOCKS = 7,     /* block pool: not enough free blocks (nothing was taken) */
-    PKV_ERR_VALIDATION = 8,    /* pkv_validate found violated preconditions (binding-level) */
+    PKV_ERR_VALIDATION = 7,    /* device contents violate a precondition (reported by the
+                                  binding after pkv_validate's counts come back) */
+    PKV_ERR_NO_BLOCKS = 8,     /* block pool: not enough free blocks (nothing was taken) */
     /* not a status: widens the enum so that any non-negative int is a value of it
        (pkv_status_string answers such values with "PKV_ERR_UNKNOWN") */
     PKV_STATUS_INT32_ = 0x7fffffff
@@ -140,7 +143,8 @@ size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_he
  *   context_lens  int32 [num_seqs], each in [0, max_blocks_per_seq*block_size]
  *   max_context_len  host-known upper bound of context_lens (sizes the grid;
  *                    a larger context is truncated to it)
- *   partition_tokens 0 = balanced split (default), else a positive multiple of 64
+ *   partition_tokens 0 = balanced split (default), else a positive multiple of
+ *                 block_size (at most 65535 partitions of max_context_len)
  *   workspace     device scratch of at least paged_attention_decode_workspace_bytes
  *                 (may be NULL when that is 0); its contents need no initialisation
  *                 and are garbage afterwards; calls sharing a workspace must not

@@ -48,8 +48,8 @@ EXPORTS = (
 )
 
 PKV_F32, PKV_BF16 = 0, 1
-PKV_ERR_NO_BLOCKS = 7
-PKV_ERR_VALIDATION = 8
+PKV_ERR_VALIDATION = 7
+PKV_ERR_NO_BLOCKS = 8
 
 _lib = None
 

@@ -23,18 +23,19 @@ int ilog2(int x) {
     return r;
 }
 
-// Shared checks of the pool geometry.  A (block, kv head) run must span at least
-// one wave-wide 16-byte load (64 lanes x 16 B = 1 KiB) so that every such load
-// stays inside one block.
+// Shared checks of the pool geometry.  The matrix-core kernels need a (block, kv
+// head) run to span at least one wave-wide 16-byte load (64 lanes x 16 B = 1 KiB) so
+// that every such load stays inside one block (small_runs = false); the cache write,
+// the block copy and the decode also take shorter runs.
 pkv_status check_geom(pkv_dtype dt, int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
-                      int32_t head_dim, PoolGeom* g) {
+                      int32_t head_dim, PoolGeom* g, bool small_runs = true) {
     if (dt != PKV_F32 && dt != PKV_BF16) return PKV_ERR_DTYPE;
     if (num_blocks <= 0 || num_kv_heads <= 0 || block_size <= 0 || head_dim <= 0)
         return PKV_ERR_SHAPE;
     if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
     if (!pow2(block_size) || block_size < 4 || block_size > 32) return PKV_ERR_UNSUPPORTED;
     const int eb = elem_bytes(dt);
-    if (block_size * head_dim * eb < 1024) return PKV_ERR_UNSUPPORTED;
+    if (!small_runs && block_size * head_dim * eb < 1024) return PKV_ERR_UNSUPPORTED;
     // slots are int64, block offsets int64; a single (block, head) run is < 2^31 bytes
     g->row_bytes = head_dim * eb;
     g->head_stride_bytes = block_size * head_dim * eb;
@@ -73,6 +74,9 @@ int64_t balanced_wave_bound() {
     return (int64_t)cus * 8;
 }
 
+// The balanced split's record of each sequence's first tile, read by the merge.
+size_t tile_prefix_bytes(int32_t num_seqs) { return ((size_t)num_seqs + 1) * sizeof(int64_t); }
+
 size_t decode_workspace(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                         int32_t head_dim, int32_t max_context_len, int32_t partition_tokens) {
     if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
@@ -84,7 +88,8 @@ size_t decode_workspace(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_he
         return (size_t)num_seqs * num_q_heads * np * (size_t)(head_dim + 2) * sizeof(float);
     }
     const int64_t group = num_q_heads / num_kv_heads;
-    return (size_t)balanced_wave_bound() * 2 * group * (size_t)(head_dim + 2) * sizeof(float);
+    return (size_t)balanced_wave_bound() * 2 * group * (size_t)(head_dim + 2) * sizeof(float) +
+           tile_prefix_bytes(num_seqs);
 }
 
 // Shared-prefix pass: the prefix keys are cut into at most kMaxPreSplits splits of a
@@ -120,6 +125,7 @@ pkv_status setup_balanced(DecodeArgs& a, int64_t resident, int32_t num_seqs, int
     a.num_waves = (int32_t)waves;
     a.part_o = static_cast<float*>(workspace);
     a.part_ml = a.part_o + (size_t)waves * 2 * group * head_dim;
+    a.tile_prefix = reinterpret_cast<int64_t*>(a.part_ml + (size_t)waves * 2 * group * 2);
     return PKV_OK;
 }
 
@@ -342,17 +348,21 @@ pkv_status paged_attention_decode(pkv_dtype dtype, void* out, const void* q, con
     if (num_q_heads % num_kv_heads) return PKV_ERR_SHAPE;
     const int group = num_q_heads / num_kv_heads;
     if (group > 8) return PKV_ERR_UNSUPPORTED;
-    if (partition_tokens < 0 || (partition_tokens % 64) != 0) return PKV_ERR_SHAPE;
+    if (partition_tokens < 0 || (partition_tokens % block_size) != 0) return PKV_ERR_SHAPE;
     if (!isfinite(scale)) return PKV_ERR_SHAPE;
     if (num_seqs == 0) return PKV_OK;
     if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PKV_ERR_NULL;
-    if ((int64_t)num_seqs * num_kv_heads > 65535) return PKV_ERR_UNSUPPORTED;  // grid.y
+    // output rows and (sequence, kv head) units are counted in 32-bit integers
+    if ((int64_t)num_seqs * num_q_heads > ((int64_t)1 << 30)) return PKV_ERR_UNSUPPORTED;
+    // fixed partitions: one grid row per partition (grid.y)
+    if (partition_tokens > 0 && num_partitions(max_context_len, partition_tokens) > 65535)
+        return PKV_ERR_UNSUPPORTED;
 
     const size_t need = decode_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                          max_context_len, partition_tokens);
     if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
 
-    DecodeArgs a;
+    DecodeArgs a{};
     a.out = out;
     a.q = q;
     a.k_pool = static_cast<const char*>(k_pool);
@@ -377,6 +387,7 @@ pkv_status paged_attention_decode(pkv_dtype dtype, void* out, const void* q, con
     a.pre_split_tokens = 64;
     a.part_o = static_cast<float*>(workspace);
     a.part_ml = nullptr;
+    a.tile_prefix = nullptr;
     if (partition_tokens > 0) {
         a.num_parts = num_partitions(max_context_len, partition_tokens);
         if (a.num_parts > 1)
@@ -446,12 +457,12 @@ pkv_status contiguous_attention_decode(pkv_dtype dtype, void* out, const void* q
     if (row_stride * 63 >= ((int64_t)1 << 31)) return PKV_ERR_UNSUPPORTED;  // 32-bit lane offsets
     if (num_seqs == 0) return PKV_OK;
     if (!out || !q || !k_cache || !v_cache || !context_lens) return PKV_ERR_NULL;
-    if ((int64_t)num_seqs * num_kv_heads > 65535) return PKV_ERR_UNSUPPORTED;
+    if ((int64_t)num_seqs * num_q_heads > ((int64_t)1 << 30)) return PKV_ERR_UNSUPPORTED;
     const size_t need = decode_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                          max_context_len, 0);
     if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
 
-    DecodeArgs a;
+    DecodeArgs a{};
     a.out = out;
     a.q = q;
     a.k_pool = static_cast<const char*>(k_cache);
@@ -492,7 +503,8 @@ size_t paged_attention_decode_multi_query_workspace_bytes(int32_t num_seqs, int3
         head_dim <= 0 || num_q_heads % num_kv_heads)
         return 0;
     const int64_t rows = (int64_t)(num_q_heads / num_kv_heads) * queries_per_seq;
-    return (size_t)balanced_wave_bound() * 2 * rows * (size_t)(head_dim + 2) * sizeof(float);
+    return (size_t)balanced_wave_bound() * 2 * rows * (size_t)(head_dim + 2) * sizeof(float) +
+           tile_prefix_bytes(num_seqs);
 }
 
 pkv_status paged_attention_decode_multi_query(
@@ -502,7 +514,7 @@ pkv_status paged_attention_decode_multi_query(
     int32_t num_seqs, int32_t queries_per_seq, int32_t max_context_len, int32_t num_q_heads,
     float scale, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     PoolGeom g;
-    const pkv_status st = check_geom(dtype, num_blocks, num_kv_heads, block_size, head_dim, &g);
+    const pkv_status st = check_geom(dtype, num_blocks, num_kv_heads, block_size, head_dim, &g, false);
     if (st != PKV_OK) return st;
     if (dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
     if (num_seqs < 0 || queries_per_seq <= 0 || max_context_len < 0 || max_blocks_per_seq <= 0 ||
@@ -520,7 +532,7 @@ pkv_status paged_attention_decode_multi_query(
         num_seqs, queries_per_seq, num_q_heads, num_kv_heads, head_dim);
     if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
 
-    DecodeArgs a;
+    DecodeArgs a{};
     a.out = out;
     a.q = q;
     a.k_pool = static_cast<const char*>(k_pool);
@@ -567,7 +579,7 @@ pkv_status paged_attention_decode_shared_prefix(
     const int32_t* group_prefix_lens, int32_t num_groups, int32_t max_group_seqs,
     int32_t max_prefix_len, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     PoolGeom g;
-    const pkv_status st = check_geom(dtype, num_blocks, num_kv_heads, block_size, head_dim, &g);
+    const pkv_status st = check_geom(dtype, num_blocks, num_kv_heads, block_size, head_dim, &g, false);
     if (st != PKV_OK) return st;
     if (dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
     if (num_seqs < 0 || max_context_len < 0 || max_blocks_per_seq <= 0 || num_q_heads <= 0 ||
@@ -582,7 +594,7 @@ pkv_status paged_attention_decode_shared_prefix(
     if (num_groups > 0 && (!seq_prefix_lens || !group_first_seq || !group_num_seqs ||
                            !group_prefix_lens))
         return PKV_ERR_NULL;
-    if ((int64_t)num_seqs * num_kv_heads > 65535) return PKV_ERR_UNSUPPORTED;
+    if ((int64_t)num_seqs * num_q_heads > ((int64_t)1 << 30)) return PKV_ERR_UNSUPPORTED;
     const size_t need = paged_attention_decode_shared_prefix_workspace_bytes(
         num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, max_prefix_len);
     if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
@@ -621,7 +633,7 @@ pkv_status paged_attention_decode_shared_prefix(
     if (e1 != hipSuccess) return launch_status(e1);
 
     // 2. every sequence's own tokens after its prefix, merged with the prefix states
-    DecodeArgs a;
+    DecodeArgs a{};
     a.out = out;
     a.q = q;
     a.k_pool = static_cast<const char*>(k_pool);
@@ -659,7 +671,7 @@ pkv_status paged_attention_prefill_chunk(pkv_dtype dtype, void* out, const void*
                                          int32_t num_q_heads, float scale, void* workspace,
                                          size_t workspace_bytes, hipStream_t stream) {
     PoolGeom g;
-    const pkv_status st = check_geom(dtype, num_blocks, num_kv_heads, block_size, head_dim, &g);
+    const pkv_status st = check_geom(dtype, num_blocks, num_kv_heads, block_size, head_dim, &g, false);
     if (st != PKV_OK) return st;
     if (dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
     if (num_chunks < 0 || max_q_len < 0 || max_context_len < 0 || max_blocks_per_seq <= 0 ||

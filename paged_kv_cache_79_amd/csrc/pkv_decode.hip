@@ -80,6 +80,9 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, int s, int h
     const uint32_t row_stride = CONTIG ? (uint32_t)a.contig_row_stride : (uint32_t)S::RB;
     const uint32_t lane_off = (uint32_t)ra * row_stride + (uint32_t)(rc * 16);
     const int32_t* table = CONTIG ? nullptr : a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+    // bf16, head_dim 64, block_size 4: a (block, head) run is 512 bytes, so one wave-wide
+    // load spans two blocks and each lane forms its own address
+    const bool small_run = !CONTIG && BF16 && D == 64 && bs * S::RB < 64 * 16;
     const int64_t head_base = CONTIG ? (int64_t)s * a.contig_seq_stride + (int64_t)h * S::RB
                                      : (int64_t)h * a.g.head_stride_bytes;
     const char* kb = (const char*)pin_uniform(a.k_pool + head_base);
@@ -124,6 +127,15 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, int s, int h
                 // row t0 + row of the sequence's slab (the slab holds a whole number of tiles)
                 const uint32_t ur = (uint32_t)(t0 + row);
                 base = ((uint64_t)__umulhi(ur, row_stride) << 32) | (uint64_t)(ur * row_stride);
+            } else if (small_run) {
+                const int lr = row + ra;                            // this lane's row of the tile
+                int pbl = __shfl(tab, lr >> a.g.log2_bs);
+                pbl = ((unsigned)pbl < (unsigned)a.g.num_blocks) ? pbl : 0;   // never a bad id
+                const uint64_t off = (uint64_t)(uint32_t)pbl * (uint64_t)a.g.block_stride_bytes +
+                                     (uint32_t)((lr & (bs - 1)) * S::RB + rc * 16);
+                kreg[i] = __builtin_nontemporal_load((global_ptr<u32x4>)(kb + off));
+                vreg[i] = __builtin_nontemporal_load((global_ptr<u32x4>)(vb + off));
+                continue;
             } else {
                 const int rel = row >> a.g.log2_bs;   // block of this load inside the tile
                 int pb = __builtin_amdgcn_readlane(tab, rel);
@@ -341,7 +353,7 @@ __global__ __launch_bounds__(64, (BF16 ? 2 : 1)) void decode_balanced_kernel(Dec
     // wave's range [wT/W, (w+1)T/W) is non-empty
     int64_t tiles_all, unused;
     int first[4];
-    count_tiles<PREFIX>(a, 0, tiles_all, unused, first);
+    count_tiles<PREFIX>(a, 0, tiles_all, unused, first, w);
     const int64_t T = tiles_all * Hkv;
     const int64_t W = min((int64_t)a.num_waves, T);
     if (w >= W) return;
@@ -398,33 +410,39 @@ __global__ __launch_bounds__(64, (BF16 ? 2 : 1)) void decode_balanced_kernel(Dec
     }
 }
 
-// Output rows (one wave each) per workgroup of the balanced merge.
+// Waves per workgroup of the balanced merge: one output row each, or (COOP) all of
+// them on one row, for batches with fewer rows than the device has merge slots.
 constexpr int kMergeRows = 4;
 
-// Merge the pieces of each (sequence, kv head) that straddles waves, one wave per
-// query head; write zero rows for empty contexts.  The first covering wave holds
-// its piece in its last slot, every later covering wave in its first slot.  In the
-// shared-prefix mode the prefix pass's states of the row are merged in as well,
-// together with the row's own-token state when one wave finished its (sequence, kv
-// head) (a row with no token after its prefix is the prefix states alone).
-// With nq queries per sequence (multi-query decode) the output row is
-// (s * nq + i) * Hq + hq, and a (sequence, kv head) has nq * G partial rows.
-template <bool BF16, int D, int G, bool PREFIX = false>
+// Merge the pieces of each (sequence, kv head) that straddles waves; write zero rows
+// for empty contexts.  The first covering wave holds its piece in its last slot, every
+// later covering wave in its first slot.  In the shared-prefix mode the prefix pass's
+// states of the row are merged in as well, together with the row's own-token state
+// when one wave finished its (sequence, kv head) (a row with no token after its prefix
+// is the prefix states alone).  With nq queries per sequence (multi-query decode) the
+// output row is (s * nq + i) * Hq + hq, and a (sequence, kv head) has nq * G partial
+// rows.  A row's place in the split comes from the tile offsets the attention kernel
+// recorded (tile_prefix), so locating it costs one load whatever the batch size.
+// COOP: the kMergeRows waves of a workgroup take turns over one row's states (wave i
+// takes batches i, i + kMergeRows, ...) and combine their sums through LDS, so a row
+// with many pieces (long contexts split over tens of waves) needs one round of loads
+// per kMergeRows batches instead of one per batch.
+template <bool BF16, int D, int G, bool PREFIX = false, bool COOP = false>
 __global__ __launch_bounds__(64 * kMergeRows) void decode_balanced_merge_kernel(DecodeArgs a,
                                                                                int nq) {
     constexpr int PER = D / 64;
+    constexpr int kBatch = 16;
     const int lane = threadIdx.x & 63;
+    const int wi = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int Hkv = a.g.num_kv_heads;
-    // kMergeRows rows per workgroup: the grid then starts 4x fewer workgroups
-    const int row = blockIdx.x * kMergeRows + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (row >= a.num_seqs * nq * a.num_q_heads) return;
+    const int row = COOP ? (int)blockIdx.x : (int)blockIdx.x * kMergeRows + wi;
+    if (row >= a.num_seqs * nq * a.num_q_heads) return;     // uniform per workgroup in COOP
     const int sq = row / a.num_q_heads;
     const int hq = row - sq * a.num_q_heads;
     const int s = sq / nq;
     const int h = hq / G;
     const int rows = nq * G, r = (sq - s * nq) * G + (hq - h * G);
-    int64_t tiles_all, before;
-    count_tiles<PREFIX>(a, s, tiles_all, before);
+    const int64_t before = a.tile_prefix[s], tiles_all = a.tile_prefix[a.num_seqs];
     const int ctx = clamp_ctx(a, a.context_lens[s]);
     const int start = seq_start<PREFIX>(a, s, ctx);
     const int nt = ntiles_of(ctx - start);
@@ -453,6 +471,7 @@ __global__ __launch_bounds__(64 * kMergeRows) void decode_balanced_merge_kernel(
     const int npre = ns + own;
     const int nst = npre + npieces;
     if (nst == 0) {
+        if (COOP && wi != 0) return;
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
             if constexpr (BF16)
@@ -479,12 +498,13 @@ __global__ __launch_bounds__(64 * kMergeRows) void decode_balanced_merge_kernel(
     // (max, sum) of state c0 + j while every lane loads its part of all the batch's
     // output rows (unconditionally, clamped to the batch); a running maximum rescales
     // what earlier batches accumulated, as in the online softmax
-    constexpr int kBatch = 16;
     float M = kNoMax, L = 0.f;                 // L: per-lane sum, reduced at the end
     float acc[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) acc[k] = 0.f;
-    for (int c0 = 0; c0 < nst; c0 += kBatch) {
+    const int first_batch = COOP ? wi * kBatch : 0;
+    const int batch_step = COOP ? kMergeRows * kBatch : kBatch;
+    for (int c0 = first_batch; c0 < nst; c0 += batch_step) {
         const int cnt = min(kBatch, nst - c0);
         float2 ml = make_float2(-INFINITY, 0.f);
         if (lane < cnt) {
@@ -517,6 +537,32 @@ __global__ __launch_bounds__(64 * kMergeRows) void decode_balanced_merge_kernel(
         }
     }
     L = wave_sum(L);
+    if constexpr (COOP) {
+        // the waves' partial sums, rescaled to the largest of their maxima
+        __shared__ float s_ml[kMergeRows][2];
+        __shared__ float s_acc[kMergeRows][D];
+        if (lane == 0) {
+            s_ml[wi][0] = M;
+            s_ml[wi][1] = L;
+        }
+#pragma unroll
+        for (int k = 0; k < PER; ++k) s_acc[wi][lane * PER + k] = acc[k];
+        __syncthreads();
+        if (wi != 0) return;
+        float Mt = s_ml[0][0];
+#pragma unroll
+        for (int i = 1; i < kMergeRows; ++i) Mt = fmaxf(Mt, s_ml[i][0]);
+        L = 0.f;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) acc[k] = 0.f;
+#pragma unroll
+        for (int i = 0; i < kMergeRows; ++i) {
+            const float c = fast_exp2(s_ml[i][0] - Mt);    // 0 for a wave that had no state
+            L = fmaf(s_ml[i][1], c, L);
+#pragma unroll
+            for (int k = 0; k < PER; ++k) acc[k] = fmaf(s_acc[i][lane * PER + k], c, acc[k]);
+        }
+    }
     const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
@@ -537,8 +583,8 @@ __global__ __launch_bounds__(64, (BF16 ? 2 : 1)) void decode_partition_kernel(De
     __shared__ __attribute__((aligned(16))) uint32_t lds_p[DecodeLds<BF16>::PWORDS];
     __shared__ __attribute__((aligned(16))) uint32_t lds_q[G * S::RB / 4];
 
-    const int part = blockIdx.x;
-    const int sh = blockIdx.y;
+    const int sh = blockIdx.x;
+    const int part = blockIdx.y;
     const int s = sh / a.g.num_kv_heads;
     const int h = sh - s * a.g.num_kv_heads;
     const int ctx = clamp_ctx(a, a.context_lens[s]);
@@ -600,8 +646,19 @@ __global__ __launch_bounds__(64) void decode_partition_merge_kernel(DecodeArgs a
 // --------------------------------------------------------------------------------------
 // host side
 // --------------------------------------------------------------------------------------
-// Workgroups of the balanced merge for `rows` output rows.
-static dim3 merge_grid(int64_t rows) { return dim3((unsigned)((rows + kMergeRows - 1) / kMergeRows)); }
+// The balanced merge over `rows` output rows: one row per wave, or, when the rows are
+// fewer than half the waves the split ran on (long contexts: each row has tens of
+// pieces), one row per workgroup whose waves share its pieces.
+template <bool BF16, int D, int G, bool PREFIX = false>
+static void launch_balanced_merge(const DecodeArgs& a, int64_t rows, int nq, hipStream_t st) {
+    if (rows * 2 < a.num_waves)
+        hipLaunchKernelGGL((decode_balanced_merge_kernel<BF16, D, G, PREFIX, true>),
+                           dim3((unsigned)rows), dim3(64 * kMergeRows), 0, st, a, nq);
+    else
+        hipLaunchKernelGGL((decode_balanced_merge_kernel<BF16, D, G, PREFIX, false>),
+                           dim3((unsigned)((rows + kMergeRows - 1) / kMergeRows)),
+                           dim3(64 * kMergeRows), 0, st, a, nq);
+}
 
 template <bool BF16, int D, int G, bool CONTIG = false, bool PREFIX = false>
 static int balanced_waves_t() {
@@ -628,7 +685,7 @@ template <bool BF16, int D, int G>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
     const int S = a.num_seqs;
     if (a.part_tokens > 0) {
-        const dim3 grid(a.num_parts, S * a.g.num_kv_heads);
+        const dim3 grid((unsigned)(S * a.g.num_kv_heads), (unsigned)a.num_parts);
         hipLaunchKernelGGL((decode_partition_kernel<BF16, D, G>), grid, dim3(64), 0, st, a);
         if (a.num_parts > 1)
             hipLaunchKernelGGL((decode_partition_merge_kernel<BF16, D>), dim3(S * a.num_q_heads),
@@ -636,8 +693,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
     } else {
         hipLaunchKernelGGL((decode_balanced_kernel<BF16, D, G>), dim3(a.num_waves), dim3(64), 0, st,
                            a);
-        hipLaunchKernelGGL((decode_balanced_merge_kernel<BF16, D, G>),
-                           merge_grid(S * a.num_q_heads), dim3(64 * kMergeRows), 0, st, a, 1);
+        launch_balanced_merge<BF16, D, G>(a, (int64_t)S * a.num_q_heads, 1, st);
     }
     return hipGetLastError();
 }
@@ -660,8 +716,7 @@ template <bool BF16, int D, int G>
 static hipError_t launch_contig_t(const DecodeArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((decode_balanced_kernel<true, D, G, true>), dim3(a.num_waves), dim3(64), 0,
                        st, a);
-    hipLaunchKernelGGL((decode_balanced_merge_kernel<true, D, G>),
-                       merge_grid(a.num_seqs * a.num_q_heads), dim3(64 * kMergeRows), 0, st, a, 1);
+    launch_balanced_merge<true, D, G>(a, (int64_t)a.num_seqs * a.num_q_heads, 1, st);
     return hipGetLastError();
 }
 template <bool BF16, int D, int G>
@@ -674,8 +729,7 @@ template <bool BF16, int D, int G>
 static hipError_t launch_prefix_decode_t(const DecodeArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((decode_balanced_kernel<true, D, G, false, true>), dim3(a.num_waves),
                        dim3(64), 0, st, a);
-    hipLaunchKernelGGL((decode_balanced_merge_kernel<true, D, G, true>),
-                       merge_grid(a.num_seqs * a.num_q_heads), dim3(64 * kMergeRows), 0, st, a, 1);
+    launch_balanced_merge<true, D, G, true>(a, (int64_t)a.num_seqs * a.num_q_heads, 1, st);
     return hipGetLastError();
 }
 template <bool BF16, int D, int G>
@@ -686,9 +740,7 @@ static int prefix_waves_t() {
 // the merge of the multi-query decode (bf16): nq * G partial rows per (sequence, kv head)
 template <bool BF16, int D, int G>
 static hipError_t launch_merge_mq_t(const DecodeArgs& a, int nq, hipStream_t st) {
-    hipLaunchKernelGGL((decode_balanced_merge_kernel<true, D, G>),
-                       merge_grid(a.num_seqs * nq * a.num_q_heads), dim3(64 * kMergeRows), 0, st, a,
-                       nq);
+    launch_balanced_merge<true, D, G>(a, (int64_t)a.num_seqs * nq * a.num_q_heads, nq, st);
     return hipGetLastError();
 }
 

@@ -269,7 +269,7 @@ __global__ __launch_bounds__(64, 2) void decode_mq_kernel(DecodeArgs a, int nq) 
 
     int64_t tiles_all, unused;
     int first[4];
-    count_tiles(a, 0, tiles_all, unused, first);
+    count_tiles(a, 0, tiles_all, unused, first, w);
     const int64_t T = tiles_all * Hkv;
     const int64_t W = min((int64_t)a.num_waves, T);
     if (w >= W) return;

@@ -65,6 +65,9 @@ struct DecodeArgs {
     // [num_waves][2][G][2].  (max in log2 units, sum of exponentials)
     float* part_o;
     float* part_ml;
+    // Balanced split: tiles of all sequences before sequence s at [s], the batch's total
+    // at [num_seqs] (written by the attention kernel, read by the merge).
+    int64_t* tile_prefix;
     PoolGeom g;
     int32_t num_seqs;
     int32_t num_q_heads;

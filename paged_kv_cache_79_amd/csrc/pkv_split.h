@@ -57,9 +57,12 @@ __device__ __forceinline__ int unit_tiles(const DecodeArgs& a, int s) {
 // Tiles of the whole batch (all sequences, one kv head) and tiles before sequence `upto`.
 // Four chunks of 64 sequences per pass, their loads issued together; the counts of
 // the first 256 sequences stay in first[q] (sequence 64q + lane) for locate_unit.
+// With a.tile_prefix set, the wave numbered `writer` records, for every pass it owns
+// (pass p belongs to wave p mod num_waves), each sequence's tiles before it, and wave 0
+// the batch's total at index num_seqs: the merge then finds a row's pieces in O(1).
 template <bool PREFIX = false>
 __device__ __forceinline__ void count_tiles(const DecodeArgs& a, int upto, int64_t& total,
-                                            int64_t& before, int (&first)[4]) {
+                                            int64_t& before, int (&first)[4], int64_t writer = -1) {
     const int lane = threadIdx.x & 63;   // lane of the wave (the merge runs several per workgroup)
     total = 0;
     before = 0;
@@ -74,6 +77,21 @@ __device__ __forceinline__ void count_tiles(const DecodeArgs& a, int upto, int64
 #pragma unroll
             for (int q = 0; q < 4; ++q) first[q] = nt[q];
         }
+        if (a.tile_prefix != nullptr && writer == (int64_t)(c0 >> 8) % a.num_waves) {
+            int64_t off = total;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                int incl = nt[q];
+#pragma unroll
+                for (int d = 1; d < 64; d <<= 1) {
+                    const int y = __shfl_up(incl, d);
+                    if (lane >= d) incl += y;
+                }
+                const int sl = c0 + q * 64 + lane;
+                if (sl < a.num_seqs) a.tile_prefix[sl] = off + (incl - nt[q]);
+                off += __builtin_amdgcn_readlane(incl, 63);
+            }
+        }
         int t = 0, u = 0;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -83,6 +101,7 @@ __device__ __forceinline__ void count_tiles(const DecodeArgs& a, int upto, int64
         total += wave_sum_int(t);
         before += wave_sum_int(u);
     }
+    if (a.tile_prefix != nullptr && writer == 0 && lane == 0) a.tile_prefix[a.num_seqs] = total;
 }
 template <bool PREFIX = false>
 __device__ __forceinline__ void count_tiles(const DecodeArgs& a, int upto, int64_t& total,

@@ -52,7 +52,8 @@ static void check_decode(const DecodeArgs& a, bool paged = true) {
     if (paged) check_geom(a.g);
     require(a.num_seqs > 0 && a.num_q_heads > 0, "decode sizes");
     require(a.part_tokens >= 0 && a.num_parts >= 1, "decode partitions");
-    require(a.part_tokens > 0 || (a.num_waves > 0 && a.part_o && a.part_ml), "balanced workspace");
+    require(a.part_tokens > 0 || (a.num_waves > 0 && a.part_o && a.part_ml && a.tile_prefix),
+            "balanced workspace");
 }
 hipError_t launch_decode(const DecodeArgs& a, bool, int, int group, int, hipStream_t) {
     check_decode(a);

@@ -42,6 +42,12 @@ def test_status_strings(lib):
     for code in range(9):
         assert pkv.status_string(code).startswith("PKV_")
     assert "UNKNOWN" in pkv.status_string(99)
+    # the numbering of the contract: VALIDATION = 7, then the block pool's NO_BLOCKS = 8
+    names = ["PKV_OK", "PKV_ERR_NULL", "PKV_ERR_SHAPE", "PKV_ERR_DTYPE", "PKV_ERR_UNSUPPORTED",
+             "PKV_ERR_WORKSPACE", "PKV_ERR_LAUNCH", "PKV_ERR_VALIDATION", "PKV_ERR_NO_BLOCKS"]
+    for code, name in enumerate(names):
+        assert pkv.status_string(code).split(":")[0] == name
+    assert (pkv.PKV_ERR_VALIDATION, pkv.PKV_ERR_NO_BLOCKS) == (7, 8)
 
 
 P = 0x1000  # a non-null dummy address; validation fails before it is ever used
@@ -73,7 +79,6 @@ def test_write_validation(lib):
     assert write(lib, d=96) == UNSUP
     assert write(lib, bs=12) == UNSUP
     assert write(lib, bs=64) == UNSUP
-    assert write(lib, bs=4, d=64) == UNSUP            # bf16 block run of 512 B < 1 KiB
     assert write(lib, nb=0) == SHAPE
     assert write(lib, hkv=262144, bs=32) == UNSUP      # one pool block of 2 GiB (bf16)
     assert write(lib, T=-1) == SHAPE
@@ -92,7 +97,12 @@ def test_copy_validation(lib):
 def test_decode_validation(lib):
     assert decode(lib, hq=9) == SHAPE                  # not a multiple of the kv heads
     assert decode(lib, hq=36, hkv=2) == UNSUP          # group of 18 heads
-    assert decode(lib, pt=100) == SHAPE                # partition not a multiple of 64
+    assert decode(lib, pt=100) == SHAPE                # partition not a multiple of block_size
+    assert decode(lib, pt=-16) == SHAPE
+    # a partition of one block is valid (it needs a workspace here: 4 partitions)
+    assert decode(lib, pt=16) == WS
+    # more than 65535 partitions of the longest context (one grid row each)
+    assert decode(lib, pt=16, maxctx=16 * 65536, mb=65536) == UNSUP
     assert decode(lib, scale=float("nan")) == SHAPE
     assert decode(lib, ptr=None) == NULL
     assert decode(lib, S=0, ptr=None) == OK
@@ -132,9 +142,11 @@ def test_workspace_sizes(lib):
     # fixed partitions: S * Hq * parts * (D + 2) floats, none when one partition suffices
     assert f(2, 8, 2, 128, 4096, 256) == 2 * 8 * 16 * 130 * 4
     assert f(2, 8, 2, 128, 200, 256) == 0
-    # balanced split: two partial slots of G heads per resident wave (8 per CU)
+    # balanced split: two partial slots of G heads per resident wave (8 per CU), and the
+    # tile offset of every sequence plus the batch total (int64)
     b = f(2, 8, 2, 128, 4096, 0)
-    assert b > 0 and b % (2 * 4 * 130 * 4) == 0
+    assert b > 0 and (b - 3 * 8) % (2 * 4 * 130 * 4) == 0
+    assert f(5, 8, 2, 128, 4096, 0) - b == 3 * 8
     assert f(0, 8, 2, 128, 4096, 0) == 0
 
 
@@ -173,6 +185,7 @@ def test_shared_prefix_validation(lib):
     assert shared(lib, dtype=7) == DTYPE
     assert shared(lib, dtype=0) == UNSUP               # the prefix pass is bf16 only
     assert shared(lib, d=96) == UNSUP
+    assert shared(lib, bs=4, d=64) == UNSUP            # bf16 runs of 512 B: matrix-core path
     assert shared(lib, hq=9) == SHAPE
     assert shared(lib, hq=36, hkv=2) == UNSUP          # group of 18 heads
     assert shared(lib, ngroups=-1) == SHAPE
@@ -210,6 +223,7 @@ def test_multi_query_validation(lib):
     assert mq(lib, dtype=7) == DTYPE
     assert mq(lib, dtype=0) == UNSUP                   # bf16 only
     assert mq(lib, d=96) == UNSUP
+    assert mq(lib, bs=4, d=64) == UNSUP                # bf16 runs of 512 B: matrix-core path
     assert mq(lib, n=0) == SHAPE
     assert mq(lib, hq=9) == SHAPE
     assert mq(lib, n=5) == UNSUP                       # 5 queries x 4 heads > 16 rows
@@ -224,9 +238,10 @@ def test_multi_query_validation(lib):
 
 def test_multi_query_workspace_sizes(lib):
     f = lib.paged_attention_decode_multi_query_workspace_bytes
-    # two partial slots of n * G rows per resident wave; n = 1 is decode's size
+    # two partial slots of n * G rows per resident wave, plus decode's tile offsets;
+    # n = 1 is decode's size
     assert f(2, 1, 8, 2, 128) == lib.paged_attention_decode_workspace_bytes(2, 8, 2, 128, 4096, 0)
-    assert f(2, 4, 8, 2, 128) == 4 * f(2, 1, 8, 2, 128)
+    assert f(2, 4, 8, 2, 128) - 3 * 8 == 4 * (f(2, 1, 8, 2, 128) - 3 * 8)
     assert f(0, 4, 8, 2, 128) == 0 and f(2, 0, 8, 2, 128) == 0
 
 

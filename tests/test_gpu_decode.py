@@ -38,7 +38,7 @@ def test_tiny_fp32_worked_example():
     check(W.tiny(), partition_tokens=64)
 
 
-@pytest.mark.parametrize("part", [0, 64, 128, 512, 8192])
+@pytest.mark.parametrize("part", [0, 16, 48, 64, 128, 512, 8192])
 def test_gqa_small_partitions(part):
     check(W.gqa(num_seqs=8), partition_tokens=part)
 
@@ -51,13 +51,16 @@ def test_group_sizes(g):
 
 
 @pytest.mark.parametrize("dtype,d,bs", [("bf16", 64, 16), ("bf16", 64, 32), ("bf16", 64, 8),
-                                        ("bf16", 128, 4), ("bf16", 128, 8), ("bf16", 128, 32),
-                                        ("f32", 64, 4), ("f32", 128, 4), ("f32", 128, 16),
-                                        ("f32", 64, 32)])
+                                        ("bf16", 64, 4), ("bf16", 128, 4), ("bf16", 128, 8),
+                                        ("bf16", 128, 32), ("f32", 64, 4), ("f32", 128, 4),
+                                        ("f32", 128, 16), ("f32", 64, 32)])
 def test_shapes(dtype, d, bs):
+    # bf16 / head_dim 64 / block_size 4 has 512-byte block runs: two blocks per wave load
     ctx = [1, 63, 64, 65, 130, 257, 600]
     check(batch(dtype, d, bs, 8, 2, ctx), partition_tokens=128)
     check(batch(dtype, d, bs, 8, 2, ctx), partition_tokens=0)
+    # partitions of a single block (the smallest split the contract allows)
+    check(batch(dtype, d, bs, 8, 2, ctx), partition_tokens=bs)
 
 
 def test_edge_lengths():
@@ -221,10 +224,11 @@ def test_many_sequences():
 
 
 @pytest.mark.parametrize("hkv,hq,d", [(4, 16, 64), (2, 16, 128)])
-def test_most_sequences_the_grid_allows(hkv, hq, d):
-    """num_seqs * num_kv_heads at the 65535 limit of the partitioned grid, contexts of
-    1..48 tokens; the balanced path on the same batch, every row compared."""
-    S = 65535 // hkv
+def test_more_units_than_a_grid_dimension(hkv, hq, d):
+    """num_seqs * num_kv_heads past 65535 (the largest grid.y), contexts of 1..48 tokens:
+    the balanced split (one wave per resident slot) and the partitioned grid (units along
+    grid.x) on the same batch, every row compared; sampled rows against the oracle."""
+    S = 70001 // hkv + 1
     rng = np.random.Generator(np.random.PCG64(43 + hkv))
     ctx = rng.integers(1, 48, size=S, endpoint=True)
     b = batch("bf16", d, 16, hq, hkv, ctx, seed=43 + hkv)
