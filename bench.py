@@ -265,7 +265,7 @@ def run_spec(args):
     import paged_kv_cache_79_amd as pkv
     import workloads as W
     log("building workload spec")
-    sb = W.spec_decode(poison=False, block_size=args.block_size)
+    sb = W.spec_decode(poison=False, block_size=args.block_size, draft=args.draft)
     pre = sb.prefill
     nq = sb.draft + 1
     pool_bytes = 2 * sb.k_pool.nbytes
@@ -659,6 +659,8 @@ def main():
                     help="pool block size of the gqa and long workloads")
     ap.add_argument("--shared-prefix", action="store_true",
                     help="prefix_cow: decode through the shared-prefix path (prefix read once)")
+    ap.add_argument("--draft", type=int, default=3,
+                    help="spec: draft tokens k per sequence (k + 1 queries each)")
     ap.add_argument("--spec-path", default="multi_query", choices=["multi_query", "prefill"],
                     help="spec: attention through the multi-query decode or chunked prefill")
     ap.add_argument("--no-prefill-split", action="store_true",

@@ -28,11 +28,13 @@
  *    beyond ceil(context_len / block_size) are never read.
  *  - A context length counts every token visible to the step's queries,
  *    including the ones written in this step.
- *  - Supported: head_dim in {64, 128}; block_size in {4, 8, 16, 32}; one pool
- *    block (all kv heads) smaller than 2 GiB; num_q_heads / num_kv_heads in 1..8.
- *    The matrix-core paths (multi-query decode, shared-prefix decode, chunked
- *    prefill) also need block_size * head_dim * element size >= 1024 bytes, which
- *    excludes bf16 with head_dim 64 and block_size 4 there (PKV_ERR_UNSUPPORTED).
+ *  - Supported by every entry point: bf16 and fp32; head_dim in {64, 128};
+ *    block_size in {4, 8, 16, 32}; one pool block (all kv heads) smaller than 2 GiB;
+ *    num_q_heads / num_kv_heads in 1..8.  The matrix-core kernels (chunked prefill,
+ *    multi-query decode, the shared-prefix pass) serve bf16 pools whose
+ *    (block, kv head) runs hold at least 1 KiB; other pools (fp32, and bf16 with
+ *    head_dim 64 and block_size 4) go through the decode's vector-unit arithmetic,
+ *    with the same results within the tolerance of their element type.
  *  - Host-checkable arguments are validated before anything is enqueued; a
  *    non-zero status means nothing was launched.  Device-resident contents
  *    (block ids, slots, lengths) are not validated; out-of-range block ids
@@ -204,8 +206,8 @@ pkv_status paged_attention_decode_noalloc(pkv_dtype dtype, void* out, const void
  *   workspace     as for paged_attention_decode with partition_tokens 0 (size from
  *                 paged_attention_decode_workspace_bytes(..., 0)); its contents need
  *                 no initialisation.
- * Errors: PKV_ERR_UNSUPPORTED for fp32 or head_dim not in {64, 128}; PKV_ERR_SHAPE for
- * max_len not a multiple of 64; otherwise as paged_attention_decode.
+ * bf16 or fp32.  Errors: PKV_ERR_UNSUPPORTED for head_dim not in {64, 128};
+ * PKV_ERR_SHAPE for max_len not a multiple of 64; otherwise as paged_attention_decode.
  */
 pkv_status contiguous_attention_decode(pkv_dtype dtype, void* out, const void* q,
                                        const void* k_cache, const void* v_cache, int32_t num_seqs,
@@ -223,14 +225,15 @@ pkv_status contiguous_attention_decode(pkv_dtype dtype, void* out, const void* q
  * of all n positions must already be in the cache (paged_kv_write earlier on the
  * stream), and n must not exceed a sequence's context.
  *
- *   out, q        [num_seqs * n][num_q_heads][head_dim] bf16 (query i of sequence s
- *                 is token s * n + i: the packed layout of paged_attention_prefill_chunk
+ *   out, q        [num_seqs * n][num_q_heads][head_dim] (query i of sequence s is
+ *                 token s * n + i: the packed layout of paged_attention_prefill_chunk
  *                 with every chunk of length n)
  *   other arguments as paged_attention_decode.
  *
  * The result equals paged_attention_prefill_chunk with cu_q_lens = 0, n, 2n, ...
- * Supported: bf16, (num_q_heads / num_kv_heads) * n <= 16 (the rows of one
- * matrix-core tile); otherwise PKV_ERR_UNSUPPORTED (use the prefill entry point).
+ * bf16 pools with (num_q_heads / num_kv_heads) * n <= 16 (the 16 columns of one
+ * matrix-core tile) run on the matrix cores; fp32, 512-byte block runs and wider row
+ * sets run query by query on the vector units (each query streams the keys it sees).
  * Workspace: paged_attention_decode_multi_query_workspace_bytes(); its contents need
  * no initialisation.
  */
@@ -264,8 +267,8 @@ pkv_status paged_attention_decode_multi_query(
  * max_group_seqs >= every group_num_seqs[g] and max_prefix_len >= every
  * group_prefix_lens[g] are host bounds (they size the prefix pass).  These device
  * contents are preconditions; violating them gives unspecified output but never an
- * out-of-range access.  bf16 only.  With num_groups == 0 this is
- * paged_attention_decode.
+ * out-of-range access.  With num_groups == 0, or a pool the matrix-core prefix pass
+ * does not serve (fp32, 512-byte block runs), this is paged_attention_decode.
  *
  * Workspace: paged_attention_decode_shared_prefix_workspace_bytes(); its contents
  * need no initialisation.
@@ -329,7 +332,9 @@ pkv_status pkv_validate(int32_t num_blocks, int32_t block_size, const int32_t* b
  *                 equal ranges and merged by log-sum-exp (the result is the same up to
  *                 rounding); without it every query tile is one workgroup.
  * The chunk's own K/V must already be in the cache (paged_kv_write earlier on the
- * stream).  bf16 only (PKV_ERR_UNSUPPORTED for fp32); runs on the matrix cores.
+ * stream).  bf16 pools with block runs of at least 1 KiB run on the matrix cores; fp32
+ * (and 512-byte runs) run query by query on the vector units with the decode's fp32
+ * arithmetic, one wave per (query, kv head), and use no workspace.
  * PKV_ERR_WORKSPACE if a workspace is given and is too small.
  */
 pkv_status paged_attention_prefill_chunk(pkv_dtype dtype, void* out, const void* q,

@@ -74,8 +74,11 @@ int64_t balanced_wave_bound() {
     return (int64_t)cus * 8;
 }
 
-// The balanced split's record of each sequence's first tile, read by the merge.
-size_t tile_prefix_bytes(int32_t num_seqs) { return ((size_t)num_seqs + 1) * sizeof(int64_t); }
+// The balanced split's record of each (sequence, kv head) unit for the merge: the wave
+// holding its first tile and the number of waves it spans.
+size_t unit_desc_bytes(int32_t num_seqs, int32_t num_kv_heads) {
+    return (size_t)num_seqs * num_kv_heads * 2 * sizeof(int32_t);
+}
 
 size_t decode_workspace(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                         int32_t head_dim, int32_t max_context_len, int32_t partition_tokens) {
@@ -89,7 +92,7 @@ size_t decode_workspace(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_he
     }
     const int64_t group = num_q_heads / num_kv_heads;
     return (size_t)balanced_wave_bound() * 2 * group * (size_t)(head_dim + 2) * sizeof(float) +
-           tile_prefix_bytes(num_seqs);
+           unit_desc_bytes(num_seqs, num_kv_heads);
 }
 
 // Shared-prefix pass: the prefix keys are cut into at most kMaxPreSplits splits of a
@@ -125,7 +128,7 @@ pkv_status setup_balanced(DecodeArgs& a, int64_t resident, int32_t num_seqs, int
     a.num_waves = (int32_t)waves;
     a.part_o = static_cast<float*>(workspace);
     a.part_ml = a.part_o + (size_t)waves * 2 * group * head_dim;
-    a.tile_prefix = reinterpret_cast<int64_t*>(a.part_ml + (size_t)waves * 2 * group * 2);
+    a.unit_desc = reinterpret_cast<int32_t*>(a.part_ml + (size_t)waves * 2 * group * 2);
     return PKV_OK;
 }
 
@@ -154,6 +157,48 @@ void* scratch_ptr() {
         g_scratch_ptr[dev] = ptr;
     }
     return g_scratch_ptr[dev];
+}
+
+// Whether the matrix-core kernels serve this pool: bf16 with block runs of at least one
+// wave-wide load (1 KiB).
+bool mfma_geometry(pkv_dtype dt, int32_t block_size, int32_t head_dim) {
+    return dt == PKV_BF16 && block_size * head_dim * 2 >= 1024;
+}
+
+// Causal query chunks on the vector units (fp32, or shapes no matrix-core kernel serves):
+// one wave per (query slot, kv head), each streaming the keys its query sees with the
+// decode's arithmetic.  cu_q_lens == nullptr: chunk c's queries are rows c * q_per_chunk..
+pkv_status launch_chunked(pkv_dtype dtype, void* out, const void* q, const int32_t* cu_q_lens,
+                          int32_t num_chunks, int32_t q_per_chunk, int32_t num_q_rows,
+                          const void* k_pool, const void* v_pool, const PoolGeom& g,
+                          int32_t head_dim, const int32_t* block_tables,
+                          int32_t max_blocks_per_seq, const int32_t* context_lens,
+                          int32_t max_context_len, int32_t num_q_heads, float scale,
+                          hipStream_t stream) {
+    const int64_t units = (int64_t)num_chunks * q_per_chunk;
+    if (product_exceeds(units, g.num_kv_heads, (int64_t)1 << 30) > ((int64_t)1 << 30) ||
+        product_exceeds(units, num_q_heads, (int64_t)1 << 30) > ((int64_t)1 << 30))
+        return PKV_ERR_UNSUPPORTED;
+    DecodeArgs a{};
+    a.out = out;
+    a.q = q;
+    a.k_pool = static_cast<const char*>(k_pool);
+    a.v_pool = static_cast<const char*>(v_pool);
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.g = g;
+    a.num_seqs = num_chunks;
+    a.num_q_heads = num_q_heads;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.max_context_len = max_context_len;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.part_tokens = std::max(max_context_len, 1);   // one partition: rows are written directly
+    a.num_parts = 1;
+    a.cu_q_lens = cu_q_lens;
+    a.q_per_chunk = q_per_chunk;
+    a.num_q_rows = num_q_rows;
+    return launch_status(launch_decode_chunked(a, dtype == PKV_BF16, head_dim,
+                                               num_q_heads / g.num_kv_heads, units, stream));
 }
 
 }  // namespace
@@ -387,7 +432,7 @@ pkv_status paged_attention_decode(pkv_dtype dtype, void* out, const void* q, con
     a.pre_split_tokens = 64;
     a.part_o = static_cast<float*>(workspace);
     a.part_ml = nullptr;
-    a.tile_prefix = nullptr;
+    a.unit_desc = nullptr;
     if (partition_tokens > 0) {
         a.num_parts = num_partitions(max_context_len, partition_tokens);
         if (a.num_parts > 1)
@@ -443,7 +488,6 @@ pkv_status contiguous_attention_decode(pkv_dtype dtype, void* out, const void* q
                                        int32_t num_q_heads, float scale, void* workspace,
                                        size_t workspace_bytes, hipStream_t stream) {
     if (dtype != PKV_F32 && dtype != PKV_BF16) return PKV_ERR_DTYPE;
-    if (dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
     if (num_seqs < 0 || max_len <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
         max_context_len < 0 || num_q_heads <= 0)
         return PKV_ERR_SHAPE;
@@ -453,7 +497,8 @@ pkv_status contiguous_attention_decode(pkv_dtype dtype, void* out, const void* q
     const int group = num_q_heads / num_kv_heads;
     if (group > 8) return PKV_ERR_UNSUPPORTED;
     if (!isfinite(scale)) return PKV_ERR_SHAPE;
-    const int64_t row_stride = (int64_t)num_kv_heads * head_dim * 2;
+    const int eb = elem_bytes(dtype);
+    const int64_t row_stride = (int64_t)num_kv_heads * head_dim * eb;
     if (row_stride * 63 >= ((int64_t)1 << 31)) return PKV_ERR_UNSUPPORTED;  // 32-bit lane offsets
     if (num_seqs == 0) return PKV_OK;
     if (!out || !q || !k_cache || !v_cache || !context_lens) return PKV_ERR_NULL;
@@ -470,8 +515,8 @@ pkv_status contiguous_attention_decode(pkv_dtype dtype, void* out, const void* q
     a.block_tables = nullptr;                                // no translation
     a.context_lens = context_lens;
     // a slab of max_len tokens seen as max_len / 64 blocks of 64 (bounds the lengths)
-    a.g.row_bytes = head_dim * 2;
-    a.g.head_stride_bytes = head_dim * 2;
+    a.g.row_bytes = head_dim * eb;
+    a.g.head_stride_bytes = head_dim * eb;
     a.g.block_stride_bytes = 64 * row_stride;
     a.g.num_blocks = max_len / 64;
     a.g.num_kv_heads = num_kv_heads;
@@ -490,10 +535,12 @@ pkv_status contiguous_attention_decode(pkv_dtype dtype, void* out, const void* q
     a.pre_o = a.pre_ml = nullptr;
     a.pre_splits = 0;
     a.pre_split_tokens = 64;
-    const pkv_status sb = setup_balanced(a, decode_contiguous_waves(head_dim, group), num_seqs,
-                                         num_kv_heads, head_dim, max_context_len, group, workspace);
+    const pkv_status sb = setup_balanced(a, decode_contiguous_waves(dtype == PKV_BF16, head_dim, group),
+                                         num_seqs, num_kv_heads, head_dim, max_context_len, group,
+                                         workspace);
     if (sb != PKV_OK) return sb;
-    return launch_status(launch_decode_contiguous(a, head_dim, group, num_seqs, stream));
+    return launch_status(
+        launch_decode_contiguous(a, dtype == PKV_BF16, head_dim, group, num_seqs, stream));
 }
 
 size_t paged_attention_decode_multi_query_workspace_bytes(int32_t num_seqs, int32_t queries_per_seq,
@@ -504,7 +551,7 @@ size_t paged_attention_decode_multi_query_workspace_bytes(int32_t num_seqs, int3
         return 0;
     const int64_t rows = (int64_t)(num_q_heads / num_kv_heads) * queries_per_seq;
     return (size_t)balanced_wave_bound() * 2 * rows * (size_t)(head_dim + 2) * sizeof(float) +
-           tile_prefix_bytes(num_seqs);
+           unit_desc_bytes(num_seqs, num_kv_heads);
 }
 
 pkv_status paged_attention_decode_multi_query(
@@ -514,15 +561,14 @@ pkv_status paged_attention_decode_multi_query(
     int32_t num_seqs, int32_t queries_per_seq, int32_t max_context_len, int32_t num_q_heads,
     float scale, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     PoolGeom g;
-    const pkv_status st = check_geom(dtype, num_blocks, num_kv_heads, block_size, head_dim, &g, false);
+    const pkv_status st = check_geom(dtype, num_blocks, num_kv_heads, block_size, head_dim, &g);
     if (st != PKV_OK) return st;
-    if (dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
     if (num_seqs < 0 || queries_per_seq <= 0 || max_context_len < 0 || max_blocks_per_seq <= 0 ||
         num_q_heads <= 0)
         return PKV_ERR_SHAPE;
     if (num_q_heads % num_kv_heads) return PKV_ERR_SHAPE;
     const int group = num_q_heads / num_kv_heads;
-    if (group > 8 || (int64_t)group * queries_per_seq > 16) return PKV_ERR_UNSUPPORTED;
+    if (group > 8) return PKV_ERR_UNSUPPORTED;
     if (!isfinite(scale)) return PKV_ERR_SHAPE;
     if (num_seqs == 0) return PKV_OK;
     if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PKV_ERR_NULL;
@@ -531,6 +577,14 @@ pkv_status paged_attention_decode_multi_query(
     const size_t need = paged_attention_decode_multi_query_workspace_bytes(
         num_seqs, queries_per_seq, num_q_heads, num_kv_heads, head_dim);
     if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+    // the matrix-core kernel packs the n * G rows of a (sequence, kv head) into one or two
+    // groups of 16 columns of its tiles; fp32, 512-byte block runs and wider row sets go
+    // query by query on the vector units
+    if (!mfma_geometry(dtype, block_size, head_dim) || (int64_t)group * queries_per_seq > 32)
+        return launch_chunked(dtype, out, q, nullptr, num_seqs, queries_per_seq,
+                              num_seqs * queries_per_seq, k_pool, v_pool, g, head_dim, block_tables,
+                              max_blocks_per_seq, context_lens, max_context_len, num_q_heads, scale,
+                              stream);
 
     DecodeArgs a{};
     a.out = out;
@@ -553,7 +607,7 @@ pkv_status paged_attention_decode_multi_query(
     a.pre_o = a.pre_ml = nullptr;
     a.pre_splits = 0;
     a.pre_split_tokens = 64;
-    const pkv_status sb = setup_balanced(a, decode_mq_waves(head_dim, group), num_seqs, num_kv_heads,
+    const pkv_status sb = setup_balanced(a, decode_mq_waves(head_dim, group, queries_per_seq), num_seqs, num_kv_heads,
                                          head_dim, max_context_len, group * queries_per_seq,
                                          workspace);
     if (sb != PKV_OK) return sb;
@@ -579,9 +633,8 @@ pkv_status paged_attention_decode_shared_prefix(
     const int32_t* group_prefix_lens, int32_t num_groups, int32_t max_group_seqs,
     int32_t max_prefix_len, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     PoolGeom g;
-    const pkv_status st = check_geom(dtype, num_blocks, num_kv_heads, block_size, head_dim, &g, false);
+    const pkv_status st = check_geom(dtype, num_blocks, num_kv_heads, block_size, head_dim, &g);
     if (st != PKV_OK) return st;
-    if (dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
     if (num_seqs < 0 || max_context_len < 0 || max_blocks_per_seq <= 0 || num_q_heads <= 0 ||
         num_groups < 0 || max_group_seqs < 0 || max_prefix_len < 0)
         return PKV_ERR_SHAPE;
@@ -598,7 +651,10 @@ pkv_status paged_attention_decode_shared_prefix(
     const size_t need = paged_attention_decode_shared_prefix_workspace_bytes(
         num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, max_prefix_len);
     if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
-    if (num_groups == 0 || max_group_seqs == 0 || max_prefix_len == 0)   // nothing shared
+    // nothing shared, or a pool the prefix pass (matrix cores) does not serve: plain
+    // decode over the same tables gives the result this call defines
+    if (num_groups == 0 || max_group_seqs == 0 || max_prefix_len == 0 ||
+        !mfma_geometry(dtype, block_size, head_dim))
         return paged_attention_decode(dtype, out, q, k_pool, v_pool, num_blocks, num_kv_heads,
                                       block_size, head_dim, block_tables, max_blocks_per_seq,
                                       context_lens, num_seqs, max_context_len, num_q_heads, scale,
@@ -671,9 +727,8 @@ pkv_status paged_attention_prefill_chunk(pkv_dtype dtype, void* out, const void*
                                          int32_t num_q_heads, float scale, void* workspace,
                                          size_t workspace_bytes, hipStream_t stream) {
     PoolGeom g;
-    const pkv_status st = check_geom(dtype, num_blocks, num_kv_heads, block_size, head_dim, &g, false);
+    const pkv_status st = check_geom(dtype, num_blocks, num_kv_heads, block_size, head_dim, &g);
     if (st != PKV_OK) return st;
-    if (dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
     if (num_chunks < 0 || max_q_len < 0 || max_context_len < 0 || max_blocks_per_seq <= 0 ||
         num_q_heads <= 0)
         return PKV_ERR_SHAPE;
@@ -688,6 +743,16 @@ pkv_status paged_attention_prefill_chunk(pkv_dtype dtype, void* out, const void*
     if (product_exceeds(product_exceeds(cdiv64(max_q_len, 128 / group), num_kv_heads, (int64_t)1 << 30),
                         num_chunks, (int64_t)1 << 30) > ((int64_t)1 << 30))
         return PKV_ERR_UNSUPPORTED;
+    if (workspace != nullptr) {
+        const size_t need = paged_attention_prefill_chunk_workspace_bytes(num_q_heads, num_kv_heads,
+                                                                          head_dim);
+        if (need > 0 && workspace_bytes < need) return PKV_ERR_WORKSPACE;
+    }
+    // fp32 and 512-byte block runs: query by query on the vector units (no workspace)
+    if (!mfma_geometry(dtype, block_size, head_dim))
+        return launch_chunked(dtype, out, q, cu_q_lens, num_chunks, max_q_len, INT32_MAX, k_pool,
+                              v_pool, g, head_dim, block_tables, max_blocks_per_seq, context_lens,
+                              max_context_len, num_q_heads, scale, stream);
 
     PrefillArgs a;
     a.out = out;

@@ -66,8 +66,10 @@ struct SegState {
 
 // Attend the G query heads of (s, h) to tokens [t_begin, t_end) of the sequence.
 // CONTIG: the unpaged baseline -- K/V in the contiguous [S][L][Hkv][D] layout, no table.
+// s picks the block-table row (or slab), s_q the query row (the same but for chunked
+// prefill, where the queries of one chunk share its table).
 template <bool BF16, int D, int G, bool CONTIG = false>
-__device__ __forceinline__ void attend_segment(const DecodeArgs& a, int s, int h, int ctx,
+__device__ __forceinline__ void attend_segment(const DecodeArgs& a, int s, int s_q, int h, int ctx,
                                                int t_begin, int t_end, char* lds_k,
                                                uint32_t* lds_p, uint32_t* lds_q,
                                                SegState<BF16, D, G>& st) {
@@ -92,7 +94,7 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, int s, int h
     __syncthreads();  // the previous segment is done with lds_q
     {
         const u32x4* qsrc = reinterpret_cast<const u32x4*>(
-            reinterpret_cast<const char*>(a.q) + ((int64_t)s * a.num_q_heads + h * G) * S::RB);
+            reinterpret_cast<const char*>(a.q) + ((int64_t)s_q * a.num_q_heads + h * G) * S::RB);
         u32x4* qdst = reinterpret_cast<u32x4*>(lds_q);
         for (int c = lane; c < G * S::RB / 16; c += 64) qdst[c] = qsrc[c];
     }
@@ -353,7 +355,7 @@ __global__ __launch_bounds__(64, (BF16 ? 2 : 1)) void decode_balanced_kernel(Dec
     // wave's range [wT/W, (w+1)T/W) is non-empty
     int64_t tiles_all, unused;
     int first[4];
-    count_tiles<PREFIX>(a, 0, tiles_all, unused, first, w);
+    count_tiles<PREFIX>(a, 0, tiles_all, unused, first);
     const int64_t T = tiles_all * Hkv;
     const int64_t W = min((int64_t)a.num_waves, T);
     if (w >= W) return;
@@ -373,9 +375,11 @@ __global__ __launch_bounds__(64, (BF16 ? 2 : 1)) void decode_balanced_kernel(Dec
         const int seg = (int)min((int64_t)(nt_s - tile), remaining);
         const int ctx = clamp_ctx(a, a.context_lens[s]);
         const int t_first = seq_start<PREFIX>(a, s, ctx);    // 0 unless in the prefix mode
-        attend_segment<BF16, D, G, CONTIG>(a, s, h, ctx, t_first + tile * kTile,
+        attend_segment<BF16, D, G, CONTIG>(a, s, s, h, ctx, t_first + tile * kTile,
                                            min(ctx, t_first + (tile + seg) * kTile), lds_k, lds_p,
                                            lds_q, st);
+        // the wave holding a unit's first tile tells the merge where its pieces are
+        if (tile == 0) record_unit(a, sp, w, s, h, e - remaining, nt_s, seg == nt_s);
         if (tile == 0 && seg == nt_s) {
             bool own = false;
             if constexpr (PREFIX) own = t_first > 0;
@@ -421,8 +425,8 @@ constexpr int kMergeRows = 4;
 // when one wave finished its (sequence, kv head) (a row with no token after its prefix
 // is the prefix states alone).  With nq queries per sequence (multi-query decode) the
 // output row is (s * nq + i) * Hq + hq, and a (sequence, kv head) has nq * G partial
-// rows.  A row's place in the split comes from the tile offsets the attention kernel
-// recorded (tile_prefix), so locating it costs one load whatever the batch size.
+// rows.  A row's pieces are located by the record the wave holding the unit's first
+// tile left (unit_desc): one load, whatever the batch size, and no split arithmetic.
 // COOP: the kMergeRows waves of a workgroup take turns over one row's states (wave i
 // takes batches i, i + kMergeRows, ...) and combine their sums through LDS, so a row
 // with many pieces (long contexts split over tens of waves) needs one round of loads
@@ -442,7 +446,7 @@ __global__ __launch_bounds__(64 * kMergeRows) void decode_balanced_merge_kernel(
     const int s = sq / nq;
     const int h = hq / G;
     const int rows = nq * G, r = (sq - s * nq) * G + (hq - h * G);
-    const int64_t before = a.tile_prefix[s], tiles_all = a.tile_prefix[a.num_seqs];
+    const int2 desc = *reinterpret_cast<const int2*>(a.unit_desc + 2 * ((int64_t)s * Hkv + h));
     const int ctx = clamp_ctx(a, a.context_lens[s]);
     const int start = seq_start<PREFIX>(a, s, ctx);
     const int nt = ntiles_of(ctx - start);
@@ -453,16 +457,15 @@ __global__ __launch_bounds__(64 * kMergeRows) void decode_balanced_merge_kernel(
     int64_t w0 = 0;
     int npieces = 0, own = 0;
     if (nt > 0) {
-        const int64_t T = tiles_all * Hkv, W = min((int64_t)a.num_waves, T);
-        const int64_t u0 = before * Hkv + (int64_t)h * nt;
-        const Split sp = make_split(a, T, W);
-        w0 = unit_owner(sp, u0);
-        const int64_t w1 = unit_owner(sp, u0 + nt - 1);
-        if (w0 == w1) {
+        // (wave holding the unit's first tile, waves its tiles span), recorded by that
+        // wave; clamped so that a stale record can never address past the workspace
+        w0 = min(max(desc.x, 0), a.num_waves - 1);
+        const int span = min(max(desc.y, 1), a.num_waves - (int)w0);
+        if (span == 1) {
             if (ns == 0) return;               // finished and written by one wave
             own = 1;                           // its state is in the row's last slot
         } else {
-            npieces = (int)(w1 - w0 + 1);
+            npieces = span;
         }
     }
     // The states of the row: in the shared-prefix mode its ns prefix splits and, when
@@ -576,7 +579,38 @@ __global__ __launch_bounds__(64 * kMergeRows) void decode_balanced_merge_kernel(
 // --------------------------------------------------------------------------------------
 // fixed partitions of part_tokens positions
 // --------------------------------------------------------------------------------------
-template <bool BF16, int D, int G>
+// Query row, block-table row and visible length of grid unit `sh`.  Decode: sequence
+// sh / Hkv, its table row, its context.  CHUNKED (causal queries of prefill chunks, or
+// of the multi-query decode when no matrix-core path serves the shape): slot v of
+// chunk c = v / q_per_chunk is query i = v mod q_per_chunk of the chunk if i < n_q; it
+// sits at position ctx_c - n_q + i and sees the keys up to it, through chunk c's table
+// row.  ok = false for slots past a chunk's queries.
+template <bool CHUNKED>
+__device__ __forceinline__ void unit_of(const DecodeArgs& a, int v, int& s_tab, int& s_q, int& ctx,
+                                        bool& ok) {
+    if constexpr (!CHUNKED) {
+        s_tab = s_q = v;
+        ctx = clamp_ctx(a, a.context_lens[v]);
+        ok = true;
+    } else {
+        const int c = v / a.q_per_chunk, i = v - c * a.q_per_chunk;
+        int q0, nq;
+        if (a.cu_q_lens != nullptr) {
+            q0 = a.cu_q_lens[c];
+            nq = a.cu_q_lens[c + 1] - q0;
+        } else {
+            q0 = c * a.q_per_chunk;
+            nq = a.q_per_chunk;
+        }
+        const int cc = clamp_ctx(a, a.context_lens[c]);
+        s_tab = c;
+        s_q = q0 + i;
+        ok = i < nq && s_q >= 0 && s_q < a.num_q_rows;
+        ctx = max(0, min(cc - nq + i + 1, cc));
+    }
+}
+
+template <bool BF16, int D, int G, bool CHUNKED = false>
 __global__ __launch_bounds__(64, (BF16 ? 2 : 1)) void decode_partition_kernel(DecodeArgs a) {
     using S = DecodeShape<BF16, D>;
     __shared__ __attribute__((aligned(16))) char lds_k[kTile * S::KPITCH];
@@ -585,22 +619,25 @@ __global__ __launch_bounds__(64, (BF16 ? 2 : 1)) void decode_partition_kernel(De
 
     const int sh = blockIdx.x;
     const int part = blockIdx.y;
-    const int s = sh / a.g.num_kv_heads;
-    const int h = sh - s * a.g.num_kv_heads;
-    const int ctx = clamp_ctx(a, a.context_lens[s]);
+    const int v = sh / a.g.num_kv_heads;
+    const int h = sh - v * a.g.num_kv_heads;
+    int s_tab, s_q, ctx;
+    bool ok;
+    unit_of<CHUNKED>(a, v, s_tab, s_q, ctx, ok);
+    if (!ok) return;
     const int t_begin = part * a.part_tokens;
     const bool single = a.num_parts == 1;
     if (t_begin >= ctx) {
-        if (single) zero_rows<BF16, D, G>(a, s, h);
+        if (single) zero_rows<BF16, D, G>(a, s_q, h);
         return;
     }
     SegState<BF16, D, G> st;
-    attend_segment<BF16, D, G>(a, s, h, ctx, t_begin, min(ctx, t_begin + a.part_tokens), lds_k,
-                               lds_p, lds_q, st);
+    attend_segment<BF16, D, G>(a, s_tab, s_q, h, ctx, t_begin, min(ctx, t_begin + a.part_tokens),
+                               lds_k, lds_p, lds_q, st);
     if (single)
-        write_rows<BF16, D, G>(a, s, h, st);
+        write_rows<BF16, D, G>(a, s_q, h, st);
     else
-        write_partial<BF16, D, G>(a, ((int64_t)s * a.num_q_heads + h * G) * a.num_parts + part,
+        write_partial<BF16, D, G>(a, ((int64_t)s_q * a.num_q_heads + h * G) * a.num_parts + part,
                                   a.num_parts, st);
 }
 
@@ -711,17 +748,42 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
         default: break;                            \
     }
 
-// the contiguous-layout (unpaged) baseline: bf16, balanced split
+// the contiguous-layout (unpaged) baseline: balanced split
 template <bool BF16, int D, int G>
 static hipError_t launch_contig_t(const DecodeArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((decode_balanced_kernel<true, D, G, true>), dim3(a.num_waves), dim3(64), 0,
+    hipLaunchKernelGGL((decode_balanced_kernel<BF16, D, G, true>), dim3(a.num_waves), dim3(64), 0,
                        st, a);
-    launch_balanced_merge<true, D, G>(a, (int64_t)a.num_seqs * a.num_q_heads, 1, st);
+    launch_balanced_merge<BF16, D, G>(a, (int64_t)a.num_seqs * a.num_q_heads, 1, st);
     return hipGetLastError();
 }
 template <bool BF16, int D, int G>
 static int contig_waves_t() {
-    return balanced_waves_t<true, D, G, true>();
+    return balanced_waves_t<BF16, D, G, true>();
+}
+
+// causal query chunks on the vector units: one single-partition wave per (query, kv head)
+template <bool BF16, int D, int G>
+static hipError_t launch_chunked_t(const DecodeArgs& a, int64_t units, hipStream_t st) {
+    hipLaunchKernelGGL((decode_partition_kernel<BF16, D, G, true>),
+                       dim3((unsigned)(units * a.g.num_kv_heads), 1u), dim3(64), 0, st, a);
+    return hipGetLastError();
+}
+template <bool BF16, int D>
+static hipError_t launch_chunked_g(const DecodeArgs& a, int group, int64_t units, hipStream_t st) {
+    PKV_DISPATCH_G(launch_chunked_t, BF16, D, group, a, units, st)
+    return hipErrorInvalidValue;
+}
+hipError_t launch_decode_chunked(const DecodeArgs& a, bool is_bf16, int head_dim, int group,
+                                 int64_t units, hipStream_t st) {
+    if (units == 0) return hipSuccess;
+    if (is_bf16) {
+        if (head_dim == 128) return launch_chunked_g<true, 128>(a, group, units, st);
+        if (head_dim == 64) return launch_chunked_g<true, 64>(a, group, units, st);
+    } else {
+        if (head_dim == 128) return launch_chunked_g<false, 128>(a, group, units, st);
+        if (head_dim == 64) return launch_chunked_g<false, 64>(a, group, units, st);
+    }
+    return hipErrorInvalidValue;
 }
 
 // the shared-prefix mode: bf16, balanced split over the tokens after each prefix
@@ -777,17 +839,27 @@ hipError_t launch_decode_prefix(const DecodeArgs& a, int head_dim, int group, in
     return hipErrorInvalidValue;
 }
 
-int decode_contiguous_waves(int head_dim, int group) {
-    if (head_dim == 128) { PKV_DISPATCH_G(contig_waves_t, true, 128, group) }
-    if (head_dim == 64) { PKV_DISPATCH_G(contig_waves_t, true, 64, group) }
+int decode_contiguous_waves(bool is_bf16, int head_dim, int group) {
+    if (is_bf16) {
+        if (head_dim == 128) { PKV_DISPATCH_G(contig_waves_t, true, 128, group) }
+        if (head_dim == 64) { PKV_DISPATCH_G(contig_waves_t, true, 64, group) }
+    } else {
+        if (head_dim == 128) { PKV_DISPATCH_G(contig_waves_t, false, 128, group) }
+        if (head_dim == 64) { PKV_DISPATCH_G(contig_waves_t, false, 64, group) }
+    }
     return 0;
 }
 
-hipError_t launch_decode_contiguous(const DecodeArgs& a, int head_dim, int group, int num_seqs,
-                                    hipStream_t st) {
+hipError_t launch_decode_contiguous(const DecodeArgs& a, bool is_bf16, int head_dim, int group,
+                                    int num_seqs, hipStream_t st) {
     if (num_seqs == 0) return hipSuccess;
-    if (head_dim == 128) { PKV_DISPATCH_G(launch_contig_t, true, 128, group, a, st) }
-    if (head_dim == 64) { PKV_DISPATCH_G(launch_contig_t, true, 64, group, a, st) }
+    if (is_bf16) {
+        if (head_dim == 128) { PKV_DISPATCH_G(launch_contig_t, true, 128, group, a, st) }
+        if (head_dim == 64) { PKV_DISPATCH_G(launch_contig_t, true, 64, group, a, st) }
+    } else {
+        if (head_dim == 128) { PKV_DISPATCH_G(launch_contig_t, false, 128, group, a, st) }
+        if (head_dim == 64) { PKV_DISPATCH_G(launch_contig_t, false, 64, group, a, st) }
+    }
     return hipErrorInvalidValue;
 }
 

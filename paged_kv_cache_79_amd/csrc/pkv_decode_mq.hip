@@ -37,7 +37,7 @@ struct MqShape {
     static constexpr int CPR = RB / 16;              // 16-byte chunks per row
     static constexpr int VJ = CPR / 8;               // chunks per key per lane in the V load
     static constexpr int VPITCH = kTile * 2 + 16;    // bytes of a V^T row in LDS
-    static constexpr int ROWS = 16;                  // MFMA columns: query rows per wave
+    static constexpr int ROWS = 16;                  // MFMA columns: query rows per column group
 };
 
 // Slot of key kk (0..63) in the V^T tile.  Within a group of 32 keys, the S^T
@@ -55,10 +55,13 @@ __device__ __forceinline__ int mq_vt_off(int d, int g) {
     return d * MqShape<D>::VPITCH + ((g ^ ((d >> 3) & 7)) << 4);
 }
 
-template <int D>
+// NC groups of 16 rows: the 16 columns of the matrix tiles hold rows n (NC = 1) or
+// n and 16 + n (NC = 2, up to 32 rows: 8 queries x 4 heads), sharing every K and V^T
+// operand read.
+template <int D, int NC>
 struct MqState {
-    floatx4_t o[MqShape<D>::DT];   // O^T of this lane's row n: d = 16 dt + 4q + j
-    float m, l;                    // running max (log2 units) and sum of the row
+    floatx4_t o[NC][MqShape<D>::DT];   // O^T of this lane's row: d = 16 dt + 4q + j
+    float m[NC], l[NC];                // running max (log2 units) and sum of the row
 };
 
 __device__ __forceinline__ floatx4_t mfma16(u32x4 a, u32x4 b, floatx4_t c) {
@@ -67,10 +70,10 @@ __device__ __forceinline__ floatx4_t mfma16(u32x4 a, u32x4 b, floatx4_t c) {
 }
 
 // Attend the nq * G rows of (s, h) to keys [t_begin, t_end) of the sequence.
-template <int D, int G>
+template <int D, int G, int NC>
 __device__ __forceinline__ void attend_mq(const DecodeArgs& a, int s, int h, int ctx, int nq,
                                           int t_begin, int t_end, char* lds_vt,
-                                          MqState<D>& st) {
+                                          MqState<D, NC>& st) {
     using P = MqShape<D>;
     const int lane = threadIdx.x;
     const int n = lane & 15, q = lane >> 4;
@@ -82,24 +85,33 @@ __device__ __forceinline__ void attend_mq(const DecodeArgs& a, int s, int h, int
     const char* vb = a.v_pool + (int64_t)h * a.g.head_stride_bytes;
     const uint64_t bstride = (uint64_t)a.g.block_stride_bytes;
 
-    // Q^T: column n is row (query qi, head h*G + hh); padding columns are zero
-    const bool live = n < rows;
-    const int qi = live ? n / G : nq - 1;
-    const int hh = live ? n - (n / G) * G : 0;
-    u32x4 qreg[P::KC];
-    {
+    // Q^T: column n of group cg is row r = 16 cg + n = (query qi, head h*G + hh);
+    // padding columns are zero
+    u32x4 qreg[NC][P::KC];
+    int lim[NC];                       // last key each of this lane's rows sees
+#pragma unroll
+    for (int cg = 0; cg < NC; ++cg) {
+        const int r = 16 * cg + n;
+        const bool live = r < rows;
+        const int qi = live ? r / G : nq - 1;
+        const int hh = live ? r - (r / G) * G : 0;
         const char* qp = reinterpret_cast<const char*>(a.q) +
                          (((int64_t)s * nq + qi) * a.num_q_heads + h * G + hh) * P::RB + q * 16;
 #pragma unroll
         for (int c = 0; c < P::KC; ++c)
-            qreg[c] = live ? *reinterpret_cast<const u32x4*>(qp + c * 64) : u32x4{0u, 0u, 0u, 0u};
+            qreg[cg][c] = live ? *reinterpret_cast<const u32x4*>(qp + c * 64) : u32x4{0u, 0u, 0u, 0u};
+        lim[cg] = ctx - nq + qi;
     }
-    const int lim = ctx - nq + qi;     // last key this row sees
 
-    float m = kNoMax, l = 0.f;
-    floatx4_t o[P::DT];
+    float m[NC], l[NC];
+    floatx4_t o[NC][P::DT];
 #pragma unroll
-    for (int dt = 0; dt < P::DT; ++dt) o[dt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    for (int cg = 0; cg < NC; ++cg) {
+        m[cg] = kNoMax;
+        l[cg] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < P::DT; ++dt) o[cg][dt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    }
     const float sl2 = a.scale_log2;
     const int kp = lane >> 3, c0 = lane & 7;
 
@@ -138,50 +150,56 @@ __device__ __forceinline__ void attend_mq(const DecodeArgs& a, int s, int h, int
             }
         tab_cur = load_tile_table(table, t0 + kTile, lbs, nblk, lane);
 
-        // ---- S^T = K Q^T: lane holds keys t0 + 16mt + 4q + j of row n -----------------
-        floatx4_t sacc[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            sacc[mt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int c = 0; c < P::KC; ++c) sacc[mt] = mfma16(kreg[mt][c], qreg[c], sacc[mt]);
-        }
-
-        // ---- online softmax over the row's 64 keys (4 lanes x 16) ---------------------
-        const bool full = t0 + kTile - 1 <= ctx - nq;    // every key visible to every row
-        float mx = -INFINITY;
+        // ---- S^T = K Q^T: lane holds keys t0 + 16mt + 4q + j of its rows --------------
+        floatx4_t sacc[NC][4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int key = t0 + 16 * mt + 4 * q + j;
-                const float sc = (full || key <= lim) ? sacc[mt][j] * sl2 : -INFINITY;
-                sacc[mt][j] = sc;
-                mx = fmaxf(mx, sc);
+            for (int cg = 0; cg < NC; ++cg) {
+                sacc[cg][mt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < P::KC; ++c)
+                    sacc[cg][mt] = mfma16(kreg[mt][c], qreg[cg][c], sacc[cg][mt]);
             }
-        mx = swap32_max(swap16_max(mx));
-        const float mn = fmaxf(m, mx);
-        const float alpha = fast_exp2(m - mn);
-        m = mn;
-        float ps = 0.f;
-        u32x4 pk[2];
+
+        // ---- online softmax over each row's 64 keys (4 lanes x 16) -------------------
+        const bool full = t0 + kTile - 1 <= ctx - nq;    // every key visible to every row
+        u32x4 pk[NC][2];
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            float p[2][4];
+        for (int cg = 0; cg < NC; ++cg) {
+            float mx = -INFINITY;
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
+            for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    p[u][j] = fast_exp2(sacc[2 * s2 + u][j] - mn);
-                    ps += p[u][j];
+                    const int key = t0 + 16 * mt + 4 * q + j;
+                    const float sc = (full || key <= lim[cg]) ? sacc[cg][mt][j] * sl2 : -INFINITY;
+                    sacc[cg][mt][j] = sc;
+                    mx = fmaxf(mx, sc);
                 }
-            pk[s2] = u32x4{pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3]),
-                           pack_bf16(p[1][0], p[1][1]), pack_bf16(p[1][2], p[1][3])};
-        }
-        l = fmaf(l, alpha, ps);
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+            mx = swap32_max(swap16_max(mx));
+            const float mn = fmaxf(m[cg], mx);
+            const float alpha = fast_exp2(m[cg] - mn);
+            m[cg] = mn;
+            float ps = 0.f;
 #pragma unroll
-            for (int dt = 0; dt < P::DT; ++dt) o[dt] *= alpha;
+            for (int s2 = 0; s2 < 2; ++s2) {
+                float p[2][4];
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        p[u][j] = fast_exp2(sacc[cg][2 * s2 + u][j] - mn);
+                        ps += p[u][j];
+                    }
+                pk[cg][s2] = u32x4{pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3]),
+                                   pack_bf16(p[1][0], p[1][1]), pack_bf16(p[1][2], p[1][3])};
+            }
+            l[cg] = fmaf(l[cg], alpha, ps);
+            if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+                for (int dt = 0; dt < P::DT; ++dt) o[cg][dt] *= alpha;
+            }
         }
 
         // ---- V^T into LDS: keys 2m, 2m+1 share a dword of each V^T row ----------------
@@ -208,60 +226,75 @@ __device__ __forceinline__ void attend_mq(const DecodeArgs& a, int s, int h, int
         }
         __syncthreads();
 
-        // ---- O^T += V^T P^T ----------------------------------------------------------
+        // ---- O^T += V^T P^T (each V^T operand serves every column group) ---------------
 #pragma unroll
         for (int dt = 0; dt < P::DT; ++dt)
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
                 const u32x4 va = *reinterpret_cast<const u32x4*>(
                     lds_vt + mq_vt_off<D>(dt * 16 + n, 4 * s2 + q));
-                o[dt] = mfma16(va, pk[s2], o[dt]);
+#pragma unroll
+                for (int cg = 0; cg < NC; ++cg) o[cg][dt] = mfma16(va, pk[cg][s2], o[cg][dt]);
             }
     }
 #pragma unroll
-    for (int dt = 0; dt < P::DT; ++dt) st.o[dt] = o[dt];
-    st.m = m;
-    st.l = swap32_sum(swap16_sum(l));
+    for (int cg = 0; cg < NC; ++cg) {
+#pragma unroll
+        for (int dt = 0; dt < P::DT; ++dt) st.o[cg][dt] = o[cg][dt];
+        st.m[cg] = m[cg];
+        st.l[cg] = swap32_sum(swap16_sum(l[cg]));
+    }
 }
 
-// Normalised rows of a finished (s, h): lane 16q + n writes d = 16dt + 4q .. +3 of row n.
-template <int D, int G>
+// Normalised rows of a finished (s, h): lane 16q + n writes d = 16dt + 4q .. +3 of rows
+// 16 cg + n.
+template <int D, int G, int NC>
 __device__ __forceinline__ void write_mq_rows(const DecodeArgs& a, int s, int h, int nq,
-                                              const MqState<D>& st) {
+                                              const MqState<D, NC>& st) {
     using P = MqShape<D>;
     const int lane = threadIdx.x;
     const int n = lane & 15, q = lane >> 4;
-    if (n >= nq * G) return;
-    const int qi = n / G, hh = n - (n / G) * G;
-    const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
-    uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) +
-                    (((int64_t)s * nq + qi) * a.num_q_heads + h * G + hh) * D + q * 4;
 #pragma unroll
-    for (int dt = 0; dt < P::DT; ++dt)
-        *reinterpret_cast<u32x2*>(dst + dt * 16) =
-            u32x2{pack_bf16(st.o[dt][0] * inv, st.o[dt][1] * inv),
-                  pack_bf16(st.o[dt][2] * inv, st.o[dt][3] * inv)};
+    for (int cg = 0; cg < NC; ++cg) {
+        const int r = 16 * cg + n;
+        if (r >= nq * G) continue;
+        const int qi = r / G, hh = r - (r / G) * G;
+        const float inv = st.l[cg] > 0.f ? 1.f / st.l[cg] : 0.f;
+        uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) +
+                        (((int64_t)s * nq + qi) * a.num_q_heads + h * G + hh) * D + q * 4;
+#pragma unroll
+        for (int dt = 0; dt < P::DT; ++dt)
+            *reinterpret_cast<u32x2*>(dst + dt * 16) =
+                u32x2{pack_bf16(st.o[cg][dt][0] * inv, st.o[cg][dt][1] * inv),
+                      pack_bf16(st.o[cg][dt][2] * inv, st.o[cg][dt][3] * inv)};
+    }
 }
 
-// Unnormalised state of row n into partial row prow0 + n.
-template <int D, int G>
+// Unnormalised state of row r into partial row prow0 + r.
+template <int D, int G, int NC>
 __device__ __forceinline__ void write_mq_partial(const DecodeArgs& a, int64_t prow0, int nq,
-                                                 const MqState<D>& st) {
+                                                 const MqState<D, NC>& st) {
     using P = MqShape<D>;
     const int lane = threadIdx.x;
     const int n = lane & 15, q = lane >> 4;
-    if (n >= nq * G) return;
-    const int64_t prow = prow0 + n;
-    float* dst = a.part_o + prow * D + q * 4;
 #pragma unroll
-    for (int dt = 0; dt < P::DT; ++dt)
-        *reinterpret_cast<float4*>(dst + dt * 16) =
-            make_float4(st.o[dt][0], st.o[dt][1], st.o[dt][2], st.o[dt][3]);
-    if (q == 0) *reinterpret_cast<float2*>(a.part_ml + prow * 2) = make_float2(st.m, st.l);
+    for (int cg = 0; cg < NC; ++cg) {
+        const int r = 16 * cg + n;
+        if (r >= nq * G) continue;
+        const int64_t prow = prow0 + r;
+        float* dst = a.part_o + prow * D + q * 4;
+#pragma unroll
+        for (int dt = 0; dt < P::DT; ++dt)
+            *reinterpret_cast<float4*>(dst + dt * 16) =
+                make_float4(st.o[cg][dt][0], st.o[cg][dt][1], st.o[cg][dt][2], st.o[cg][dt][3]);
+        if (q == 0)
+            *reinterpret_cast<float2*>(a.part_ml + prow * 2) = make_float2(st.m[cg], st.l[cg]);
+    }
 }
 
-template <int D, int G>
-__global__ __launch_bounds__(64, 2) void decode_mq_kernel(DecodeArgs a, int nq) {
+// NC = 1: two waves per SIMD; NC = 2 doubles the accumulators and runs one wave per SIMD.
+template <int D, int G, int NC>
+__global__ __launch_bounds__(64, 3 - NC) void decode_mq_kernel(DecodeArgs a, int nq) {
     __shared__ __attribute__((aligned(16))) char lds_vt[D * MqShape<D>::VPITCH];
     const int64_t w = blockIdx.x;
     const int Hkv = a.g.num_kv_heads;
@@ -269,7 +302,7 @@ __global__ __launch_bounds__(64, 2) void decode_mq_kernel(DecodeArgs a, int nq) 
 
     int64_t tiles_all, unused;
     int first[4];
-    count_tiles(a, 0, tiles_all, unused, first, w);
+    count_tiles(a, 0, tiles_all, unused, first);
     const int64_t T = tiles_all * Hkv;
     const int64_t W = min((int64_t)a.num_waves, T);
     if (w >= W) return;
@@ -284,18 +317,19 @@ __global__ __launch_bounds__(64, 2) void decode_mq_kernel(DecodeArgs a, int nq) 
     int h = (int)(rel / nt_s);
     int tile = (int)(rel - (int64_t)h * nt_s);
     int64_t remaining = e - b;
-    MqState<D> st;
+    MqState<D, NC> st;
     while (remaining > 0) {
         const int seg = (int)min((int64_t)(nt_s - tile), remaining);
         const int ctx = clamp_ctx(a, a.context_lens[s]);
-        attend_mq<D, G>(a, s, h, ctx, nq, tile * kTile, min(ctx, (tile + seg) * kTile), lds_vt,
-                        st);
+        attend_mq<D, G, NC>(a, s, h, ctx, nq, tile * kTile, min(ctx, (tile + seg) * kTile), lds_vt,
+                            st);
+        if (tile == 0) record_unit(a, sp, w, s, h, e - remaining, nt_s, seg == nt_s);
         if (tile == 0 && seg == nt_s) {
-            write_mq_rows<D, G>(a, s, h, nq, st);
+            write_mq_rows<D, G, NC>(a, s, h, nq, st);
         } else {
             // slot 1 for a piece that starts the unit, slot 0 for one that starts inside
             // it (the merge's reading order, as for decode)
-            write_mq_partial<D, G>(a, (w * 2 + (tile == 0 ? 1 : 0)) * rows, nq, st);
+            write_mq_partial<D, G, NC>(a, (w * 2 + (tile == 0 ? 1 : 0)) * rows, nq, st);
         }
         remaining -= seg;
         if (remaining > 0) {
@@ -314,8 +348,8 @@ __global__ __launch_bounds__(64, 2) void decode_mq_kernel(DecodeArgs a, int nq) 
 // --------------------------------------------------------------------------------------
 // host side
 // --------------------------------------------------------------------------------------
-template <int D, int G>
-static int mq_waves_t() {
+template <int D, int G, int NC>
+static int mq_waves_nc() {
     static std::mutex mu;
     static int cache[64] = {0};
     int dev = 0;
@@ -324,7 +358,7 @@ static int mq_waves_t() {
     if (cache[dev] == 0) {
         int per_cu = 0, cus = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per_cu, reinterpret_cast<const void*>(decode_mq_kernel<D, G>), 64, 0) !=
+                &per_cu, reinterpret_cast<const void*>(decode_mq_kernel<D, G, NC>), 64, 0) !=
                 hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return 0;
@@ -332,10 +366,18 @@ static int mq_waves_t() {
     }
     return cache[dev];
 }
+// resident waves of the kernel that serves nq queries of G heads
+template <int D, int G>
+static int mq_waves_t(int nq) {
+    return nq * G <= MqShape<D>::ROWS ? mq_waves_nc<D, G, 1>() : mq_waves_nc<D, G, 2>();
+}
 
 template <int D, int G>
 static hipError_t launch_mq_t(const DecodeArgs& a, int nq, hipStream_t st) {
-    hipLaunchKernelGGL((decode_mq_kernel<D, G>), dim3(a.num_waves), dim3(64), 0, st, a, nq);
+    if (nq * G <= MqShape<D>::ROWS)
+        hipLaunchKernelGGL((decode_mq_kernel<D, G, 1>), dim3(a.num_waves), dim3(64), 0, st, a, nq);
+    else
+        hipLaunchKernelGGL((decode_mq_kernel<D, G, 2>), dim3(a.num_waves), dim3(64), 0, st, a, nq);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_balanced_merge_mq(a, D, G, nq, st);
@@ -354,16 +396,16 @@ static hipError_t launch_mq_t(const DecodeArgs& a, int nq, hipStream_t st) {
         default: break;                        \
     }
 
-int decode_mq_waves(int head_dim, int group) {
-    if (head_dim == 128) { PKV_MQ_DISPATCH(mq_waves_t, 128, group) }
-    if (head_dim == 64) { PKV_MQ_DISPATCH(mq_waves_t, 64, group) }
+int decode_mq_waves(int head_dim, int group, int nq) {
+    if (head_dim == 128) { PKV_MQ_DISPATCH(mq_waves_t, 128, group, nq) }
+    if (head_dim == 64) { PKV_MQ_DISPATCH(mq_waves_t, 64, group, nq) }
     return 0;
 }
 
 hipError_t launch_decode_mq(const DecodeArgs& a, int head_dim, int group, int nq, int num_seqs,
                             hipStream_t st) {
     if (num_seqs == 0) return hipSuccess;
-    if (nq < 1 || nq * group > MqShape<128>::ROWS) return hipErrorInvalidValue;
+    if (nq < 1 || nq * group > 2 * MqShape<128>::ROWS) return hipErrorInvalidValue;
     if (head_dim == 128) { PKV_MQ_DISPATCH(launch_mq_t, 128, group, a, nq, st) }
     if (head_dim == 64) { PKV_MQ_DISPATCH(launch_mq_t, 64, group, a, nq, st) }
     return hipErrorInvalidValue;

@@ -65,9 +65,10 @@ struct DecodeArgs {
     // [num_waves][2][G][2].  (max in log2 units, sum of exponentials)
     float* part_o;
     float* part_ml;
-    // Balanced split: tiles of all sequences before sequence s at [s], the batch's total
-    // at [num_seqs] (written by the attention kernel, read by the merge).
-    int64_t* tile_prefix;
+    // Balanced split: for unit (s, h) at [2 (s Hkv + h)], the wave holding its first
+    // tile and the number of waves its tiles span (written by that wave, read by the
+    // merge; units without tiles are not written).
+    int32_t* unit_desc;
     PoolGeom g;
     int32_t num_seqs;
     int32_t num_q_heads;
@@ -91,6 +92,13 @@ struct DecodeArgs {
     float* pre_ml;
     int32_t pre_splits;
     int32_t pre_split_tokens;
+    // Chunked mode (causal query chunks on the vector units): grid unit v is query
+    // v mod q_per_chunk of chunk v / q_per_chunk; the chunk's queries start at row
+    // cu_q_lens[c] (or c * q_per_chunk without cu_q_lens) of q and out, which hold
+    // num_q_rows rows; context_lens and block_tables are per chunk.
+    const int32_t* cu_q_lens;
+    int32_t q_per_chunk;
+    int32_t num_q_rows;
     float scale_log2;      // scale * log2(e)
 };
 
@@ -127,8 +135,12 @@ struct PrefixArgs {
     int32_t split_tokens;    // keys per split (a multiple of 64)
     float scale_log2;
 };
-// Persistent waves of the contiguous-layout decode (bf16 only).
-int decode_contiguous_waves(int head_dim, int group);
+// Persistent waves of the contiguous-layout decode.
+int decode_contiguous_waves(bool is_bf16, int head_dim, int group);
+// Causal query chunks, one wave per (query, kv head) streaming its visible keys with
+// decode's arithmetic (fp32, or shapes without a matrix-core path); units = grid slots.
+hipError_t launch_decode_chunked(const DecodeArgs& a, bool is_bf16, int head_dim, int group,
+                                 int64_t units, hipStream_t st);
 
 struct PrefillArgs {
     void* out;
@@ -172,9 +184,9 @@ hipError_t launch_swap(const SwapArgs& a, hipStream_t st);
 // is_bf16 selects the element type; group = num_q_heads / num_kv_heads (1..8).
 hipError_t launch_decode(const DecodeArgs& a, bool is_bf16, int head_dim, int group,
                          int num_seqs, hipStream_t st);
-// Decode over the contiguous [S][L][Hkv][D] layout (bf16, balanced split).
-hipError_t launch_decode_contiguous(const DecodeArgs& a, int head_dim, int group, int num_seqs,
-                                    hipStream_t st);
+// Decode over the contiguous [S][L][Hkv][D] layout (balanced split).
+hipError_t launch_decode_contiguous(const DecodeArgs& a, bool is_bf16, int head_dim, int group,
+                                    int num_seqs, hipStream_t st);
 hipError_t launch_prefix(const PrefixArgs& a, int head_dim, int group, int num_groups,
                          int max_group_seqs, hipStream_t st);
 // Decode over the tokens after each sequence's shared prefix, merging the prefix pass.
@@ -184,8 +196,8 @@ hipError_t launch_decode_prefix(const DecodeArgs& a, int head_dim, int group, in
 int prefill_wgs(int head_dim, int group);
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int group, int num_chunks,
                           int max_q_len, hipStream_t st);
-// Multi-query decode (bf16): nq queries per sequence, nq * group <= 16, balanced split.
-int decode_mq_waves(int head_dim, int group);
+// Multi-query decode (bf16): nq queries per sequence, nq * group <= 32, balanced split.
+int decode_mq_waves(int head_dim, int group, int nq);
 hipError_t launch_decode_mq(const DecodeArgs& a, int head_dim, int group, int nq, int num_seqs,
                             hipStream_t st);
 // The balanced merge for nq queries per sequence (used by the multi-query decode).

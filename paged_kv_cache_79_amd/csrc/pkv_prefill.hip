@@ -397,7 +397,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, int num_
         if (w >= W) return;
         tiles = p.T;
         nw = W;
-        const Split sp{p.T, W, p.T, W};
+        const Split sp = even_split(p.T, W);
         u = __builtin_amdgcn_readfirstlane((int)range_begin(sp, w));
         e = __builtin_amdgcn_readfirstlane((int)range_begin(sp, w + 1));
         if (u >= e) return;
@@ -472,7 +472,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a, int num_
         // pieces (none when it finishes the item itself)
         if (a.part_o != nullptr && threadIdx.x == 0) {
             const int pieces =
-                k1 == nt ? 0 : (int)(unit_owner(Split{tiles, nw, tiles, nw}, (int64_t)u + nt - 1) - w + 1);
+                k1 == nt ? 0 : (int)(unit_owner(even_split(tiles, nw), (int64_t)u + nt - 1) - w + 1);
             const int item = (c * Hkv + h) * num_q_tiles + qt;
             *reinterpret_cast<int2*>(a.item_desc + 2 * item) = make_int2(w, pieces);
         }

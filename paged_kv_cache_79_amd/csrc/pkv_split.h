@@ -57,12 +57,9 @@ __device__ __forceinline__ int unit_tiles(const DecodeArgs& a, int s) {
 // Tiles of the whole batch (all sequences, one kv head) and tiles before sequence `upto`.
 // Four chunks of 64 sequences per pass, their loads issued together; the counts of
 // the first 256 sequences stay in first[q] (sequence 64q + lane) for locate_unit.
-// With a.tile_prefix set, the wave numbered `writer` records, for every pass it owns
-// (pass p belongs to wave p mod num_waves), each sequence's tiles before it, and wave 0
-// the batch's total at index num_seqs: the merge then finds a row's pieces in O(1).
 template <bool PREFIX = false>
 __device__ __forceinline__ void count_tiles(const DecodeArgs& a, int upto, int64_t& total,
-                                            int64_t& before, int (&first)[4], int64_t writer = -1) {
+                                            int64_t& before, int (&first)[4]) {
     const int lane = threadIdx.x & 63;   // lane of the wave (the merge runs several per workgroup)
     total = 0;
     before = 0;
@@ -77,21 +74,6 @@ __device__ __forceinline__ void count_tiles(const DecodeArgs& a, int upto, int64
 #pragma unroll
             for (int q = 0; q < 4; ++q) first[q] = nt[q];
         }
-        if (a.tile_prefix != nullptr && writer == (int64_t)(c0 >> 8) % a.num_waves) {
-            int64_t off = total;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                int incl = nt[q];
-#pragma unroll
-                for (int d = 1; d < 64; d <<= 1) {
-                    const int y = __shfl_up(incl, d);
-                    if (lane >= d) incl += y;
-                }
-                const int sl = c0 + q * 64 + lane;
-                if (sl < a.num_seqs) a.tile_prefix[sl] = off + (incl - nt[q]);
-                off += __builtin_amdgcn_readlane(incl, 63);
-            }
-        }
         int t = 0, u = 0;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -101,7 +83,6 @@ __device__ __forceinline__ void count_tiles(const DecodeArgs& a, int upto, int64
         total += wave_sum_int(t);
         before += wave_sum_int(u);
     }
-    if (a.tile_prefix != nullptr && writer == 0 && lane == 0) a.tile_prefix[a.num_seqs] = total;
 }
 template <bool PREFIX = false>
 __device__ __forceinline__ void count_tiles(const DecodeArgs& a, int upto, int64_t& total,
@@ -110,30 +91,110 @@ __device__ __forceinline__ void count_tiles(const DecodeArgs& a, int upto, int64
     count_tiles<PREFIX>(a, upto, total, before, first);
 }
 
-// The split of T tiles over W waves: the first Wl waves share the first F tiles
-// evenly, the other W - Wl waves the remaining T - F (every range non-empty).
+// Share of the tiles each wave gets, by the XCD it runs on (in 1/256).  The dispatcher
+// hands workgroup w to XCD w mod 8, so in a grid that fills every wave slot the waves
+// of one XCD are those with one w mod 8.  Per-wave timestamps on two MI355X machines
+// (GQA and long-context batches, 24 calls) put the mean finish of the waves of XCDs 0..7
+// at 0.956, 1.005, 0.974, 1.026, 0.993, 1.039, 0.975, 1.034 of the average: odd XCDs
+// stream about 5% slower.  The weights take three quarters of the inverse.
+constexpr int kXcdWeight[8] = {265, 255, 261, 251, 257, 249, 261, 250};
+// Sum of the weights of waves 0..n-1.  The partial period is summed with selects over
+// the table's entries as immediates: indexing it at run time would compile to a memory
+// load, a dependent round trip in every evaluation.
+__device__ __forceinline__ int64_t xcd_weight_prefix(int64_t n) {
+    int64_t sum = 0;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) sum += kXcdWeight[x];
+    const int r = (int)(n & 7);
+    int pre = 0;
+#pragma unroll
+    for (int x = 0; x < 7; ++x) pre += x < r ? kXcdWeight[x] : 0;
+    return (n >> 3) * sum + pre;
+}
+
+// The split of T tiles over W waves into contiguous ranges, every range non-empty.
+// Weighted (the grid fills every wave slot, W a multiple of 16, and the lightest wave's
+// share T w_min / Ptot is at least one tile): wave w gets a share proportional to its
+// class weight (lw for the first half of the grid, which wins issue arbitration when
+// two waves share a SIMD, gw for the second) times its XCD's weight.  Otherwise the T
+// tiles are shared evenly.
 struct Split {
-    int64_t T, W, F, Wl;
+    int64_t T, W;
+    int64_t Wl;          // lead waves (W / 2); 0 for the even split
+    int64_t lw, gw;      // class weights (lead, lag)
+    int64_t Ptot;        // total weight of the W waves
+    double inv_ptot;     // 1 / Ptot, for the estimates range_begin corrects
 };
+__device__ __forceinline__ Split even_split(int64_t T, int64_t W) {
+    return Split{T, W, 0, 1, 1, W, 1.0 / (double)W};
+}
 __device__ __forceinline__ Split make_split(const DecodeArgs& a, int64_t T, int64_t W) {
-    Split p{T, W, T, W};                       // even split: one class of waves
-    if (W == a.num_waves && W % 2 == 0) {
-        const int64_t F = T * a.lead_share_q10 / 1024, Wl = W / 2;
-        if (F >= Wl && T - F >= W - Wl) {
-            p.F = F;
-            p.Wl = Wl;
+    Split p = even_split(T, W);
+    if (W == a.num_waves && W % 16 == 0 && a.lead_share_q10 > 0 && a.lead_share_q10 < 1024) {
+        const int64_t lw = a.lead_share_q10, gw = 1024 - a.lead_share_q10;
+        const int64_t Ptot = (lw + gw) * xcd_weight_prefix(W / 2);
+        constexpr int64_t kXcdMin = 249;       // smallest entry of kXcdWeight
+        if (T * (min(lw, gw) * kXcdMin) >= Ptot) {
+            p.Wl = W / 2;
+            p.lw = lw;
+            p.gw = gw;
+            p.Ptot = Ptot;
+            p.inv_ptot = 1.0 / (double)Ptot;
         }
     }
     return p;
 }
-// First tile of wave w's range [begin(w), begin(w + 1)); begin(Wl) = F, begin(W) = T.
-__device__ __forceinline__ int64_t range_begin(const Split& p, int64_t w) {
-    return w <= p.Wl ? w * p.F / p.Wl : p.F + (w - p.Wl) * (p.T - p.F) / (p.W - p.Wl);
+// Weight of waves 0..w-1.
+__device__ __forceinline__ int64_t split_prefix(const Split& p, int64_t w) {
+    if (p.Wl == 0) return w;
+    return w <= p.Wl ? p.lw * xcd_weight_prefix(w)
+                     : p.lw * xcd_weight_prefix(p.Wl) + p.gw * xcd_weight_prefix(w - p.Wl);
 }
-// Wave whose range holds tile u.
+// First tile of wave w's range [begin(w), begin(w + 1)): floor(T P(w) / Ptot);
+// begin(W) = T.  64-bit integer division is a long software sequence on the GPU, so
+// while T and Ptot stay below 2^31 (T P < 2^62) the quotient is estimated with the
+// split's double-precision reciprocal (off by at most one) and corrected with exact
+// 64-bit products.
+__device__ __forceinline__ int64_t range_begin(const Split& p, int64_t w) {
+    const int64_t P = split_prefix(p, w);
+    if (p.T < ((int64_t)1 << 31) && p.Ptot < ((int64_t)1 << 31)) {
+        const int64_t num = p.T * P;
+        int64_t c = (int64_t)((double)num * p.inv_ptot);
+        while (c * p.Ptot > num) --c;
+        while ((c + 1) * p.Ptot <= num) ++c;
+        return c;
+    }
+    return (p.T / p.Ptot) * P + (p.T % p.Ptot) * P / p.Ptot;
+}
+// Wave whose range holds tile u (0 <= u < T): the last w with begin(w) <= u.  Within
+// each class the shares differ only by the XCD weights (a few percent), so spreading
+// the class's tiles evenly over its waves lands within a wave or two of the owner,
+// which a short walk over exact range starts settles.
 __device__ __forceinline__ int64_t unit_owner(const Split& p, int64_t u) {
-    return u < p.F ? ((u + 1) * p.Wl - 1) / p.F
-                   : p.Wl + ((u - p.F + 1) * (p.W - p.Wl) - 1) / (p.T - p.F);
+    int64_t w;
+    if (p.Wl == 0) {
+        w = (int64_t)(((float)u + 0.5f) * (float)p.W * __builtin_amdgcn_rcpf((float)p.T));
+    } else {
+        const int64_t bl = range_begin(p, p.Wl);          // first tile of the lag class
+        w = u < bl ? (int64_t)(((float)u + 0.5f) * (float)p.Wl * __builtin_amdgcn_rcpf((float)bl))
+                   : p.Wl + (int64_t)(((float)(u - bl) + 0.5f) * (float)(p.W - p.Wl) *
+                                      __builtin_amdgcn_rcpf((float)(p.T - bl)));
+    }
+    w = max((int64_t)0, min(w, p.W - 1));
+    while (w > 0 && range_begin(p, w) > u) --w;
+    while (w + 1 < p.W && range_begin(p, w + 1) <= u) ++w;
+    return w;
+}
+
+// Record, from the wave w that holds the first tile u0 of unit (s, h) with nt tiles,
+// that wave and how many waves the unit's tiles span (one: w finished it, which the
+// caller knows without locating the last tile's owner).
+__device__ __forceinline__ void record_unit(const DecodeArgs& a, const Split& sp, int64_t w, int s,
+                                            int h, int64_t u0, int nt, bool finished) {
+    const int64_t w1 = finished ? w : unit_owner(sp, u0 + nt - 1);
+    if ((threadIdx.x & 63) == 0)
+        *reinterpret_cast<int2*>(a.unit_desc + 2 * ((int64_t)s * a.g.num_kv_heads + h)) =
+            make_int2((int)w, (int)(w1 - w + 1));
 }
 
 // Sequence holding unit b (the first s with Hkv * (tiles up to s) > b) and the tiles

@@ -26,8 +26,8 @@ static void check_geom(const PoolGeom& g) {
 // Waves and workgroups a 256-CU device keeps resident.
 int decode_balanced_waves(bool, int, int) { return 2048; }
 int decode_prefix_waves(int, int) { return 2048; }
-int decode_contiguous_waves(int, int) { return 2048; }
-int decode_mq_waves(int, int) { return 2048; }
+int decode_contiguous_waves(bool, int, int) { return 2048; }
+int decode_mq_waves(int, int, int nq) { return nq > 0 ? 2048 : 0; }
 int prefill_wgs(int, int) { return 512; }
 
 hipError_t launch_validate(const ValidateArgs& v, hipStream_t) {
@@ -52,7 +52,7 @@ static void check_decode(const DecodeArgs& a, bool paged = true) {
     if (paged) check_geom(a.g);
     require(a.num_seqs > 0 && a.num_q_heads > 0, "decode sizes");
     require(a.part_tokens >= 0 && a.num_parts >= 1, "decode partitions");
-    require(a.part_tokens > 0 || (a.num_waves > 0 && a.part_o && a.part_ml && a.tile_prefix),
+    require(a.part_tokens > 0 || (a.num_waves > 0 && a.part_o && a.part_ml && a.unit_desc),
             "balanced workspace");
 }
 hipError_t launch_decode(const DecodeArgs& a, bool, int, int group, int, hipStream_t) {
@@ -60,9 +60,17 @@ hipError_t launch_decode(const DecodeArgs& a, bool, int, int group, int, hipStre
     require(group >= 1 && group <= 8, "group");
     return hipSuccess;
 }
-hipError_t launch_decode_contiguous(const DecodeArgs& a, int, int, int, hipStream_t) {
+hipError_t launch_decode_contiguous(const DecodeArgs& a, bool, int, int, int, hipStream_t) {
     check_decode(a, false);          // the slab is described as 64-token blocks of one row each
     require(a.contig_row_stride > 0 && a.contig_seq_stride > 0, "contiguous strides");
+    return hipSuccess;
+}
+hipError_t launch_decode_chunked(const DecodeArgs& a, bool, int, int group, int64_t units,
+                                 hipStream_t) {
+    check_geom(a.g);
+    require(units > 0 && a.q_per_chunk > 0 && a.num_parts == 1, "chunked units");
+    require(units * a.g.num_kv_heads <= ((int64_t)1 << 30), "chunked grid");
+    require(group >= 1 && group <= 8, "group");
     return hipSuccess;
 }
 hipError_t launch_prefix(const PrefixArgs& a, int, int, int, int, hipStream_t) {

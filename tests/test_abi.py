@@ -142,11 +142,11 @@ def test_workspace_sizes(lib):
     # fixed partitions: S * Hq * parts * (D + 2) floats, none when one partition suffices
     assert f(2, 8, 2, 128, 4096, 256) == 2 * 8 * 16 * 130 * 4
     assert f(2, 8, 2, 128, 200, 256) == 0
-    # balanced split: two partial slots of G heads per resident wave (8 per CU), and the
-    # tile offset of every sequence plus the batch total (int64)
+    # balanced split: two partial slots of G heads per resident wave (8 per CU), and a
+    # record of two int32 per (sequence, kv head)
     b = f(2, 8, 2, 128, 4096, 0)
-    assert b > 0 and (b - 3 * 8) % (2 * 4 * 130 * 4) == 0
-    assert f(5, 8, 2, 128, 4096, 0) - b == 3 * 8
+    assert b > 0 and (b - 2 * 2 * 8) % (2 * 4 * 130 * 4) == 0
+    assert f(5, 8, 2, 128, 4096, 0) - b == 3 * 2 * 8
     assert f(0, 8, 2, 128, 4096, 0) == 0
 
 
@@ -159,7 +159,6 @@ def contig(lib, dtype=1, S=2, L=128, hkv=2, d=128, maxctx=100, hq=8, scale=0.1, 
 @dummy_ptrs
 def test_contiguous_validation(lib):
     assert contig(lib, dtype=7) == DTYPE
-    assert contig(lib, dtype=0) == UNSUP               # fp32: the baseline is bf16 only
     assert contig(lib, d=96) == UNSUP
     assert contig(lib, L=100) == SHAPE                 # slab not a whole number of tiles
     assert contig(lib, L=0) == SHAPE
@@ -183,9 +182,7 @@ def shared(lib, dtype=1, nb=8, hkv=2, bs=16, d=128, mb=4, S=2, maxctx=64, hq=8, 
 @dummy_ptrs
 def test_shared_prefix_validation(lib):
     assert shared(lib, dtype=7) == DTYPE
-    assert shared(lib, dtype=0) == UNSUP               # the prefix pass is bf16 only
     assert shared(lib, d=96) == UNSUP
-    assert shared(lib, bs=4, d=64) == UNSUP            # bf16 runs of 512 B: matrix-core path
     assert shared(lib, hq=9) == SHAPE
     assert shared(lib, hq=36, hkv=2) == UNSUP          # group of 18 heads
     assert shared(lib, ngroups=-1) == SHAPE
@@ -221,12 +218,9 @@ def mq(lib, dtype=1, nb=8, hkv=2, bs=16, d=128, mb=4, S=2, n=4, maxctx=64, hq=8,
 @dummy_ptrs
 def test_multi_query_validation(lib):
     assert mq(lib, dtype=7) == DTYPE
-    assert mq(lib, dtype=0) == UNSUP                   # bf16 only
     assert mq(lib, d=96) == UNSUP
-    assert mq(lib, bs=4, d=64) == UNSUP                # bf16 runs of 512 B: matrix-core path
     assert mq(lib, n=0) == SHAPE
     assert mq(lib, hq=9) == SHAPE
-    assert mq(lib, n=5) == UNSUP                       # 5 queries x 4 heads > 16 rows
     assert mq(lib, hq=36, hkv=2, n=1) == UNSUP         # group of 18 heads
     assert mq(lib, scale=float("nan")) == SHAPE
     assert mq(lib, ptr=None) == NULL
@@ -238,10 +232,10 @@ def test_multi_query_validation(lib):
 
 def test_multi_query_workspace_sizes(lib):
     f = lib.paged_attention_decode_multi_query_workspace_bytes
-    # two partial slots of n * G rows per resident wave, plus decode's tile offsets;
+    # two partial slots of n * G rows per resident wave, plus decode's unit records;
     # n = 1 is decode's size
     assert f(2, 1, 8, 2, 128) == lib.paged_attention_decode_workspace_bytes(2, 8, 2, 128, 4096, 0)
-    assert f(2, 4, 8, 2, 128) - 3 * 8 == 4 * (f(2, 1, 8, 2, 128) - 3 * 8)
+    assert f(2, 4, 8, 2, 128) - 2 * 2 * 8 == 4 * (f(2, 1, 8, 2, 128) - 2 * 2 * 8)
     assert f(0, 4, 8, 2, 128) == 0 and f(2, 0, 8, 2, 128) == 0
 
 
@@ -267,7 +261,6 @@ def test_prefill_validation(lib):
         return f(a["dtype"], a["out"], a["q"], a["cu"], a["nc"], a["mq"], a["k"], a["v"], a["nb"],
                  a["hkv"], a["bs"], a["d"], a["bt"], a["mb"], a["ctx"], a["mctx"], a["hq"], a["scale"],
                  a.get("ws"), a.get("wsb", 0), None)
-    assert call(dtype=0) == UNSUP                      # fp32 prefill is not offered
     assert call(hq=9) == SHAPE                         # not a multiple of the kv heads
     assert call(q=None) == NULL
     assert call(nc=0, q=None) == OK

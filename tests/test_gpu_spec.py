@@ -60,17 +60,15 @@ def test_small(draft, path):
         path)
 
 
-def test_prefill_draft_7():
-    """8 queries x 4 heads = 32 rows: beyond one matrix-core tile of the multi-query
-    decode, which rejects it; the prefill path serves it."""
-    sb = W.spec_decode(seed=7, num_seqs=6, draft=7, ctx_range=(1, 700))
-    run(sb, list(range(6)), "prefill")
-    k = dev(sb.k_pool)
-    pre = sb.prefill
-    with pytest.raises(pkv.PagedKVError):
-        pkv.paged_attention_decode_multi_query(
-            torch.empty(pre.q.shape, dtype=torch.bfloat16, device="cuda"), dev(pre.q), k, k,
-            dev(pre.block_tables), dev(pre.context_lens), 8, pre.max_context_len, pre.scale)
+@pytest.mark.parametrize("draft", [4, 5, 6, 7])
+def test_drafts_past_one_matrix_tile(draft):
+    """(k + 1) x 4 heads = 20..32 rows: more than the 16 columns of the multi-query
+    kernel's matrix tile; the entry point serves them query by query on the vector
+    units, and the prefill path serves them on the matrix cores."""
+    sb = W.spec_decode(seed=70 + draft, num_seqs=6, draft=draft, ctx_range=(1, 700))
+    mq, _, _ = run(sb, list(range(6)), "multi_query")
+    pf, _, _ = run(sb, list(range(6)), "prefill")
+    assert rownorm_err(O.widen(mq, "bf16"), O.widen(pf, "bf16")) <= TOL["bf16"]
 
 
 @pytest.mark.parametrize("path", ["multi_query", "prefill"])
