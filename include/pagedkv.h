@@ -312,6 +312,21 @@ pkv_status pkv_validate(int32_t num_blocks, int32_t block_size, const int32_t* b
                         hipStream_t stream);
 
 /*
+ * pkv_validate_chunks -- device-side check of the chunk descriptors that
+ * paged_attention_prefill_chunk trusts ("Inside vLLM, part 2", chunked prefill: a chunk's
+ * queries are the last positions of its context, packed chunk after chunk).  Enqueues
+ * kernels that set *count (int32, device memory owned by the caller) to the number of
+ * chunks c in [0, num_chunks) with cu_q_lens[c + 1] < cu_q_lens[c], a negative context,
+ * more queries than context (cu_q_lens[c + 1] - cu_q_lens[c] > context_lens[c]), or queries
+ * ending past total_q rows (when total_q >= 0), counting chunk 0 also when cu_q_lens[0]
+ * != 0.  The call does not wait.  Errors: PKV_ERR_NULL / PKV_ERR_SHAPE (nothing
+ * enqueued); num_chunks == 0 enqueues nothing and leaves *count as it is.
+ */
+pkv_status pkv_validate_chunks(const int32_t* cu_q_lens, const int32_t* context_lens,
+                               int32_t num_chunks, int32_t total_q, int32_t* count,
+                               hipStream_t stream);
+
+/*
  * paged_attention_prefill_chunk -- causal attention of prefill query chunks over
  * their paged contexts ("Inside vLLM, part 2", chunked prefill: a long prompt is
  * processed a bounded number of tokens per step, each chunk attending to the

@@ -12,7 +12,10 @@ The kernels trust what lies in device memory; these are the rules that trust res
     one write cannot share a slot (negative slots are padding, skipped);
   * the same chapter (section 6): copy-on-write copies whole blocks, src -> dst, all
     at once, so every id must name a block, no block may be written twice, and no
-    block may be both written and read in one call.
+    block may be both written and read in one call;
+  * "Inside vLLM, part 2" (chunked prefill): a chunk's queries are the last positions
+    of its context, so a chunk cannot hold more queries than its context, and the
+    chunks' queries are packed one after another from row 0.
 
 validate() counts the violations of each rule the way the device check does: each
 offending table entry, sequence, token or pair once.
@@ -80,3 +83,18 @@ def validate(num_blocks, block_size, block_tables, context_lens, slot_mapping=()
                      bad_context_lens(block_size, mb, context_lens),
                      bad_slots(num_blocks, block_size, slot_mapping),
                      bad_copy_pairs(num_blocks, block_mapping)], dtype=np.int32)
+
+
+def bad_chunks(cu_q_lens, context_lens, total_q=-1) -> int:
+    """Chunks whose query range runs backwards, whose context is negative or shorter than
+    its queries, or whose queries end past total_q rows (total_q >= 0); chunk 0 also
+    when the packing does not start at row 0."""
+    cu = [int(x) for x in np.asarray(cu_q_lens)]
+    bad = 0
+    for c, ctx in enumerate(np.asarray(context_lens)):
+        ctx = int(ctx)
+        q0, q1 = cu[c], cu[c + 1]
+        if (c == 0 and q0 != 0) or q1 < q0 or ctx < 0 or q1 - q0 > ctx or \
+                (total_q >= 0 and q1 > total_q):
+            bad += 1
+    return bad

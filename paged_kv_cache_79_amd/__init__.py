@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 EXPORTS = (
     "pkv_status_string",
     "pkv_validate",
+    "pkv_validate_chunks",
     "paged_kv_write",
     "copy_blocks",
     "paged_attention_decode_workspace_bytes",
@@ -113,6 +114,8 @@ def load_library(path: Optional[str] = None):
     lib.swap_blocks.restype = ctypes.c_int
     lib.pkv_validate.argtypes = [I32, I32, VP, I32, VP, I32, VP, I32, VP, I32, VP, VP]
     lib.pkv_validate.restype = ctypes.c_int
+    lib.pkv_validate_chunks.argtypes = [VP, VP, I32, I32, VP, VP]
+    lib.pkv_validate_chunks.restype = ctypes.c_int
     lib.pkv_pool_create.argtypes = [I32]
     lib.pkv_pool_create.restype = VP
     lib.pkv_pool_destroy.argtypes = [VP]
@@ -533,6 +536,26 @@ def validate(num_blocks: int, block_size: int, block_tables=None, context_lens=N
     c = counts.cpu().tolist()
     return {"bad_table_entries": c[0], "bad_context_lens": c[1], "bad_slots": c[2],
             "bad_copy_pairs": c[3]}
+
+
+def validate_chunks(cu_q_lens, context_lens, total_q: int = -1, stream=None) -> int:
+    """Device-side check of prefill chunk descriptors (pkv_validate_chunks): the number
+    of malformed chunks, after synchronising the stream."""
+    import torch
+    _dev(cu_q_lens, "cu_q_lens", torch.int32)
+    _dev(context_lens, "context_lens", torch.int32)
+    n = int(context_lens.numel())
+    if cu_q_lens.numel() != n + 1:
+        raise ValueError("cu_q_lens must hold num_chunks + 1 entries")
+    if stream is None:
+        count = torch.zeros(1, dtype=torch.int32, device=context_lens.device)
+    else:
+        with torch.cuda.stream(stream):
+            count = torch.zeros(1, dtype=torch.int32, device=context_lens.device)
+    _check("pkv_validate_chunks", load_library().pkv_validate_chunks(
+        _ptr(cu_q_lens), _ptr(context_lens), n, int(total_q), _ptr(count), _stream(stream)))
+    (torch.cuda.current_stream(context_lens.device) if stream is None else stream).synchronize()
+    return int(count.item())
 
 
 def check_preconditions(num_blocks: int, block_size: int, **kw) -> None:

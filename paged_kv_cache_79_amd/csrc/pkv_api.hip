@@ -287,6 +287,17 @@ pkv_status pkv_validate(int32_t num_blocks, int32_t block_size, const int32_t* b
     return launch_status(launch_validate(v, stream));
 }
 
+pkv_status pkv_validate_chunks(const int32_t* cu_q_lens, const int32_t* context_lens,
+                               int32_t num_chunks, int32_t total_q, int32_t* count,
+                               hipStream_t stream) {
+    if (num_chunks < 0) return PKV_ERR_SHAPE;
+    if (!count) return PKV_ERR_NULL;
+    if (num_chunks > 0 && (!cu_q_lens || !context_lens)) return PKV_ERR_NULL;
+    if (num_chunks == 0) return PKV_OK;
+    return launch_status(
+        launch_validate_chunks(cu_q_lens, context_lens, num_chunks, total_q, count, stream));
+}
+
 size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                               int32_t num_kv_heads, int32_t head_dim,
                                               int32_t max_context_len, int32_t partition_tokens) {

@@ -178,6 +178,9 @@ struct ValidateArgs {
 };
 
 hipError_t launch_validate(const ValidateArgs& v, hipStream_t st);
+hipError_t launch_validate_chunks(const int32_t* cu_q_lens, const int32_t* context_lens,
+                                  int32_t num_chunks, int32_t total_q, int32_t* count,
+                                  hipStream_t st);
 hipError_t launch_kv_write(const WriteArgs& a, hipStream_t st);
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t st);
 hipError_t launch_swap(const SwapArgs& a, hipStream_t st);

@@ -52,7 +52,8 @@ namespace pkv {
 // ---- the plan of the balanced split -----------------------------------------------
 
 // Chunk c as the kernels see it: first query row, queries, clamped context, and the
-// query tiles that hold work (none for a malformed chunk, n_q > ctx).
+// query tiles that hold work (none for a malformed chunk: n_q > ctx, or a negative
+// first row).
 struct PfChunk {
     int q0, nq, ctx, nqt;
 };
@@ -63,7 +64,7 @@ __device__ __forceinline__ PfChunk pf_chunk(const PrefillArgs& a, int c, int num
     k.nq = as_const(a.cu_q_lens)[c + 1] - k.q0;
     const int ctx = as_const(a.context_lens)[c];
     k.ctx = max(0, min(ctx, min(a.max_context_len, a.max_blocks_per_seq * a.g.block_size)));
-    k.nqt = (k.nq <= 0 || k.nq > k.ctx) ? 0 : min((k.nq + QP - 1) / QP, num_q_tiles);
+    k.nqt = (k.q0 < 0 || k.nq <= 0 || k.nq > k.ctx) ? 0 : min((k.nq + QP - 1) / QP, num_q_tiles);
     return k;
 }
 // 64-key tiles query tile qt (< nqt) reads: keys up to the causal limit of its last row.

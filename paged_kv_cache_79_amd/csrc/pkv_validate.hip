@@ -20,8 +20,8 @@ namespace pkv {
 
 constexpr int kValidateThreads = 256;
 
-__global__ __launch_bounds__(64) void validate_zero_kernel(int32_t* counts) {
-    if (threadIdx.x < 4) counts[threadIdx.x] = 0;
+__global__ __launch_bounds__(64) void validate_zero_kernel(int32_t* counts, int n) {
+    if ((int)threadIdx.x < n) counts[threadIdx.x] = 0;
 }
 
 // Adds this thread's `bad` into counts[which], one global atomic per workgroup.
@@ -94,8 +94,34 @@ __global__ __launch_bounds__(kValidateThreads) void validate_pairs_kernel(
     add_count(bad ? 1 : 0, counts, 3);
 }
 
+// one thread per chunk: cu_q_lens[0] must be 0, each chunk's queries must not run
+// backwards, outnumber its context or end past total_q rows (total_q < 0: unknown)
+__global__ __launch_bounds__(kValidateThreads) void validate_chunks_kernel(
+    const int32_t* cu_q_lens, const int32_t* context_lens, int32_t num_chunks, int32_t total_q,
+    int32_t* count) {
+    const int c = blockIdx.x * kValidateThreads + threadIdx.x;
+    int bad = 0;
+    if (c < num_chunks) {
+        const int q0 = cu_q_lens[c], q1 = cu_q_lens[c + 1], ctx = context_lens[c];
+        bad = (c == 0 && q0 != 0) || q1 < q0 || ctx < 0 || q1 - q0 > ctx ||
+              (total_q >= 0 && q1 > total_q);
+    }
+    add_count(bad, count, 0);
+}
+
+hipError_t launch_validate_chunks(const int32_t* cu_q_lens, const int32_t* context_lens,
+                                  int32_t num_chunks, int32_t total_q, int32_t* count,
+                                  hipStream_t st) {
+    hipLaunchKernelGGL(validate_zero_kernel, dim3(1), dim3(64), 0, st, count, 1);
+    hipLaunchKernelGGL(validate_chunks_kernel,
+                       dim3((num_chunks + kValidateThreads - 1) / kValidateThreads),
+                       dim3(kValidateThreads), 0, st, cu_q_lens, context_lens, num_chunks, total_q,
+                       count);
+    return hipGetLastError();
+}
+
 hipError_t launch_validate(const ValidateArgs& v, hipStream_t st) {
-    hipLaunchKernelGGL(validate_zero_kernel, dim3(1), dim3(64), 0, st, v.counts);
+    hipLaunchKernelGGL(validate_zero_kernel, dim3(1), dim3(64), 0, st, v.counts, 4);
     if (v.num_seqs > 0)
         hipLaunchKernelGGL(validate_tables_kernel, dim3(v.num_seqs), dim3(kValidateThreads), 0, st,
                            v.block_tables, v.max_blocks_per_seq, v.context_lens, v.num_blocks,

@@ -95,6 +95,8 @@ int main() {
                                            next_u64() % 2 ? pfw : wsb, nullptr));
         note(pkv_validate(nb, bs, (const int32_t*)ptr, mb, (const int32_t*)P, S, (const int64_t*)P, T,
                           (const int64_t*)P, pick(), (int32_t*)P, nullptr));
+        note(pkv_validate_chunks((const int32_t*)ptr, (const int32_t*)P, pick(), pick(),
+                                 next_u64() % 2 ? (int32_t*)P : nullptr, nullptr));
         // swap_blocks reads its host block mapping: a real host array, ids checked first
         std::vector<int64_t> map((size_t)2 * 8);
         for (auto& x : map) x = (int64_t)(int32_t)pick();

@@ -34,6 +34,11 @@ hipError_t launch_validate(const ValidateArgs& v, hipStream_t) {
     require(v.counts != nullptr, "validate counts");
     return hipSuccess;
 }
+hipError_t launch_validate_chunks(const int32_t* cu_q_lens, const int32_t* context_lens,
+                                  int32_t num_chunks, int32_t, int32_t* count, hipStream_t) {
+    require(cu_q_lens && context_lens && count && num_chunks > 0, "validate chunks");
+    return hipSuccess;
+}
 hipError_t launch_kv_write(const WriteArgs& a, hipStream_t) {
     check_geom(a.g);
     require(a.num_tokens > 0 && a.slot_mapping, "write");

@@ -37,6 +37,20 @@ def test_pin_copy_pairs():
     assert V.bad_copy_pairs(8, [(0, 1), (0, 2), (0, 3)]) == 0
 
 
+def test_pin_chunks():
+    # chunk 1 runs backwards, chunk 2 has 4 queries over a 3-token context, chunk 3 a
+    # negative context; chunks 0 and 4 are fine (0 queries over 0 tokens is allowed)
+    cu = [0, 5, 3, 7, 7, 7]
+    assert V.bad_chunks(cu, [5, 9, 3, -1, 0]) == 3
+    # packing that does not start at row 0 counts chunk 0; queries past total_q rows
+    assert V.bad_chunks([2, 4], [10]) == 1
+    assert V.bad_chunks([0, 4, 9], [4, 100], total_q=8) == 1
+    assert V.bad_chunks([0, 4, 9], [4, 100], total_q=9) == 0
+    pre = W.prefill_only(seed=9, chunk_lens=[70, 0, 129], contexts=[300, 5, 129], num_q_heads=4,
+                         num_kv_heads=2, head_dim=64, block_size=16)[0]
+    assert V.bad_chunks(pre.cu_q_lens, pre.context_lens, total_q=pre.q.shape[0]) == 0
+
+
 def test_clean_workloads_count_zero():
     b = W.gqa(num_seqs=8)
     assert V.validate(b.num_blocks, b.block_size, b.block_tables, b.context_lens,
@@ -100,3 +114,32 @@ def test_device_clean_workloads_and_raise():
     with pytest.raises(pkv.PagedKVError) as e:
         pkv.check_preconditions(b.num_blocks, b.block_size, slot_mapping=dev(bad))
     assert e.value.status == pkv.PKV_ERR_VALIDATION
+
+
+def planted_chunks(seed, C=300):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    nq = rng.integers(0, 40, C)
+    ctx = (nq + rng.integers(0, 500, C)).astype(np.int32)
+    cu = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    hit = rng.choice(C, 12, replace=False)
+    ctx[hit[:4]] = -rng.integers(1, 9, 4)
+    ctx[hit[4:8]] = np.maximum(nq[hit[4:8]] - 1, 0)
+    cu[hit[8:11] + 1] = cu[hit[8:11]] - 1
+    return cu, ctx, int(cu[-1]) - 3
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("seed", [4, 5])
+def test_device_chunk_counts_match_model(seed):
+    import paged_kv_cache_79_amd as pkv
+    from tests.gpu_helpers import dev
+    cu, ctx, total = planted_chunks(seed)
+    print(f"validate_chunks seed={seed}", flush=True)
+    for t in (-1, total):
+        want = V.bad_chunks(cu, ctx, total_q=t)
+        assert want > 0
+        assert pkv.validate_chunks(dev(cu), dev(ctx), total_q=t) == want
+    pre = W.prefill_only(seed=9, chunk_lens=[70, 0, 129], contexts=[300, 5, 129], num_q_heads=4,
+                         num_kv_heads=2, head_dim=64, block_size=16)[0]
+    assert pkv.validate_chunks(dev(pre.cu_q_lens), dev(pre.context_lens),
+                               total_q=pre.q.shape[0]) == 0
