@@ -35,6 +35,8 @@
 // is by sequence position instead and does not depend on the device.
 #include <mutex>
 
+#include <type_traits>
+
 #include "pkv_split.h"
 
 namespace pkv {
@@ -497,48 +499,58 @@ __global__ __launch_bounds__(64 * kMergeRows) void decode_balanced_merge_kernel(
             sml = a.part_ml + rr * 2;
         }
     };
-    // states in batches of kBatch, each batch one round of loads: lane j holds the
-    // (max, sum) of state c0 + j while every lane loads its part of all the batch's
-    // output rows (unconditionally, clamped to the batch); a running maximum rescales
-    // what earlier batches accumulated, as in the online softmax
+    // states in batches, each batch one round of loads: lane j holds the (max, sum) of
+    // state c0 + j while every lane loads its part of all the batch's output rows
+    // (unconditionally, clamped to the batch); a running maximum rescales what earlier
+    // batches accumulated, as in the online softmax.  A row with few states takes a
+    // batch of 4 or 8, so that it issues no more loads than it has states.
     float M = kNoMax, L = 0.f;                 // L: per-lane sum, reduced at the end
     float acc[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) acc[k] = 0.f;
-    const int first_batch = COOP ? wi * kBatch : 0;
-    const int batch_step = COOP ? kMergeRows * kBatch : kBatch;
-    for (int c0 = first_batch; c0 < nst; c0 += batch_step) {
-        const int cnt = min(kBatch, nst - c0);
-        float2 ml = make_float2(-INFINITY, 0.f);
-        if (lane < cnt) {
-            const float *so, *sml;
-            state(c0 + lane, so, sml);
-            ml = *reinterpret_cast<const float2*>(sml);
-        }
-        float v[kBatch][PER];
+    auto batches = [&](auto batch_c) {
+        constexpr int B = decltype(batch_c)::value;
+        const int first_batch = COOP ? wi * B : 0;
+        const int batch_step = COOP ? kMergeRows * B : B;
+        for (int c0 = first_batch; c0 < nst; c0 += batch_step) {
+            const int cnt = min(B, nst - c0);
+            float2 ml = make_float2(-INFINITY, 0.f);
+            if (lane < cnt) {
+                const float *so, *sml;
+                state(c0 + lane, so, sml);
+                ml = *reinterpret_cast<const float2*>(sml);
+            }
+            float v[B][PER];
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-            const float *so, *sml;
-            state(c0 + min(j, cnt - 1), so, sml);
+            for (int j = 0; j < B; ++j) {
+                const float *so, *sml;
+                state(c0 + min(j, cnt - 1), so, sml);
 #pragma unroll
-            for (int k = 0; k < PER; ++k) v[j][k] = so[lane * PER + k];
-        }
-        const float Mn = fmaxf(M, wave_max(ml.x));
-        const float c = fast_exp2(M - Mn);
-        M = Mn;
-        const float wgt = lane < cnt ? fast_exp2(ml.x - Mn) : 0.f;
-        L = fmaf(L, c, wgt * ml.y);
+                for (int k = 0; k < PER; ++k) v[j][k] = so[lane * PER + k];
+            }
+            const float Mn = fmaxf(M, wave_max(ml.x));
+            const float c = fast_exp2(M - Mn);
+            M = Mn;
+            const float wgt = lane < cnt ? fast_exp2(ml.x - Mn) : 0.f;
+            L = fmaf(L, c, wgt * ml.y);
 #pragma unroll
-        for (int k = 0; k < PER; ++k) acc[k] *= c;
+            for (int k = 0; k < PER; ++k) acc[k] *= c;
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-            if (j < cnt) {
-                const float wj = u2f(__builtin_amdgcn_readlane(f2u(wgt), j));
+            for (int j = 0; j < B; ++j) {
+                if (j < cnt) {
+                    const float wj = u2f(__builtin_amdgcn_readlane(f2u(wgt), j));
 #pragma unroll
-                for (int k = 0; k < PER; ++k) acc[k] = fmaf(wj, v[j][k], acc[k]);
+                    for (int k = 0; k < PER; ++k) acc[k] = fmaf(wj, v[j][k], acc[k]);
+                }
             }
         }
-    }
+    };
+    if (COOP || nst > 8)
+        batches(std::integral_constant<int, kBatch>{});
+    else if (nst > 4)
+        batches(std::integral_constant<int, 8>{});
+    else
+        batches(std::integral_constant<int, 4>{});
     L = wave_sum(L);
     if constexpr (COOP) {
         // the waves' partial sums, rescaled to the largest of their maxima
