@@ -115,16 +115,24 @@ __device__ __forceinline__ void attend_mq(const DecodeArgs& a, int s, int h, int
     const float sl2 = a.scale_log2;
     const int kp = lane >> 3, c0 = lane & 7;
 
-    int tab_cur = load_tile_table(table, t_begin, lbs, nblk, lane);
-    for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
-        const int tab = tab_cur;
-        const int b0 = t0 >> lbs;
-        // ---- loads: K in the A layout, V as key pairs (both clamped to the context;
-        //      keys past it are masked out of the scores, so their values never count)
-        u32x4 kreg[4][P::KC];
+    // NC = 2 (one wave per SIMD, nothing else to hide its loads): loads run one tile
+    // ahead in the registers the current tile has finished with -- the next tile's K
+    // goes out right after the S^T products, its V right after the V^T stage, and the
+    // table entries of the tile after it in between, so that each wait of the in-order
+    // load counter covers only the loads it needs.  Keys are clamped to the segment's
+    // last key, so the loads past the last tile re-read that row (no branch, which
+    // would make the compiler wait for every load).  NC = 1 (two waves per SIMD) loads
+    // each tile at the top of its iteration: running ahead would push it past 256
+    // registers.
+    constexpr bool AHEAD = NC == 2;
+    const int klast = t_end - 1;
+    u32x4 kreg[4][P::KC];
+    u32x4 vreg[4][2][P::VJ];
+    auto load_k = [&](int t0, int tab) {
+        const int b0 = min(t0, klast) >> lbs;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            const int key = min(t0 + 16 * mt + n, ctx - 1);
+            const int key = min(t0 + 16 * mt + n, klast);
             int pb = __shfl(tab, (key >> lbs) - b0);
             pb = ((unsigned)pb < (unsigned)a.g.num_blocks) ? pb : 0;   // never a bad id
             const char* row = kb + (uint64_t)(uint32_t)pb * bstride +
@@ -133,12 +141,14 @@ __device__ __forceinline__ void attend_mq(const DecodeArgs& a, int s, int h, int
             for (int c = 0; c < P::KC; ++c)
                 kreg[mt][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + c * 64));
         }
-        u32x4 vreg[4][2][P::VJ];
+    };
+    auto load_v = [&](int t0, int tab) {
+        const int b0 = min(t0, klast) >> lbs;
 #pragma unroll
         for (int p = 0; p < 4; ++p)
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
-                const int key = min(t0 + 2 * (8 * p + kp) + r, ctx - 1);
+                const int key = min(t0 + 2 * (8 * p + kp) + r, klast);
                 int pb = __shfl(tab, (key >> lbs) - b0);
                 pb = ((unsigned)pb < (unsigned)a.g.num_blocks) ? pb : 0;
                 const char* row = vb + (uint64_t)(uint32_t)pb * bstride +
@@ -148,8 +158,26 @@ __device__ __forceinline__ void attend_mq(const DecodeArgs& a, int s, int h, int
                     vreg[p][r][j] =
                         __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + j * 128));
             }
-        tab_cur = load_tile_table(table, t0 + kTile, lbs, nblk, lane);
-
+    };
+    // block ids of the tile at t0 (a tile past the segment re-reads the last one's)
+    auto table_of = [&](int t0) { return load_tile_table(table, min(t0, klast), lbs, nblk, lane); };
+    int tab_cur = table_of(t_begin);
+    int tab_next = 0;
+    if constexpr (AHEAD) {
+        // issued in the loop's order (K, table, V), or the loop's first wait, which
+        // joins this path, would have to cover all of them
+        load_k(t_begin, tab_cur);
+        __builtin_amdgcn_sched_barrier(0);
+        tab_next = table_of(t_begin + kTile);
+        __builtin_amdgcn_sched_barrier(0);
+        load_v(t_begin, tab_cur);
+    }
+    for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
+        if constexpr (!AHEAD) {
+            load_k(t0, tab_cur);
+            load_v(t0, tab_cur);
+            tab_cur = table_of(t0 + kTile);
+        }
         // ---- S^T = K Q^T: lane holds keys t0 + 16mt + 4q + j of its rows --------------
         floatx4_t sacc[NC][4];
 #pragma unroll
@@ -161,6 +189,12 @@ __device__ __forceinline__ void attend_mq(const DecodeArgs& a, int s, int h, int
                 for (int c = 0; c < P::KC; ++c)
                     sacc[cg][mt] = mfma16(kreg[mt][c], qreg[cg][c], sacc[cg][mt]);
             }
+        if constexpr (AHEAD) {
+            // the next tile's K, then the block ids of the one after it
+            load_k(t0 + kTile, tab_next);
+            tab_cur = tab_next;
+            tab_next = table_of(t0 + 2 * kTile);
+        }
 
         // ---- online softmax over each row's 64 keys (4 lanes x 16) -------------------
         const bool full = t0 + kTile - 1 <= ctx - nq;    // every key visible to every row
@@ -224,18 +258,29 @@ __device__ __forceinline__ void attend_mq(const DecodeArgs& a, int s, int h, int
                 }
             }
         }
+        // the next tile's V (tab_cur now holds its block ids)
+        if constexpr (AHEAD) load_v(t0 + kTile, tab_cur);
         __syncthreads();
 
         // ---- O^T += V^T P^T (each V^T operand serves every column group) ---------------
+        // operand i = (dt, s2) = (i / 2, i % 2); the LDS reads run kAhead operands ahead
+        // of the products, so a product does not wait for its own read
+        constexpr int kOps = P::DT * 2, kAhead = 4;
+        auto vt_operand = [&](int i) {
+            return *reinterpret_cast<const u32x4*>(
+                lds_vt + mq_vt_off<D>((i >> 1) * 16 + n, 4 * (i & 1) + q));
+        };
+        u32x4 vbuf[kAhead];
 #pragma unroll
-        for (int dt = 0; dt < P::DT; ++dt)
+        for (int i = 0; i < kAhead; ++i) vbuf[i] = vt_operand(i);
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                const u32x4 va = *reinterpret_cast<const u32x4*>(
-                    lds_vt + mq_vt_off<D>(dt * 16 + n, 4 * s2 + q));
+        for (int i = 0; i < kOps; ++i) {
+            const u32x4 va = vbuf[i % kAhead];
+            if (i + kAhead < kOps) vbuf[i % kAhead] = vt_operand(i + kAhead);
 #pragma unroll
-                for (int cg = 0; cg < NC; ++cg) o[cg][dt] = mfma16(va, pk[cg][s2], o[cg][dt]);
-            }
+            for (int cg = 0; cg < NC; ++cg)
+                o[cg][i >> 1] = mfma16(va, pk[cg][i & 1], o[cg][i >> 1]);
+        }
     }
 #pragma unroll
     for (int cg = 0; cg < NC; ++cg) {
