@@ -356,8 +356,8 @@ __global__ __launch_bounds__(64, (BF16 ? 2 : 1)) void decode_balanced_kernel(Dec
     // units = 64-token tiles, ordered by (sequence, kv head, tile); with W <= T every
     // wave's range [wT/W, (w+1)T/W) is non-empty
     int64_t tiles_all, unused;
-    int first[4];
-    count_tiles<PREFIX>(a, 0, tiles_all, unused, first);
+    int first[4], first_ctx[4];
+    count_tiles<PREFIX>(a, 0, tiles_all, unused, first, first_ctx);
     const int64_t T = tiles_all * Hkv;
     const int64_t W = min((int64_t)a.num_waves, T);
     if (w >= W) return;
@@ -367,7 +367,10 @@ __global__ __launch_bounds__(64, (BF16 ? 2 : 1)) void decode_balanced_kernel(Dec
     int s = 0;
     int64_t before = 0;
     locate_unit<PREFIX>(a, b, Hkv, first, s, before);
-    int nt_s = unit_tiles<PREFIX>(a, s);
+    // the first unit's counts come from the registers count_tiles filled (no round trip
+    // before the first loads); later units reload theirs
+    int nt_s = s < 256 ? lane_value(first, s) : unit_tiles<PREFIX>(a, s);
+    int ctx = s < 256 ? lane_value(first_ctx, s) : clamp_ctx(a, a.context_lens[s]);
     const int64_t rel = b - before * Hkv;
     int h = (int)(rel / nt_s);
     int tile = (int)(rel - (int64_t)h * nt_s);
@@ -375,7 +378,6 @@ __global__ __launch_bounds__(64, (BF16 ? 2 : 1)) void decode_balanced_kernel(Dec
     SegState<BF16, D, G> st;
     while (remaining > 0) {
         const int seg = (int)min((int64_t)(nt_s - tile), remaining);
-        const int ctx = clamp_ctx(a, a.context_lens[s]);
         const int t_first = seq_start<PREFIX>(a, s, ctx);    // 0 unless in the prefix mode
         attend_segment<BF16, D, G, CONTIG>(a, s, s, h, ctx, t_first + tile * kTile,
                                            min(ctx, t_first + (tile + seg) * kTile), lds_k, lds_p,
@@ -411,6 +413,7 @@ __global__ __launch_bounds__(64, (BF16 ? 2 : 1)) void decode_balanced_kernel(Dec
                     ++s;
                     nt_s = unit_tiles<PREFIX>(a, s);
                 } while (nt_s == 0);
+                ctx = clamp_ctx(a, a.context_lens[s]);
             }
         }
     }

@@ -346,8 +346,8 @@ __global__ __launch_bounds__(64, 3 - NC) void decode_mq_kernel(DecodeArgs a, int
     const int rows = nq * G;
 
     int64_t tiles_all, unused;
-    int first[4];
-    count_tiles(a, 0, tiles_all, unused, first);
+    int first[4], first_ctx[4];
+    count_tiles(a, 0, tiles_all, unused, first, first_ctx);
     const int64_t T = tiles_all * Hkv;
     const int64_t W = min((int64_t)a.num_waves, T);
     if (w >= W) return;
@@ -357,7 +357,9 @@ __global__ __launch_bounds__(64, 3 - NC) void decode_mq_kernel(DecodeArgs a, int
     int s = 0;
     int64_t before = 0;
     locate_unit(a, b, Hkv, first, s, before);
-    int nt_s = unit_tiles<false>(a, s);
+    // the first unit's counts come from the registers count_tiles filled
+    int nt_s = s < 256 ? lane_value(first, s) : unit_tiles<false>(a, s);
+    int ctx = s < 256 ? lane_value(first_ctx, s) : clamp_ctx(a, a.context_lens[s]);
     const int64_t rel = b - before * Hkv;
     int h = (int)(rel / nt_s);
     int tile = (int)(rel - (int64_t)h * nt_s);
@@ -365,7 +367,6 @@ __global__ __launch_bounds__(64, 3 - NC) void decode_mq_kernel(DecodeArgs a, int
     MqState<D, NC> st;
     while (remaining > 0) {
         const int seg = (int)min((int64_t)(nt_s - tile), remaining);
-        const int ctx = clamp_ctx(a, a.context_lens[s]);
         attend_mq<D, G, NC>(a, s, h, ctx, nq, tile * kTile, min(ctx, (tile + seg) * kTile), lds_vt,
                             st);
         if (tile == 0) record_unit(a, sp, w, s, h, e - remaining, nt_s, seg == nt_s);
@@ -385,6 +386,7 @@ __global__ __launch_bounds__(64, 3 - NC) void decode_mq_kernel(DecodeArgs a, int
                     ++s;
                     nt_s = unit_tiles<false>(a, s);
                 } while (nt_s == 0);
+                ctx = clamp_ctx(a, a.context_lens[s]);
             }
         }
     }

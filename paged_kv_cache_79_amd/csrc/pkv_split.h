@@ -55,24 +55,30 @@ __device__ __forceinline__ int unit_tiles(const DecodeArgs& a, int s) {
 }
 
 // Tiles of the whole batch (all sequences, one kv head) and tiles before sequence `upto`.
-// Four chunks of 64 sequences per pass, their loads issued together; the counts of
-// the first 256 sequences stay in first[q] (sequence 64q + lane) for locate_unit.
+// Four chunks of 64 sequences per pass, their loads issued together; the tile counts
+// and clamped lengths of the first 256 sequences stay in first[q] and first_ctx[q]
+// (sequence 64q + lane) for locate_unit and the wave's first unit.
 template <bool PREFIX = false>
 __device__ __forceinline__ void count_tiles(const DecodeArgs& a, int upto, int64_t& total,
-                                            int64_t& before, int (&first)[4]) {
+                                            int64_t& before, int (&first)[4],
+                                            int (&first_ctx)[4]) {
     const int lane = threadIdx.x & 63;   // lane of the wave (the merge runs several per workgroup)
     total = 0;
     before = 0;
     for (int c0 = 0; c0 < a.num_seqs; c0 += 256) {
-        int nt[4];
+        int nt[4], cl[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int sl = c0 + q * 64 + lane;
-            nt[q] = sl < a.num_seqs ? unit_tiles<PREFIX>(a, sl) : 0;
+            cl[q] = sl < a.num_seqs ? clamp_ctx(a, a.context_lens[sl]) : 0;
+            nt[q] = sl < a.num_seqs ? ntiles_of(cl[q] - seq_start<PREFIX>(a, sl, cl[q])) : 0;
         }
         if (c0 == 0) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) first[q] = nt[q];
+            for (int q = 0; q < 4; ++q) {
+                first[q] = nt[q];
+                first_ctx[q] = cl[q];
+            }
         }
         int t = 0, u = 0;
 #pragma unroll
@@ -84,11 +90,12 @@ __device__ __forceinline__ void count_tiles(const DecodeArgs& a, int upto, int64
         before += wave_sum_int(u);
     }
 }
-template <bool PREFIX = false>
-__device__ __forceinline__ void count_tiles(const DecodeArgs& a, int upto, int64_t& total,
-                                            int64_t& before) {
-    int first[4];
-    count_tiles<PREFIX>(a, upto, total, before, first);
+// Value of uniform sequence s < 256 among per-lane values kept as count_tiles keeps them
+// (sequence 64q + lane in v[q]): no memory access.
+__device__ __forceinline__ int lane_value(const int (&v)[4], int s) {
+    const int q = s >> 6;
+    const int x = q == 0 ? v[0] : q == 1 ? v[1] : q == 2 ? v[2] : v[3];
+    return __builtin_amdgcn_readlane(x, s & 63);
 }
 
 // Share of the tiles each wave gets, by the XCD it runs on (in 1/256).  The dispatcher
