@@ -66,15 +66,49 @@ struct SegState {
     float m[G], l[G], o[G][DecodeShape<BF16, D>::EPC];
 };
 
+// What a segment loads before its first tile: the block ids of that tile (lane j: block
+// t_begin / bs + j) and the G query rows of (s_q, h), this lane's 16-byte chunks
+// lane + 64 i.  The balanced kernel loads the next segment's while it attends the
+// current one, so a wave moving on to the next kv head of its sequence does not wait
+// for them.
+template <bool BF16, int D, int G>
+struct SegInputs {
+    static constexpr int QC = G * DecodeShape<BF16, D>::RB / 16;   // 16-byte chunks of the rows
+    static constexpr int QN = (QC + 63) / 64;
+    int tab;
+    u32x4 q[QN];
+};
+// nblk: table entries the reads may touch (the sequence's blocks, or the whole row when
+// the length is not at hand; entries past the context are never used).
+template <bool BF16, int D, int G, bool CONTIG = false>
+__device__ __forceinline__ void load_seg_inputs(const DecodeArgs& a, int s, int s_q, int h, int nblk,
+                                                int t_begin, SegInputs<BF16, D, G>& in) {
+    using I = SegInputs<BF16, D, G>;
+    const int lane = threadIdx.x;
+    if constexpr (CONTIG) {
+        in.tab = 0;
+    } else {
+        in.tab = load_tile_table(a.block_tables + (int64_t)s * a.max_blocks_per_seq, t_begin,
+                                 a.g.log2_bs, nblk, lane);
+    }
+    const u32x4* qsrc = reinterpret_cast<const u32x4*>(
+        reinterpret_cast<const char*>(a.q) +
+        ((int64_t)s_q * a.num_q_heads + h * G) * DecodeShape<BF16, D>::RB);
+#pragma unroll
+    for (int i = 0; i < I::QN; ++i) in.q[i] = qsrc[min(lane + 64 * i, I::QC - 1)];
+}
+
 // Attend the G query heads of (s, h) to tokens [t_begin, t_end) of the sequence.
 // CONTIG: the unpaged baseline -- K/V in the contiguous [S][L][Hkv][D] layout, no table.
 // s picks the block-table row (or slab), s_q the query row (the same but for chunked
 // prefill, where the queries of one chunk share its table).
+// `in`: the segment's inputs, loaded by the caller (null: loaded here).
 template <bool BF16, int D, int G, bool CONTIG = false>
 __device__ __forceinline__ void attend_segment(const DecodeArgs& a, int s, int s_q, int h, int ctx,
                                                int t_begin, int t_end, char* lds_k,
                                                uint32_t* lds_p, uint32_t* lds_q,
-                                               SegState<BF16, D, G>& st) {
+                                               SegState<BF16, D, G>& st,
+                                               const SegInputs<BF16, D, G>* in = nullptr) {
     using S = DecodeShape<BF16, D>;
     const int lane = threadIdx.x;
     const int bs = a.g.block_size;
@@ -92,13 +126,19 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, int s, int s
     const char* kb = (const char*)pin_uniform(a.k_pool + head_base);
     const char* vb = (const char*)pin_uniform(a.v_pool + head_base);
 
-    int tab_cur = CONTIG ? 0 : load_tile_table(table, t_begin, a.g.log2_bs, nblk, lane);
+    using I = SegInputs<BF16, D, G>;
+    SegInputs<BF16, D, G> own;
+    if (in == nullptr) {
+        load_seg_inputs<BF16, D, G, CONTIG>(a, s, s_q, h, nblk, t_begin, own);
+        in = &own;
+    }
+    int tab_cur = in->tab;
     __syncthreads();  // the previous segment is done with lds_q
     {
-        const u32x4* qsrc = reinterpret_cast<const u32x4*>(
-            reinterpret_cast<const char*>(a.q) + ((int64_t)s_q * a.num_q_heads + h * G) * S::RB);
         u32x4* qdst = reinterpret_cast<u32x4*>(lds_q);
-        for (int c = lane; c < G * S::RB / 16; c += 64) qdst[c] = qsrc[c];
+#pragma unroll
+        for (int i = 0; i < I::QN; ++i)
+            if (lane + 64 * i < I::QC) qdst[lane + 64 * i] = in->q[i];
     }
 
     float m[G], l[G], o[G][S::EPC];
@@ -376,12 +416,22 @@ __global__ __launch_bounds__(64, (BF16 ? 2 : 1)) void decode_balanced_kernel(Dec
     int tile = (int)(rel - (int64_t)h * nt_s);
     int64_t remaining = e - b;
     SegState<BF16, D, G> st;
+    // Inputs of the current segment when the previous one loaded them, and of the next
+    // kv head of the same sequence (same table row and length), loaded ahead.  (Loading
+    // the next sequence's ahead as well measured no faster and needs more registers.)
+    SegInputs<BF16, D, G> in_cur, in_next;
+    bool have_cur = false;
     while (remaining > 0) {
         const int seg = (int)min((int64_t)(nt_s - tile), remaining);
         const int t_first = seq_start<PREFIX>(a, s, ctx);    // 0 unless in the prefix mode
+        const int nblk = (ctx + a.g.block_size - 1) >> a.g.log2_bs;
+        if (!have_cur)
+            load_seg_inputs<BF16, D, G, CONTIG>(a, s, s, h, nblk, t_first + tile * kTile, in_cur);
+        const bool ahead = remaining > seg && h + 1 < Hkv;    // uniform
+        if (ahead) load_seg_inputs<BF16, D, G, CONTIG>(a, s, s, h + 1, nblk, t_first, in_next);
         attend_segment<BF16, D, G, CONTIG>(a, s, s, h, ctx, t_first + tile * kTile,
                                            min(ctx, t_first + (tile + seg) * kTile), lds_k, lds_p,
-                                           lds_q, st);
+                                           lds_q, st, &in_cur);
         // the wave holding a unit's first tile tells the merge where its pieces are
         if (tile == 0) record_unit(a, sp, w, s, h, e - remaining, nt_s, seg == nt_s);
         if (tile == 0 && seg == nt_s) {
@@ -405,6 +455,8 @@ __global__ __launch_bounds__(64, (BF16 ? 2 : 1)) void decode_balanced_kernel(Dec
             write_partial<BF16, D, G>(a, (w * 2 + (tile == 0 ? 1 : 0)) * G, 1, st);
         }
         remaining -= seg;
+        have_cur = ahead;
+        if (ahead) in_cur = in_next;
         if (remaining > 0) {
             tile = 0;
             if (++h == Hkv) {
