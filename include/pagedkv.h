@@ -172,8 +172,9 @@ pkv_status paged_attention_decode(pkv_dtype dtype, void* out, const void* q,
  *   - PKV_ERR_WORKSPACE (nothing launched) when the call would need more workspace
  *     than that (paged_attention_decode_workspace_bytes() > the scratch size): the
  *     default split needs at most 2 * 8 * num_compute_units * G * (head_dim + 2) * 4
- *     bytes (17 MB at G = 8, head_dim 128 on 256 compute units); fixed partitions
- *     need num_seqs * num_q_heads * partitions * (head_dim + 2) * 4.
+ *     bytes (17 MB at G = 8, head_dim 128 on 256 compute units) plus 8 bytes per
+ *     (sequence, kv head); fixed partitions need
+ *     num_seqs * num_q_heads * partitions * (head_dim + 2) * 4.
  *   - Every call on a device shares that device's scratch: calls that overlap in
  *     time on one device (other streams, other threads) race and give unspecified
  *     output.  Calls ordered on one stream are fine.  The scratch keeps the last
