@@ -250,6 +250,15 @@ def test_validate_validation(lib):
     assert f(8, 16, None, 0, None, 0, None, 0, None, 2, P, None) == NULL  # pairs missing
 
 
+def test_validate_chunks_validation(lib):
+    f = lib.pkv_validate_chunks
+    assert f(P, P, -1, -1, P, None) == SHAPE          # negative chunk count
+    assert f(P, P, 3, -1, None, None) == NULL         # no count
+    assert f(None, P, 3, -1, P, None) == NULL         # cu_q_lens missing
+    assert f(P, None, 3, 10, P, None) == NULL         # context lengths missing
+    assert f(None, None, 0, 0, P, None) == OK         # nothing to check, nothing enqueued
+
+
 @dummy_ptrs
 def test_prefill_validation(lib):
     f = lib.paged_attention_prefill_chunk
