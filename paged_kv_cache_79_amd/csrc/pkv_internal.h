@@ -51,7 +51,7 @@ struct SwapArgs {
 
 // Most key splits of a shared prefix (the prefix pass writes one partial state per
 // split; the merge reads them with all loads in flight at once).
-constexpr int kMaxPreSplits = 8;
+constexpr int kMaxPreSplits = 4;
 
 struct DecodeArgs {
     void* out;
