@@ -337,7 +337,9 @@ def run_spec(args):
         "kv_bytes_per_step": byts,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic("spec") if mq and pre.block_size == 16 else None,
+                     # the counters were taken on the default batch (block 16, 3 drafts)
+                     "traffic": recorded_traffic("spec")
+                     if mq and pre.block_size == 16 and sb.draft == 3 else None,
                      "kernel": ("paged_attention_decode_multi_query (attention kernel + merge "
                                 "kernel)" if mq else
                                 "paged_attention_prefill_chunk with k + 1 queries per sequence"),
