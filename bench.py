@@ -124,26 +124,27 @@ def oracle_pool():
     return mp.get_context("fork").Pool(used), avail, used
 
 
-def cpu_baseline(pool, avail, used, name, target_s=8.0):
+def cpu_baseline(pool, avail, used, name, target_cpu_s=20.0):
     """Time the oracle's decode of the batch registered as `name` on this host: one
-    sequence per task over the worker pool, passes repeated until about target_s."""
+    sequence per task over the worker pool, whole passes over the batch repeated until
+    about target_cpu_s of CPU work (wall time x workers)."""
     b = _ORACLE_BATCHES[name][0]
-    # one single-process pass over a few sequences estimates the per-sequence cost
+    units = [(name, s) for s in range(b.num_seqs)]
+    # an untimed pass warms the workers up; the first timed pass sizes the sample:
+    # whole passes until about target_cpu_s
+    pool.map(_oracle_unit, units, chunksize=1)
     t0 = time.perf_counter()
-    probe = list(range(min(2, b.num_seqs)))
-    for s in probe:
-        _oracle_unit((name, s))
-    per_seq = (time.perf_counter() - t0) / len(probe)
-    est_pass = per_seq * b.num_seqs / used
-    passes = max(1, min(8, int(math.ceil(target_s / max(est_pass, 1e-3)))))
-    t0 = time.perf_counter()
-    for _ in range(passes):
-        pool.map(_oracle_unit, [(name, s) for s in range(b.num_seqs)], chunksize=1)
+    pool.map(_oracle_unit, units, chunksize=1)
+    first = time.perf_counter() - t0
+    passes = max(1, min(64, int(round(target_cpu_s / max(first * used, 1e-3)))))
+    for _ in range(passes - 1):
+        pool.map(_oracle_unit, units, chunksize=1)
     wall = time.perf_counter() - t0
     byts = passes * kv_bytes(b.context_lens, b.num_kv_heads, b.head_dim, 2 if b.dtype == "bf16" else 4)
     return {"value": round(byts / wall / 1e9, 4), "unit": "GB/s", "cores": used,
             "cores_available": avail, "kind": "oracle",
             "seqs_per_s": round(passes * b.num_seqs / wall, 2), "wall_s": round(wall, 2),
+            "cpu_s": round(wall * used, 1),
             "sample": f"{passes} pass(es) of fp64 numpy decode over all {b.num_seqs} sequences of "
                       f"the {b.name} batch, one sequence per task on {used} worker processes "
                       f"({avail} cores in the affinity mask, {CPU_SHARE} the job's share)"}
