@@ -140,6 +140,14 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, int s, int s
         for (int i = 0; i < I::QN; ++i)
             if (lane + 64 * i < I::QC) qdst[lane + 64 * i] = in->q[i];
     }
+    // bf16: QK runs on the matrix cores (16x16x32 MFMA, S^T = K Q^T with the G heads in
+    // the first G of 16 columns).  Lane 16 qq + n takes, for k-step c, elements
+    // 32c + 8qq .. +7 of head n's q row as the B operand; the columns past G repeat the
+    // last head (finite values whose scores nothing reads).
+    constexpr int KC = D / 32;
+    const int qn = lane & 15, qq = lane >> 4;
+    const char* qcol = reinterpret_cast<const char*>(lds_q) + min(qn, G - 1) * S::RB + qq * 16;
+    float mh = kNoMax, ll = 0.f;   // bf16: running max and per-lane sum of head qn
 
     float m[G], l[G], o[G][S::EPC];
 #pragma unroll
@@ -202,6 +210,55 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, int s, int s
             *reinterpret_cast<u32x4*>(lds_k + (i * S::R + ra) * S::KPITCH + rc * 16) = kreg[i];
         __syncthreads();
 
+        float alpha[G];
+        if constexpr (BF16) {
+            // ---- 2. QK: S^T = K Q^T; lane 16qq + n ends with head n's scores of keys
+            //         16mt + 4qq + j (mt, j < 4)
+            floatx4_t sacc[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                sacc[mt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < KC; ++c) {
+                    const u32x4 ka = *reinterpret_cast<const u32x4*>(
+                        lds_k + (16 * mt + qn) * S::KPITCH + c * 64 + qq * 16);
+                    const u32x4 qb = *reinterpret_cast<const u32x4*>(qcol + c * 64);
+                    sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, ka), __builtin_bit_cast(bf16x8_t, qb),
+                        sacc[mt], 0, 0, 0);
+                }
+            }
+            // ---- 3. online softmax of head qn over the lanes qn, 16 + qn, 32 + qn, 48 + qn
+            float mx = -INFINITY;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const bool valid = t0 + 16 * mt + 4 * qq + j < t_end;
+                    const float sc = valid ? sacc[mt][j] * a.scale_log2 : -INFINITY;
+                    sacc[mt][j] = sc;
+                    mx = fmaxf(mx, sc);
+                }
+            mx = swap32_max(swap16_max(mx));
+            const float mn = fmaxf(mh, mx);
+            const float al = fast_exp2(mh - mn);
+            mh = mn;
+            float ps = 0.f;
+            // keys t and t + 16 (mt = 2mp, 2mp + 1) share one dword of the probabilities,
+            // the pairing the P.V step reads
+#pragma unroll
+            for (int mp = 0; mp < 2; ++mp)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float p0 = fast_exp2(sacc[2 * mp][j] - mn);
+                    const float p1 = fast_exp2(sacc[2 * mp + 1][j] - mn);
+                    ps += p0 + p1;
+                    if (qn < G) lds_p[(mp * 16 + 4 * qq + j) * 8 + qn] = pack_bf16(p0, p1);
+                }
+            ll = fmaf(ll, al, ps);
+#pragma unroll
+            for (int hh = 0; hh < G; ++hh) alpha[hh] = u2f(__builtin_amdgcn_readlane(f2u(al), hh));
+        } else {
         // ---- 2. QK: lane = token ------------------------------------------------
         float acc[G];
 #pragma unroll
@@ -236,7 +293,6 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, int s, int s
 
         // ---- 3. online softmax ------------------------------------------------------
         const bool valid = (t0 + lane) < t_end;
-        float alpha[G];
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
             const float sc = valid ? acc[hh] * a.scale_log2 : -INFINITY;
@@ -254,6 +310,7 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, int s, int s
                 reinterpret_cast<float*>(lds_p)[lane * 8 + hh] = p;
             }
         }
+        }
         __syncthreads();
 
         // ---- 4. PV ------------------------------------------------------------------
@@ -267,10 +324,13 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, int s, int s
 #pragma unroll
             for (int e = 0; e < S::EPC; ++e) o[hh][e] *= alpha[hh];
         if constexpr (BF16) {
+            constexpr int PS = 16 / S::R;      // loads between tokens t and t + 16
 #pragma unroll
             for (int ii = 0; ii < S::NL / 2; ++ii) {
-                const u32x4 v0 = vreg[2 * ii], v1 = vreg[2 * ii + 1];
-                const uint32_t* pp = lds_p + (ii * S::R + ra) * 8;
+                const int i0 = (ii / PS) * 2 * PS + ii % PS;
+                const int tk = i0 * S::R + ra;        // token of load i0: 0..15 or 32..47
+                const u32x4 v0 = vreg[i0], v1 = vreg[i0 + PS];
+                const uint32_t* pp = lds_p + ((tk >> 5) * 16 + (tk & 15)) * 8;
                 const u32x4 pa = *reinterpret_cast<const u32x4*>(pp);
                 const u32x4 pz = *reinterpret_cast<const u32x4*>(pp + 4);
                 const uint32_t pk[8] = {pa.x, pa.y, pa.z, pa.w, pz.x, pz.y, pz.z, pz.w};
@@ -304,10 +364,16 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, int s, int s
     }
 
     // ---- combine lanes: per-lane sums, then the row groups sharing a chunk -----------
+    const float lsum = swap32_sum(swap16_sum(ll));   // bf16: head qn's total in its lanes
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-        st.m[hh] = m[hh];
-        st.l[hh] = wave_sum(l[hh]);
+        if constexpr (BF16) {
+            st.m[hh] = u2f(__builtin_amdgcn_readlane(f2u(mh), hh));
+            st.l[hh] = u2f(__builtin_amdgcn_readlane(f2u(lsum), hh));
+        } else {
+            st.m[hh] = m[hh];
+            st.l[hh] = wave_sum(l[hh]);
+        }
 #pragma unroll
         for (int e = 0; e < S::EPC; ++e) st.o[hh][e] = group_sum<S::R>(o[hh][e]);
     }
