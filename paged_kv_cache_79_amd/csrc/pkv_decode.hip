@@ -11,15 +11,18 @@
 //              order, so one wave instruction covers 1 KiB of contiguous K (or V)
 //              of one block; the tile's block ids arrive with one vector load
 //              (issued a tile ahead) and are taken with readlane into scalar bases;
-//   2. QK      K is restaged through LDS so that lane t owns token t of the
-//              tile and forms the dot products of all G query heads of its
-//              group (grouped-query packing: one K read serves G heads) with q
-//              broadcast from LDS -- no cross-lane reduction;
-//   3. softmax tile maximum by DPP row rotations + permlane swaps; running max
-//              per head, per-lane running sums (summed once per segment);
+//   2. QK      K is restaged through LDS.  bf16: S^T = K Q^T on 16x16x32 MFMAs,
+//              the tile's K rows as the A operand and the G query heads of the
+//              group in the first G of 16 B-operand columns (grouped-query
+//              packing: one K read serves G heads); lane 16qq + n ends with head
+//              n's scores of 16 keys.  fp32: lane t owns token t and forms the G
+//              dot products against q broadcast from LDS;
+//   3. softmax bf16: per head over its four lanes (two permlane swaps); fp32: tile
+//              maximum by DPP row rotations + permlane swaps; running max per
+//              head, per-lane running sums (summed once per segment);
 //   4. PV      V stays in the load layout (lane = 8 elements of one token row);
-//              bf16 probabilities of two tokens are paired with the matching V
-//              halves (byte permute) and accumulated with v_dot2.
+//              bf16 probabilities of tokens t and t + 16 are paired with the
+//              matching V halves (byte permute) and accumulated with v_dot2.
 // Tokens at or beyond the valid length are removed by selection (score -inf,
 // V row zero), never by arithmetic, so stale or NaN slots cannot leak in.
 //
