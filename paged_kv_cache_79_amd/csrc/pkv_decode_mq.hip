@@ -18,9 +18,9 @@
 //                   registers for the whole segment;
 //   softmax         a lane holds 16 keys of its row: lane-local max and sum plus
 //                   two permlane swaps across the four lanes of the row;
-//   O^T += V^T P^T  P^T is the S^T registers converted to bf16 in place; V^T is
-//                   staged through LDS, written transposed with keys permuted to
-//                   match P^T's register order.
+//   O^T += V^T P^T  P^T is the S^T registers converted to bf16 in place; V is
+//                   staged through LDS row-major and read transposed (gfx950
+//                   ds_read_b64_tr_b16), keys in P^T's register order.
 // Straddling (sequence, kv head) pairs leave partial states that the balanced
 // merge combines, as for decode.
 #include <mutex>
@@ -36,24 +36,19 @@ struct MqShape {
     static constexpr int DT = D / 16;                // 16-row tiles of O^T
     static constexpr int CPR = RB / 16;              // 16-byte chunks per row
     static constexpr int VJ = CPR / 8;               // chunks per key per lane in the V load
-    static constexpr int VPITCH = kTile * 2 + 16;    // bytes of a V^T row in LDS
+    static constexpr int VPITCH = RB + 32;           // bytes of a V row in LDS (72 dwords)
     static constexpr int ROWS = 16;                  // MFMA columns: query rows per column group
 };
 
-// Slot of key kk (0..63) in the V^T tile.  Within a group of 32 keys, the S^T
-// registers of lane 16q + n hold keys 4q + j and 16 + 4q + j (j < 4), which the PV
-// product takes as B-operand slots 8q + j and 8q + 4 + j.
-__device__ __forceinline__ int mq_slot(int kk) {
-    return (kk & 32) | (((kk & 15) >> 2) << 3) | (((kk >> 4) & 1) << 2) | (kk & 3);
-}
-
-// Byte offset of slot group g (8 slots, 16 bytes) of V^T row d; groups are
-// XOR-swizzled by d / 8 so that the transposing writes of rows 8 apart spread over
-// the banks.
-template <int D>
-__device__ __forceinline__ int mq_vt_off(int d, int g) {
-    return d * MqShape<D>::VPITCH + ((g ^ ((d >> 3) & 7)) << 4);
-}
+// The V tile sits in LDS row-major (key rows at a 288-byte pitch for D = 128: four
+// consecutive rows start 8 banks apart).  The P.V product's A operand is V^T: lane
+// 16q + n needs elements d = 16dt + n of the 8 keys of B-operand slots 8q .. 8q + 7,
+// which hold keys 4q + j and 16 + 4q + j (j < 4) of the 32-key half, the order the
+// S^T registers give the probabilities.  ds_read_b64_tr_b16 gives lane i of each 16
+// lanes element i mod 4 of the 8-byte chunks addressed by lanes 4r + i / 4 (r < 4), so
+// lane 4r + m of group q addresses key (4q + r) [+ 16], elements 16dt + 4m .. + 3.
+typedef short mq_v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) mq_v4i16 mq_lds_v4i16;
 
 // NC groups of 16 rows: the 16 columns of the matrix tiles hold rows n (NC = 1) or
 // n and 16 + n (NC = 2, up to 32 rows: 8 queries x 4 heads), sharing every K and V^T
@@ -236,28 +231,16 @@ __device__ __forceinline__ void attend_mq(const DecodeArgs& a, int s, int h, int
             }
         }
 
-        // ---- V^T into LDS: keys 2m, 2m+1 share a dword of each V^T row ----------------
-        __syncthreads();               // the previous tile's V^T reads are done
+        // ---- the V tile into LDS, row-major ----------------------------------------------
+        __syncthreads();               // the previous tile's V reads are done
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int slot = mq_slot(2 * (8 * p + kp));
-            const int g = slot >> 3, within = (slot & 7) * 2;
+        for (int p = 0; p < 4; ++p)
 #pragma unroll
-            for (int j = 0; j < P::VJ; ++j) {
-                const u32x4 x0 = vreg[p][0][j], x1 = vreg[p][1][j];
-                const uint32_t a0[4] = {x0.x, x0.y, x0.z, x0.w};
-                const uint32_t a1[4] = {x1.x, x1.y, x1.z, x1.w};
-                const int dbase = (c0 + 8 * j) * 8;
+            for (int r = 0; r < 2; ++r)
 #pragma unroll
-                for (int w2 = 0; w2 < 4; ++w2) {
-                    const int d = dbase + 2 * w2;
-                    *reinterpret_cast<uint32_t*>(lds_vt + mq_vt_off<D>(d, g) + within) =
-                        pair_lo(a0[w2], a1[w2]);
-                    *reinterpret_cast<uint32_t*>(lds_vt + mq_vt_off<D>(d + 1, g) + within) =
-                        pair_hi(a0[w2], a1[w2]);
-                }
-            }
-        }
+                for (int j = 0; j < P::VJ; ++j)
+                    *reinterpret_cast<u32x4*>(lds_vt + (2 * (8 * p + kp) + r) * P::VPITCH +
+                                              (c0 + 8 * j) * 16) = vreg[p][r][j];
         // the next tile's V (tab_cur now holds its block ids)
         if constexpr (AHEAD) load_v(t0 + kTile, tab_cur);
         __syncthreads();
@@ -267,8 +250,14 @@ __device__ __forceinline__ void attend_mq(const DecodeArgs& a, int s, int h, int
         // of the products, so a product does not wait for its own read
         constexpr int kOps = P::DT * 2, kAhead = 4;
         auto vt_operand = [&](int i) {
-            return *reinterpret_cast<const u32x4*>(
-                lds_vt + mq_vt_off<D>((i >> 1) * 16 + n, 4 * (i & 1) + q));
+            const int dt = i >> 1, s2 = i & 1;
+            const char* row = lds_vt + (32 * s2 + 4 * q + (n >> 2)) * P::VPITCH +
+                              (16 * dt + 4 * (n & 3)) * 2;
+            const mq_v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((mq_lds_v4i16*)row);
+            const mq_v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (mq_lds_v4i16*)(row + 16 * P::VPITCH));
+            const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+            return u32x4{l2.x, l2.y, h2.x, h2.y};
         };
         u32x4 vbuf[kAhead];
 #pragma unroll
@@ -340,7 +329,7 @@ __device__ __forceinline__ void write_mq_partial(const DecodeArgs& a, int64_t pr
 // NC = 1: two waves per SIMD; NC = 2 doubles the accumulators and runs one wave per SIMD.
 template <int D, int G, int NC>
 __global__ __launch_bounds__(64, 3 - NC) void decode_mq_kernel(DecodeArgs a, int nq) {
-    __shared__ __attribute__((aligned(16))) char lds_vt[D * MqShape<D>::VPITCH];
+    __shared__ __attribute__((aligned(16))) char lds_vt[kTile * MqShape<D>::VPITCH];
     const int64_t w = blockIdx.x;
     const int Hkv = a.g.num_kv_heads;
     const int rows = nq * G;
