@@ -20,9 +20,13 @@
 //   3. softmax bf16: per head over its four lanes (two permlane swaps); fp32: tile
 //              maximum by DPP row rotations + permlane swaps; running max per
 //              head, per-lane running sums (summed once per segment);
-//   4. PV      V stays in the load layout (lane = 8 elements of one token row);
-//              bf16 probabilities of tokens t and t + 16 are paired with the
-//              matching V halves (byte permute) and accumulated with v_dot2.
+//   4. PV      bf16: O^T += V^T P^T on 16x16x32 MFMAs.  P^T is the S^T registers
+//              rounded to bf16 (no LDS round trip); V is stored row-major into the
+//              K buffer once the scores are done and read transposed
+//              (ds_read_b64_tr_b16) in the key order of those registers; lane
+//              16qq + n ends with elements 16dt + 4qq + j of head n's output.
+//              fp32: V stays in the load layout (lane = 4 elements of one token
+//              row) and is accumulated with FMAs against probabilities from LDS.
 // Tokens at or beyond the valid length are removed by selection (score -inf,
 // V row zero), never by arithmetic, so stale or NaN slots cannot leak in.
 //
@@ -58,16 +62,37 @@ struct DecodeShape {
 
 template <bool BF16>
 struct DecodeLds {
-    static constexpr int PWORDS = BF16 ? kTile / 2 * 8 : kTile * 8;   // probabilities (dwords)
+    // fp32: the probabilities of a tile (dwords); bf16 keeps them in registers
+    static constexpr int PWORDS = BF16 ? 4 : kTile * 8;
 };
 
 // Softmax state of one segment of one (sequence, kv head) for its G query heads,
-// after the per-lane pieces have been combined: m and l are uniform; lanes of row
-// group 0 hold o for their 16-byte chunk of the head dimension.
+// after the per-lane pieces have been combined.  fp32: m and l are uniform; lanes of
+// row group 0 hold o for their 16-byte chunk of the head dimension.
 template <bool BF16, int D, int G>
 struct SegState {
     float m[G], l[G], o[G][DecodeShape<BF16, D>::EPC];
 };
+// bf16: lane 16 qq + n holds head n's max and sum, and O^T tile dt of the matrix-core
+// P.V product: elements d = 16 dt + 4 qq + j (j < 4) of head n's row.
+template <int D, int G>
+struct SegState<true, D, G> {
+    float m, l;
+    floatx4_t o[D / 16];
+};
+
+// The bf16 V tile sits in the K buffer once the scores are done: rows unpadded
+// (D * 2 bytes), 16-byte chunk c of key row k at chunk position c ^ v_swz(k).  The
+// P.V operand reads (ds_read_b64_tr_b16: per 16 lanes, 8 bytes from each of four
+// consecutive keys, four lanes per key) then fall on 64 distinct banks per 32 lanes,
+// and the row-wise stores stay conflict-free.
+template <int D>
+__device__ __forceinline__ int v_swz(int k) {
+    constexpr int RB = D * 2, RPL = 256 / RB, CPR = RB / 16;   // rows per 256 bytes
+    return 2 * ((k / RPL) & (CPR / 2 - 1));
+}
+typedef short dec_v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) dec_v4i16 dec_lds_v4i16;
 
 // What a segment loads before its first tile: the block ids of that tile (lane j: block
 // t_begin / bs + j) and the G query rows of (s_q, h), this lane's 16-byte chunks
@@ -160,6 +185,10 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, int s, int s
 #pragma unroll
         for (int e = 0; e < S::EPC; ++e) o[hh][e] = 0.f;
     }
+    // bf16: O^T of head qn, lane 16 qq + qn holding d = 16 dt + 4 qq + j
+    floatx4_t oacc[BF16 ? D / 16 : 1];
+#pragma unroll
+    for (int dt = 0; dt < (BF16 ? D / 16 : 1); ++dt) oacc[dt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
     for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
         // ---- 1. loads of this tile; the next tile's table entries go out after them
@@ -213,7 +242,6 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, int s, int s
             *reinterpret_cast<u32x4*>(lds_k + (i * S::R + ra) * S::KPITCH + rc * 16) = kreg[i];
         __syncthreads();
 
-        float alpha[G];
         if constexpr (BF16) {
             // ---- 2. QK: S^T = K Q^T; lane 16qq + n ends with head n's scores of keys
             //         16mt + 4qq + j (mt, j < 4)
@@ -246,118 +274,133 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, int s, int s
             const float mn = fmaxf(mh, mx);
             const float al = fast_exp2(mh - mn);
             mh = mn;
+            // P^T as the B operand of the P.V product, for each 32-key half ks: lane
+            // 16qq + n holds head n's probabilities of keys 32ks + 4qq + j and
+            // 32ks + 16 + 4qq + j (j < 4), straight from the S^T registers
             float ps = 0.f;
-            // keys t and t + 16 (mt = 2mp, 2mp + 1) share one dword of the probabilities,
-            // the pairing the P.V step reads
+            u32x4 pk[2];
 #pragma unroll
-            for (int mp = 0; mp < 2; ++mp)
+            for (int ks = 0; ks < 2; ++ks) {
+                float p[2][4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float p0 = fast_exp2(sacc[2 * mp][j] - mn);
-                    const float p1 = fast_exp2(sacc[2 * mp + 1][j] - mn);
-                    ps += p0 + p1;
-                    if (qn < G) lds_p[(mp * 16 + 4 * qq + j) * 8 + qn] = pack_bf16(p0, p1);
-                }
+                for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        p[hf][j] = fast_exp2(sacc[2 * ks + hf][j] - mn);
+                        ps += p[hf][j];
+                    }
+                pk[ks] = u32x4{pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3]),
+                               pack_bf16(p[1][0], p[1][1]), pack_bf16(p[1][2], p[1][3])};
+            }
             ll = fmaf(ll, al, ps);
+
+            // ---- 4. PV: O^T += V^T P^T on the matrix cores.  V goes into the K buffer
+            //         row-major (every K read of the tile is done), tail rows zeroed
+            __syncthreads();
+            if (t0 + kTile > t_end) {
 #pragma unroll
-            for (int hh = 0; hh < G; ++hh) alpha[hh] = u2f(__builtin_amdgcn_readlane(f2u(al), hh));
+                for (int i = 0; i < S::NL; ++i)
+                    if (t0 + i * S::R + ra >= t_end) vreg[i] = u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int i = 0; i < S::NL; ++i) {
+                const int row = i * S::R + ra;
+                *reinterpret_cast<u32x4*>(lds_k + row * S::RB + ((rc ^ v_swz<D>(row)) << 4)) =
+                    vreg[i];
+            }
+            __syncthreads();
+            if (__builtin_amdgcn_ballot_w64(al != 1.f)) {
+#pragma unroll
+                for (int dt = 0; dt < D / 16; ++dt) oacc[dt] *= al;
+            }
+            // operand i = (dt, ks) = (i / 2, i % 2): lane 16qq + n gets elements
+            // d = 16dt + n of the keys of B slots 8qq .. 8qq + 7 from two transposing
+            // reads (lane 4r + m of each 16 addresses key 32ks + 4qq + r [+ 16],
+            // elements 16dt + 4m .. + 3); the reads run four operands ahead
+            constexpr int kOps = (D / 16) * 2, kAhead = 4;
+            auto vt_operand = [&](int i) {
+                const int dt = i >> 1, ks = i & 1;
+                const int row = 32 * ks + 4 * qq + (qn >> 2);
+                const int c = 2 * dt + ((qn >> 1) & 1);
+                const char* ptr = lds_k + row * S::RB + ((c ^ v_swz<D>(row)) << 4) + (qn & 1) * 8;
+                const dec_v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((dec_lds_v4i16*)ptr);
+                const dec_v4i16 hi =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((dec_lds_v4i16*)(ptr + 16 * S::RB));
+                const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+                return u32x4{l2.x, l2.y, h2.x, h2.y};
+            };
+            u32x4 vbuf[kAhead];
+#pragma unroll
+            for (int i = 0; i < kAhead; ++i) vbuf[i] = vt_operand(i);
+#pragma unroll
+            for (int i = 0; i < kOps; ++i) {
+                const u32x4 va = vbuf[i % kAhead];
+                if (i + kAhead < kOps) vbuf[i % kAhead] = vt_operand(i + kAhead);
+                oacc[i >> 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, va), __builtin_bit_cast(bf16x8_t, pk[i & 1]),
+                    oacc[i >> 1], 0, 0, 0);
+            }
+            // the next tile's K store reuses the buffer
+            __syncthreads();
         } else {
-        // ---- 2. QK: lane = token ------------------------------------------------
-        float acc[G];
+            // ---- 2. QK (fp32): lane = token -------------------------------------------------
+            float acc[G];
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) acc[hh] = 0.f;
-        const char* krow = lds_k + lane * S::KPITCH;
-        // q is re-read from LDS every tile: an opaque zero offset stops the compiler from
-        // hoisting all G*D q values out of the loop into registers
-        uint32_t qoff = 0;
-        asm volatile("" : "+v"(qoff));
+            for (int hh = 0; hh < G; ++hh) acc[hh] = 0.f;
+            const char* krow = lds_k + lane * S::KPITCH;
+            // q is re-read from LDS every tile: an opaque zero offset stops the compiler
+            // from hoisting all G*D q values out of the loop into registers
+            uint32_t qoff = 0;
+            asm volatile("" : "+v"(qoff));
 #pragma unroll
-        for (int j = 0; j < S::CPR; ++j) {
-            const u32x4 kk = *reinterpret_cast<const u32x4*>(krow + j * 16);
+            for (int j = 0; j < S::CPR; ++j) {
+                const u32x4 kk = *reinterpret_cast<const u32x4*>(krow + j * 16);
+#pragma unroll
+                for (int hh = 0; hh < G; ++hh) {
+                    const u32x4 qv = *reinterpret_cast<const u32x4*>(
+                        reinterpret_cast<const char*>(lds_q) + qoff + (hh * (S::RB / 4) + j * 4) * 4);
+                    acc[hh] = fmaf(u2f(kk.x), u2f(qv.x), acc[hh]);
+                    acc[hh] = fmaf(u2f(kk.y), u2f(qv.y), acc[hh]);
+                    acc[hh] = fmaf(u2f(kk.z), u2f(qv.z), acc[hh]);
+                    acc[hh] = fmaf(u2f(kk.w), u2f(qv.w), acc[hh]);
+                }
+                // keep the LDS reads of two chunks at a time in flight, not all of them
+                if (j & 1) __builtin_amdgcn_sched_barrier(0);
+            }
+
+            // ---- 3. online softmax ----------------------------------------------------------
+            const bool valid = (t0 + lane) < t_end;
+            float alpha[G];
 #pragma unroll
             for (int hh = 0; hh < G; ++hh) {
-                const u32x4 qq = *reinterpret_cast<const u32x4*>(
-                    reinterpret_cast<const char*>(lds_q) + qoff + (hh * (S::RB / 4) + j * 4) * 4);
-                if constexpr (BF16) {
-                    acc[hh] = dot2_bf16(kk.x, qq.x, acc[hh]);
-                    acc[hh] = dot2_bf16(kk.y, qq.y, acc[hh]);
-                    acc[hh] = dot2_bf16(kk.z, qq.z, acc[hh]);
-                    acc[hh] = dot2_bf16(kk.w, qq.w, acc[hh]);
-                } else {
-                    acc[hh] = fmaf(u2f(kk.x), u2f(qq.x), acc[hh]);
-                    acc[hh] = fmaf(u2f(kk.y), u2f(qq.y), acc[hh]);
-                    acc[hh] = fmaf(u2f(kk.z), u2f(qq.z), acc[hh]);
-                    acc[hh] = fmaf(u2f(kk.w), u2f(qq.w), acc[hh]);
-                }
-            }
-            // keep the LDS reads of two chunks at a time in flight, not all of them
-            if (j & 1) __builtin_amdgcn_sched_barrier(0);
-        }
-
-        // ---- 3. online softmax ------------------------------------------------------
-        const bool valid = (t0 + lane) < t_end;
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-            const float sc = valid ? acc[hh] * a.scale_log2 : -INFINITY;
-            const float mn = fmaxf(m[hh], wave_max(sc));
-            alpha[hh] = fast_exp2(m[hh] - mn);
-            const float p = fast_exp2(sc - mn);
-            m[hh] = mn;
-            l[hh] = l[hh] * alpha[hh] + p;
-            if constexpr (BF16) {
-                // rows i*R+a and (i^1)*R+a share one dword: (even row lo, odd row hi)
-                const int i = lane / S::R, ar = lane - (lane / S::R) * S::R;
-                const int pidx = (i >> 1) * S::R + ar;
-                reinterpret_cast<uint16_t*>(lds_p)[(pidx * 8 + hh) * 2 + (i & 1)] = f32_to_bf16(p);
-            } else {
+                const float sc = valid ? acc[hh] * a.scale_log2 : -INFINITY;
+                const float mn = fmaxf(m[hh], wave_max(sc));
+                alpha[hh] = fast_exp2(m[hh] - mn);
+                const float p = fast_exp2(sc - mn);
+                m[hh] = mn;
+                l[hh] = l[hh] * alpha[hh] + p;
                 reinterpret_cast<float*>(lds_p)[lane * 8 + hh] = p;
             }
-        }
-        }
-        __syncthreads();
+            __syncthreads();
 
-        // ---- 4. PV ------------------------------------------------------------------
-        if (t0 + kTile > t_end) {  // tail tile: rows past the valid length contribute nothing
+            // ---- 4. PV (fp32): lane = 4 elements of one token row ---------------------------
+            if (t0 + kTile > t_end) {  // tail tile: rows past the valid length contribute nothing
 #pragma unroll
-            for (int i = 0; i < S::NL; ++i)
-                if (t0 + i * S::R + ra >= t_end) vreg[i] = u32x4{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-            for (int e = 0; e < S::EPC; ++e) o[hh][e] *= alpha[hh];
-        if constexpr (BF16) {
-            constexpr int PS = 16 / S::R;      // loads between tokens t and t + 16
-#pragma unroll
-            for (int ii = 0; ii < S::NL / 2; ++ii) {
-                const int i0 = (ii / PS) * 2 * PS + ii % PS;
-                const int tk = i0 * S::R + ra;        // token of load i0: 0..15 or 32..47
-                const u32x4 v0 = vreg[i0], v1 = vreg[i0 + PS];
-                const uint32_t* pp = lds_p + ((tk >> 5) * 16 + (tk & 15)) * 8;
-                const u32x4 pa = *reinterpret_cast<const u32x4*>(pp);
-                const u32x4 pz = *reinterpret_cast<const u32x4*>(pp + 4);
-                const uint32_t pk[8] = {pa.x, pa.y, pa.z, pa.w, pz.x, pz.y, pz.z, pz.w};
-                const uint32_t w0[4] = {v0.x, v0.y, v0.z, v0.w};
-                const uint32_t w1[4] = {v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const uint32_t lo = pair_lo(w0[w], w1[w]);
-                    const uint32_t hi = pair_hi(w0[w], w1[w]);
-#pragma unroll
-                    for (int hh = 0; hh < G; ++hh) {
-                        o[hh][2 * w] = dot2_bf16(pk[hh], lo, o[hh][2 * w]);
-                        o[hh][2 * w + 1] = dot2_bf16(pk[hh], hi, o[hh][2 * w + 1]);
-                    }
-                }
+                for (int i = 0; i < S::NL; ++i)
+                    if (t0 + i * S::R + ra >= t_end) vreg[i] = u32x4{0u, 0u, 0u, 0u};
             }
-        } else {
+#pragma unroll
+            for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+                for (int e = 0; e < S::EPC; ++e) o[hh][e] *= alpha[hh];
 #pragma unroll
             for (int i = 0; i < S::NL; ++i) {
                 const float* pr = reinterpret_cast<const float*>(lds_p) + (i * S::R + ra) * 8;
                 const float4 pa = *reinterpret_cast<const float4*>(pr);
                 const float4 pz = *reinterpret_cast<const float4*>(pr + 4);
                 const float pv[8] = {pa.x, pa.y, pa.z, pa.w, pz.x, pz.y, pz.z, pz.w};
-                const float v[4] = {u2f(vreg[i].x), u2f(vreg[i].y), u2f(vreg[i].z), u2f(vreg[i].w)};
+                const float v[4] = {u2f(vreg[i].x), u2f(vreg[i].y), u2f(vreg[i].z),
+                                    u2f(vreg[i].w)};
 #pragma unroll
                 for (int hh = 0; hh < G; ++hh)
 #pragma unroll
@@ -366,19 +409,22 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, int s, int s
         }
     }
 
-    // ---- combine lanes: per-lane sums, then the row groups sharing a chunk -----------
-    const float lsum = swap32_sum(swap16_sum(ll));   // bf16: head qn's total in its lanes
+    // ---- combine lanes -----------------------------------------------------------------
+    if constexpr (BF16) {
+        // head qn's sum over its four lanes; O^T stays where the products left it
+        st.m = mh;
+        st.l = swap32_sum(swap16_sum(ll));
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-        if constexpr (BF16) {
-            st.m[hh] = u2f(__builtin_amdgcn_readlane(f2u(mh), hh));
-            st.l[hh] = u2f(__builtin_amdgcn_readlane(f2u(lsum), hh));
-        } else {
+        for (int dt = 0; dt < D / 16; ++dt) st.o[dt] = oacc[dt];
+    } else {
+        // per-lane sums, then the row groups sharing a chunk
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
             st.m[hh] = m[hh];
             st.l[hh] = wave_sum(l[hh]);
-        }
 #pragma unroll
-        for (int e = 0; e < S::EPC; ++e) st.o[hh][e] = group_sum<S::R>(o[hh][e]);
+            for (int e = 0; e < S::EPC; ++e) st.o[hh][e] = group_sum<S::R>(o[hh][e]);
+        }
     }
 }
 
@@ -388,20 +434,25 @@ __device__ __forceinline__ void write_rows(const DecodeArgs& a, int s, int h,
                                            const SegState<BF16, D, G>& st) {
     using S = DecodeShape<BF16, D>;
     const int lane = threadIdx.x;
-    const int ra = lane / S::CPR, rc = lane - (lane / S::CPR) * S::CPR;
-    if (ra != 0) return;
+    if constexpr (BF16) {
+        // lane 16qq + n: elements 16dt + 4qq .. + 3 of head n's row
+        const int n = lane & 15, qq = lane >> 4;
+        if (n >= G) return;
+        const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
+        uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) +
+                        ((int64_t)s * a.num_q_heads + h * G + n) * D + 4 * qq;
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-        const float inv = st.l[hh] > 0.f ? 1.f / st.l[hh] : 0.f;
-        const int64_t row = ((int64_t)s * a.num_q_heads + h * G + hh) * D + rc * S::EPC;
-        if constexpr (BF16) {
-            uint4 w;
-            w.x = pack_bf16(st.o[hh][0] * inv, st.o[hh][1] * inv);
-            w.y = pack_bf16(st.o[hh][2] * inv, st.o[hh][3] * inv);
-            w.z = pack_bf16(st.o[hh][4] * inv, st.o[hh][5] * inv);
-            w.w = pack_bf16(st.o[hh][6] * inv, st.o[hh][7] * inv);
-            *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.out) + row) = w;
-        } else {
+        for (int dt = 0; dt < D / 16; ++dt)
+            *reinterpret_cast<u32x2*>(dst + 16 * dt) =
+                u32x2{pack_bf16(st.o[dt][0] * inv, st.o[dt][1] * inv),
+                      pack_bf16(st.o[dt][2] * inv, st.o[dt][3] * inv)};
+    } else {
+        const int ra = lane / S::CPR, rc = lane - (lane / S::CPR) * S::CPR;
+        if (ra != 0) return;
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+            const float inv = st.l[hh] > 0.f ? 1.f / st.l[hh] : 0.f;
+            const int64_t row = ((int64_t)s * a.num_q_heads + h * G + hh) * D + rc * S::EPC;
             *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + row) =
                 make_float4(st.o[hh][0] * inv, st.o[hh][1] * inv, st.o[hh][2] * inv,
                             st.o[hh][3] * inv);
@@ -416,19 +467,31 @@ __device__ __forceinline__ void write_state(float* o_base, float* ml_base, int64
                                             int64_t prow_step, const SegState<BF16, D, G>& st) {
     using S = DecodeShape<BF16, D>;
     const int lane = threadIdx.x;
-    const int ra = lane / S::CPR, rc = lane - (lane / S::CPR) * S::CPR;
+    if constexpr (BF16) {
+        const int n = lane & 15, qq = lane >> 4;
+        if (n >= G) return;
+        const int64_t prow = prow0 + n * prow_step;
+        float* dst = o_base + prow * D + 4 * qq;
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-        const int64_t prow = prow0 + hh * prow_step;
-        if (ra == 0) {
-            float* dst = o_base + prow * D + rc * S::EPC;
+        for (int dt = 0; dt < D / 16; ++dt)
+            *reinterpret_cast<float4*>(dst + 16 * dt) =
+                make_float4(st.o[dt][0], st.o[dt][1], st.o[dt][2], st.o[dt][3]);
+        if (qq == 0) *reinterpret_cast<float2*>(ml_base + prow * 2) = make_float2(st.m, st.l);
+    } else {
+        const int ra = lane / S::CPR, rc = lane - (lane / S::CPR) * S::CPR;
 #pragma unroll
-            for (int e = 0; e < S::EPC; e += 4)
-                *reinterpret_cast<float4*>(dst + e) =
-                    make_float4(st.o[hh][e], st.o[hh][e + 1], st.o[hh][e + 2], st.o[hh][e + 3]);
+        for (int hh = 0; hh < G; ++hh) {
+            const int64_t prow = prow0 + hh * prow_step;
+            if (ra == 0) {
+                float* dst = o_base + prow * D + rc * S::EPC;
+#pragma unroll
+                for (int e = 0; e < S::EPC; e += 4)
+                    *reinterpret_cast<float4*>(dst + e) = make_float4(
+                        st.o[hh][e], st.o[hh][e + 1], st.o[hh][e + 2], st.o[hh][e + 3]);
+            }
+            if (lane == 0)
+                *reinterpret_cast<float2*>(ml_base + prow * 2) = make_float2(st.m[hh], st.l[hh]);
         }
-        if (lane == 0)
-            *reinterpret_cast<float2*>(ml_base + prow * 2) = make_float2(st.m[hh], st.l[hh]);
     }
 }
 // ... into the balanced split's slots of the workspace.

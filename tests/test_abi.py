@@ -202,9 +202,9 @@ def test_shared_prefix_workspace_sizes(lib):
     dec = lib.paged_attention_decode_workspace_bytes(4, 8, 2, 128, 4096, 0)
     assert f(4, 8, 2, 128, 4096, 0) == dec
     # prefix states: S * Hq * (splits + 1) * (D + 2) floats (one slot per split and one
-    # for the row's own tokens); at most 8 splits of a multiple of 64 keys: 2032 keys ->
-    # 8 splits of 256, 100 -> 2 of 64, 64 -> 1
-    for mpl, splits in ((2032, 8), (100, 2), (64, 1), (1, 1), (20000, 8)):
+    # for the row's own tokens); at most 4 splits of a multiple of 64 keys: 2032 keys ->
+    # 4 splits of 512, 100 -> 2 of 64, 64 -> 1, 20000 -> 4 of 5056
+    for mpl, splits in ((2032, 4), (100, 2), (64, 1), (1, 1), (20000, 4)):
         assert f(4, 8, 2, 128, 4096, mpl) - dec == 4 * 8 * (splits + 1) * 130 * 4, mpl
     assert f(0, 8, 2, 128, 4096, 2032) == 0
 

@@ -69,7 +69,7 @@ def test_block_sizes_and_head_dim_64(bs):
 
 def test_many_row_blocks_and_ragged_splits():
     """70 members at G=4 fill three 32-member row blocks (the last partly); a 1000-token
-    prefix at block size 8 is cut into 8 splits of 128 keys, the last one ragged."""
+    prefix at block size 8 is cut into 4 splits of 256 keys, the last one ragged."""
     check_groups(W.prefix_groups(301, [(70, 125), (3, 0), (33, 40)], suffix_range=(1, 130),
                                  block_size=8))
 
