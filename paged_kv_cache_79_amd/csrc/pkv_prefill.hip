@@ -372,46 +372,6 @@ __device__ __forceinline__ void attend(const PrefillArgs& a, const PfChunk& k, i
         }
 }
 
-// ---- D = 128: K/V tiles straight from the pool into LDS --------------------------
-//
-// The tile loop above stages every K/V tile through 64 registers per lane and writes V
-// transposed into LDS with byte permutes.  For D = 128 the tiles instead go from the pool
-// into LDS with the gfx950 direct loads (global_load_lds_dwordx4: lane t's 16 bytes land
-// at the wave's LDS base + 16 t), K and V both row-major with 256-byte rows, and the
-// V^T operand of the P.V product is read with the transposing ds_read_b64_tr_b16.  No
-// registers hold a tile in flight, and no vector instruction touches it on its way.
-//
-// Which 16-byte chunk of a row a lane fetches decides where it lands, so the chunks of
-// each row are permuted (a XOR with row bits) to keep the operand reads free of bank
-// conflicts:
-//   K: chunk c of row r at position c ^ (r % 16).  The S^T = K Q^T operand of lane l is
-//      chunk 2 ks + l / 32 of row 32 mt + l % 32: 16 consecutive rows, 16 positions.
-//   V: chunk c of row r at position c ^ 4 (r % 4).  A transposing read serves 32 lanes
-//      from 4 consecutive rows x 4 consecutive chunks: 16 positions.
-struct PfLdsDma {
-    char k[2][kKeyTile * 256];
-    char v[2][kKeyTile * 256];
-};
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)reinterpret_cast<uintptr_t>(p);
-}
-
-// One wave-wide direct load, lane t: 16 bytes from gbase + voff to LDS lds + 16 t.  It is
-// written as inline asm so that the compiler, which cannot tell the LDS buffers apart, does
-// not wait for it before every later LDS read; the wait is explicit (wait_dma).  The nops
-// cover the hazards of a base or M0 written just before (VALU write of an SGPR that a
-// vector memory instruction reads: 5 wait states).
-__device__ __forceinline__ void dma16(uint32_t lds, const char* gbase, uint32_t voff) {
-    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "{m0}"(lds)
-                 : "memory");
-}
-// Every direct load of this wave has written LDS (and every other vector load is back).
-__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-typedef short pf_v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) pf_v4i16 pf_lds_v4i16;
-
 template <int G>
 __device__ __forceinline__ void attend_dma(const PrefillArgs& a, const PfChunk& k, int c, int h,
                                            int qt, int k0, int k1, int64_t slot, PfLdsDma& lds) {
@@ -426,14 +386,12 @@ __device__ __forceinline__ void attend_dma(const PrefillArgs& a, const PfChunk& 
     const int n = lane & 31;
     const int half = lane >> 5;
     const int Hq = a.num_q_heads;
-    const int bs = a.g.block_size;
     const int mb = a.max_blocks_per_seq;
 
     const int q0 = k.q0, nq = k.nq, ctx = k.ctx;
     const int32_t* table = a.block_tables + (int64_t)c * mb;
     const char* kb = a.k_pool + (int64_t)h * a.g.head_stride_bytes;
     const char* vb = a.v_pool + (int64_t)h * a.g.head_stride_bytes;
-    const uint32_t stride = (uint32_t)a.g.block_stride_bytes, nbk = (uint32_t)a.g.num_blocks;
 
     const int r = w * 32 + n;
     const int qi = r / G;
@@ -469,183 +427,8 @@ __device__ __forceinline__ void attend_dma(const PrefillArgs& a, const PfChunk& 
     const int t_begin = k0 * kKeyTile;
     const int t_end = min(k1 * kKeyTile, ctx - nq + min(nq, (qt + 1) * QP));
 
-    // ---- direct loads: wave w moves rows 16 w .. 16 w + 15 of each tile, four loads of
-    // four rows; lane t takes row t / 16 of a load and fills chunk position t % 16
-    const int dr = lane >> 4, dp = lane & 15;
-    uint32_t kvo[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) kvo[i] = (uint32_t)(16 * (dp ^ ((4 * i + dr) & 15)));
-    const uint32_t vvo = (uint32_t)(16 * (dp ^ (4 * dr)));
-    const uint32_t drow = (uint32_t)dr * RB;
-    // block ids of a tile's four loads (lane i < 4: load i), read a tile ahead
-    auto tile_ids = [&](int t0) {
-        const int tb = min(t0 + 16 * w + 4 * min(lane, 3), ctx - 1);
-        return table[(uint32_t)tb >> a.g.log2_bs];
-    };
-    auto issue_loads = [&](int t0, int buf, int ids, auto ragged_c) {
-        constexpr bool ragged = decltype(ragged_c)::value;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int tb = t0 + 16 * w + 4 * i;
-            const int tbc = min(tb, ctx - 1);
-            uint32_t id = (uint32_t)__builtin_amdgcn_readlane(ids, i);
-            id = id < nbk ? id : 0u;
-            const uint32_t roff = (uint32_t)(tbc & (bs - 1)) * RB;
-            const uint64_t boff = (((uint64_t)__umulhi(id, stride) << 32) | (uint64_t)(id * stride)) + roff;
-            const uint32_t row = ragged ? (uint32_t)(min(tb + dr, ctx - 1) - tbc) * RB : drow;
-            const uint32_t lk = lds_addr(lds.k[buf]) + (uint32_t)((16 * w + 4 * i) * RB);
-            const uint32_t lv = lds_addr(lds.v[buf]) + (uint32_t)((16 * w + 4 * i) * RB);
-            dma16(lk, kb + boff, row + kvo[i]);
-            dma16(lv, vb + boff, row + vvo);
-        }
-    };
-    // rows past the context (only in the last tile) read the last token's row
-    auto issue = [&](int t0, int buf, int ids) {
-        if (t0 + kKeyTile > ctx)
-            issue_loads(t0, buf, ids, std::true_type{});
-        else
-            issue_loads(t0, buf, ids, std::false_type{});
-    };
-
-    // ---- operand offsets inside a tile buffer
-    uint32_t koff[P::KSTEPS];      // S^T = K Q^T: row n (+32 mt), chunk 2 ks + half
-#pragma unroll
-    for (int ks = 0; ks < P::KSTEPS; ++ks)
-        koff[ks] = (uint32_t)(n * RB + 16 * ((2 * ks + half) ^ (n & 15)));
-    // P.V: the transposing read of lane a (of 16-lane group g) addresses key row
-    // 4 (g / 2) + a / 4 (+ 16 u, + 8 for the second half of the operand), elements
-    // 32 dt + 16 (g % 2) + 4 (a % 4) .. + 3
-    uint32_t vtoff[P::DT];
-    {
-        const int g = lane >> 4, ai = lane & 15, rr = ai >> 2, qq = ai & 3;
-#pragma unroll
-        for (int dt = 0; dt < P::DT; ++dt)
-            vtoff[dt] = (uint32_t)((4 * (g >> 1) + rr) * RB +
-                                   16 * (4 * (dt ^ rr) + 2 * (g & 1) + (qq >> 1)) + 8 * (qq & 1));
-    }
-
-    int ids_next = 0;
-    if (t_begin < t_end) {
-        const int ids0 = tile_ids(t_begin);
-        issue(t_begin, 0, ids0);
-        if (t_begin + kKeyTile < t_end) ids_next = tile_ids(t_begin + kKeyTile);
-    }
-    wait_dma();
-    __syncthreads();
-
-    auto step = [&](int t0, int buf) {
-        const char* tk = lds.k[buf];
-        const char* tv = lds.v[buf];
-        // tile t0 + 64 into the other buffer (every wave finished reading it before the
-        // last barrier); block ids of tile t0 + 128 for the next step
-        if (t0 + kKeyTile < t_end) {
-            issue(t0 + kKeyTile, buf ^ 1, ids_next);
-            if (t0 + 2 * kKeyTile < t_end) ids_next = tile_ids(t0 + 2 * kKeyTile);
-        }
-        // ---- S^T = K Q^T, operands read two ahead
-        floatx16_t sacc[2];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) sacc[mt][e] = 0.f;
-        {
-            constexpr int NK = 2 * P::KSTEPS, AH = 3;
-            auto kop = [&](int i) {
-                return *reinterpret_cast<const u32x4*>(tk + (i / P::KSTEPS) * 32 * RB +
-                                                       koff[i % P::KSTEPS]);
-            };
-            u32x4 kbuf[AH];
-#pragma unroll
-            for (int i = 0; i < AH; ++i) kbuf[i] = kop(i);
-#pragma unroll
-            for (int i = 0; i < NK; ++i) {
-                const u32x4 ka = kbuf[i % AH];
-                if (i + AH < NK) kbuf[i % AH] = kop(i + AH);
-                sacc[i / P::KSTEPS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8_t, ka),
-                    __builtin_bit_cast(bf16x8_t, qreg[i % P::KSTEPS]), sacc[i / P::KSTEPS], 0, 0, 0);
-                // keep the reads ahead of the products as written
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-
-        // ---- online softmax (as in attend)
-        const bool scaled = t0 + kKeyTile > full_end || !(sl2 > 0.f);
-        const float mul = scaled ? 1.f : sl2;
-        if (scaled) {
-            const int lim = last_key - t0 - 4 * half;
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    sacc[mt][e] = (mt * 32 + 8 * (e >> 2) + (e & 3) <= lim) ? sacc[mt][e] * sl2
-                                                                            : -INFINITY;
-        }
-        float mloc = -INFINITY;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, sacc[mt][e]);
-        const float mx = fmaxf(m, swap32_max(mloc) * mul);
-        if (__builtin_amdgcn_ballot_w64(mx > m + kLazyMax)) {
-            const float alpha = fast_exp2(m - mx);
-            l *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < P::DT; ++dt)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
-            m = mx;
-        }
-        const float mn = m;
-        u32x4 pk[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int mt = u >> 1, e0 = (u & 1) * 8;
-            float p[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) p[j] = fast_exp2(__builtin_fmaf(sacc[mt][e0 + j], mul, -mn));
-            pk[u] = u32x4{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
-                          pack_bf16(p[6], p[7])};
-            l = sum_bf16x8(pk[u], l);
-        }
-
-        // ---- O^T += V^T P^T: operand (dt, u) from two transposing reads of key rows
-        // 16 u + 4 (g / 2) + 0..3 and + 8, read two operands ahead
-        {
-            constexpr int NV = P::DT * 4, AH = 2;
-            auto vop = [&](int i) {
-                const int dt = i >> 2, u = i & 3;
-                const char* p0 = tv + 16 * u * RB + vtoff[dt];
-                const pf_v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((pf_lds_v4i16*)p0);
-                const pf_v4i16 hi =
-                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((pf_lds_v4i16*)(p0 + 8 * RB));
-                const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-                return u32x4{l2.x, l2.y, h2.x, h2.y};
-            };
-            u32x4 vbuf[AH];
-#pragma unroll
-            for (int i = 0; i < AH; ++i) vbuf[i] = vop(i);
-#pragma unroll
-            for (int i = 0; i < NV; ++i) {
-                const u32x4 va = vbuf[i % AH];
-                if (i + AH < NV) vbuf[i % AH] = vop(i + AH);
-                oacc[i >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8_t, va), __builtin_bit_cast(bf16x8_t, pk[i & 3]),
-                    oacc[i >> 2], 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-        // this wave's loads of the next tile are in LDS; the barrier publishes them and
-        // frees this buffer
-        wait_dma();
-        asm volatile("" : "+v"(ids_next));   // its load is back too: no wait in the next step
-        __syncthreads();
-    };
-    for (int t0 = t_begin; t0 < t_end; t0 += 2 * kKeyTile) {
-        step(t0, 0);
-        if (t0 + kKeyTile >= t_end) break;
-        step(t0 + kKeyTile, 1);
-    }
+    dma_attend_tiles(lds, table, a.g, kb, vb, ctx, t_begin, t_end, full_end, last_key, sl2, qreg,
+                     oacc, m, l);
 
     const float lt = swap32_sum(l);
     if (!row_valid) return;

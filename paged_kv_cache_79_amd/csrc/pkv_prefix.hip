@@ -13,7 +13,8 @@
 //
 // Mapping: one workgroup (4 waves) owns 128 packed (member, head) rows of one
 // (group, kv head) and one split of the prefix keys; K/V tiles come through the
-// same pipelined staging as chunked prefill (pkv_attn_tiles.h).  Work items are
+// same tile pipeline as chunked prefill (pkv_attn_tiles.h: straight into LDS for
+// head dim 128, staged through registers otherwise).  Work items are
 // ordered (group, kv head, split, row block) and dealt so that the row blocks of
 // one split, which read the same keys, share an XCD.
 #include "pkv_attn_tiles.h"
@@ -25,8 +26,6 @@ __global__ __launch_bounds__(256, 2) void prefix_kernel(PrefixArgs a, int num_ro
                                                         int num_items) {
     using P = PrefillShape<D>;
     constexpr int QP = kRowsPerWg / G;           // members per workgroup
-    __shared__ __attribute__((aligned(16))) char lds_k[2][kKeyTile * P::KPITCH];
-    __shared__ __attribute__((aligned(16))) char lds_vt[2][D * P::VPITCH];
 
     const int nwg = gridDim.x;
     const int item = (blockIdx.x % kXcds) * (nwg / kXcds) + blockIdx.x / kXcds;
@@ -73,6 +72,12 @@ __global__ __launch_bounds__(256, 2) void prefix_kernel(PrefixArgs a, int num_ro
         for (int ks = 0; ks < P::KSTEPS; ++ks)
             qreg[ks] = row_valid ? *reinterpret_cast<const u32x4*>(qp + ks * 32)
                                  : u32x4{0u, 0u, 0u, 0u};
+        if constexpr (D == 128) {
+            // the rows are back before the tile loop, whose direct loads a wait inside it
+            // would also wait for
+#pragma unroll
+            for (int ks = 0; ks < P::KSTEPS; ++ks) asm volatile("" : "+v"(qreg[ks]));
+        }
     }
 
     floatx16_t oacc[P::DT];
@@ -83,6 +88,14 @@ __global__ __launch_bounds__(256, 2) void prefix_kernel(PrefixArgs a, int num_ro
     float m = kNoMax, l = 0.f;           // running max (log2 units) and sum of the row
     const float sl2 = a.scale_log2;
 
+    if constexpr (D == 128) {
+        // K/V straight into LDS (dma_attend_tiles); every row sees every key of [k0, k1),
+        // and rows past k1 in the last tile read key k1 - 1
+        __shared__ __attribute__((aligned(16))) PfLdsDma lds;
+        dma_attend_tiles(lds, table, a.g, kb, vb, k1, k0, k1, k1, k1 - 1, sl2, qreg, oacc, m, l);
+    } else {
+    __shared__ __attribute__((aligned(16))) char lds_k[2][kKeyTile * P::KPITCH];
+    __shared__ __attribute__((aligned(16))) char lds_vt[2][D * P::VPITCH];
     // keys [k0, k1): keys >= k1 of the last tile are masked below (see load_ids).
     // The same pipeline as chunked prefill: two K/V register stages and two id sets
     // alternating with the tile parity, two LDS buffers, one barrier per tile.
@@ -185,6 +198,8 @@ __global__ __launch_bounds__(256, 2) void prefix_kernel(PrefixArgs a, int num_ro
         step(t0, 0, st0, st1, ids0, ids1);
         if (t0 + kKeyTile >= k1) break;
         step(t0 + kKeyTile, 1, st1, st0, ids1, ids0);
+    }
+
     }
 
     // ---- partial state of the row: lane holds d = 32dt + 8(e/4) + 4half + e%4 -------
