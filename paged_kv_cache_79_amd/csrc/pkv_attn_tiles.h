@@ -251,8 +251,9 @@ __device__ __forceinline__ void dma_attend_tiles(PfLdsDma& lds, const int32_t* t
         const int tb = min(t0 + 16 * w + 4 * min(lane, 3), ctx - 1);
         return table[(uint32_t)tb >> geom.log2_bs];
     };
-    auto issue_loads = [&](int t0, int buf, int ids, auto ragged_c) {
+    auto issue_loads = [&](int t0, int buf, int ids, auto ragged_c, auto kv_c) {
         constexpr bool ragged = decltype(ragged_c)::value;
+        constexpr int kv = decltype(kv_c)::value;      // 0: K, 1: V
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int tb = t0 + 16 * w + 4 * i;
@@ -262,19 +263,24 @@ __device__ __forceinline__ void dma_attend_tiles(PfLdsDma& lds, const int32_t* t
             const uint32_t roff = (uint32_t)(tbc & (bs - 1)) * RB;
             const uint64_t boff = (((uint64_t)__umulhi(id, stride) << 32) | (uint64_t)(id * stride)) + roff;
             const uint32_t row = ragged ? (uint32_t)(min(tb + dr, ctx - 1) - tbc) * RB : drow;
-            const uint32_t lk = lds_addr(lds.k[buf]) + (uint32_t)((16 * w + 4 * i) * RB);
-            const uint32_t lv = lds_addr(lds.v[buf]) + (uint32_t)((16 * w + 4 * i) * RB);
-            dma16(lk, kb + boff, row + kvo[i]);
-            dma16(lv, vb + boff, row + vvo);
+            if constexpr (kv == 0)
+                dma16(lds_addr(lds.k[buf]) + (uint32_t)((16 * w + 4 * i) * RB), kb + boff,
+                      row + kvo[i]);
+            else
+                dma16(lds_addr(lds.v[buf]) + (uint32_t)((16 * w + 4 * i) * RB), vb + boff,
+                      row + vvo);
         }
     };
-    // rows past the context (only in the last tile) read the last token's row
-    auto issue = [&](int t0, int buf, int ids) {
+    // the K (kv 0) or V (kv 1) rows of the tile at t0; rows past the context (only in the
+    // last tile) read the last token's row
+    auto issue = [&](int t0, int buf, int ids, auto kv_c) {
         if (t0 + kKeyTile > ctx)
-            issue_loads(t0, buf, ids, std::true_type{});
+            issue_loads(t0, buf, ids, std::true_type{}, kv_c);
         else
-            issue_loads(t0, buf, ids, std::false_type{});
+            issue_loads(t0, buf, ids, std::false_type{}, kv_c);
     };
+    using KT = std::integral_constant<int, 0>;
+    using VT = std::integral_constant<int, 1>;
 
     // ---- operand offsets inside a tile buffer
     uint32_t koff[P::KSTEPS];      // S^T = K Q^T: row n (+32 mt), chunk 2 ks + half
@@ -293,52 +299,66 @@ __device__ __forceinline__ void dma_attend_tiles(PfLdsDma& lds, const int32_t* t
                                    16 * (4 * (dt ^ rr) + 2 * (g & 1) + (qq >> 1)) + 8 * (qq & 1));
     }
 
-    int ids_next = 0;
-    if (t_begin < t_end) {
-        const int ids0 = tile_ids(t_begin);
-        issue(t_begin, 0, ids0);
-        if (t_begin + kKeyTile < t_end) ids_next = tile_ids(t_begin + kKeyTile);
-    }
-    wait_dma();
-    __syncthreads();
+    if (t_begin >= t_end) return;          // uniform over the workgroup
+    const int nt = (t_end - t_begin + kKeyTile - 1) / kKeyTile;
 
-    auto step = [&](int t0, int buf) {
-        const char* tk = lds.k[buf];
-        const char* tv = lds.v[buf];
-        // tile t0 + 64 into the other buffer (every wave finished reading it before the
-        // last barrier); block ids of tile t0 + 128 for the next step
-        if (t0 + kKeyTile < t_end) {
-            issue(t0 + kKeyTile, buf ^ 1, ids_next);
-            if (t0 + 2 * kKeyTile < t_end) ids_next = tile_ids(t0 + 2 * kKeyTile);
-        }
-        // ---- S^T = K Q^T, operands read two ahead
-        floatx16_t sacc[2];
+    // S^T = K Q^T of the tile in K buffer kbuf, operands read three ahead
+    auto qk_plain = [&](int kbuf, floatx16_t (&sacc)[2]) {
+        const char* tk = lds.k[kbuf];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int e = 0; e < 16; ++e) sacc[mt][e] = 0.f;
-        {
-            constexpr int NK = 2 * P::KSTEPS, AH = 3;
-            auto kop = [&](int i) {
-                return *reinterpret_cast<const u32x4*>(tk + (i / P::KSTEPS) * 32 * RB +
-                                                       koff[i % P::KSTEPS]);
-            };
-            u32x4 kbuf[AH];
+        constexpr int NK = 2 * P::KSTEPS, AH = 3;
+        auto kop = [&](int i) {
+            return *reinterpret_cast<const u32x4*>(tk + (i / P::KSTEPS) * 32 * RB +
+                                                   koff[i % P::KSTEPS]);
+        };
+        u32x4 kbf[AH];
 #pragma unroll
-            for (int i = 0; i < AH; ++i) kbuf[i] = kop(i);
+        for (int i = 0; i < AH; ++i) kbf[i] = kop(i);
 #pragma unroll
-            for (int i = 0; i < NK; ++i) {
-                const u32x4 ka = kbuf[i % AH];
-                if (i + AH < NK) kbuf[i % AH] = kop(i + AH);
-                sacc[i / P::KSTEPS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8_t, ka),
-                    __builtin_bit_cast(bf16x8_t, qreg[i % P::KSTEPS]), sacc[i / P::KSTEPS], 0, 0, 0);
-                // keep the reads ahead of the products as written
-                __builtin_amdgcn_sched_barrier(0);
-            }
+        for (int i = 0; i < NK; ++i) {
+            const u32x4 ka = kbf[i % AH];
+            if (i + AH < NK) kbf[i % AH] = kop(i + AH);
+            sacc[i / P::KSTEPS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8_t, ka), __builtin_bit_cast(bf16x8_t, qreg[i % P::KSTEPS]),
+                sacc[i / P::KSTEPS], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // Prologue: K and V of tile 0, K of tile 1; S of tile 0.  From then on step j issues V
+    // of tile j + 1 and K of tile j + 2, and runs the products of tile j + 1 beside the
+    // exponentials of tile j.
+    int ids1 = 0, ids2 = 0;
+    {
+        const int ids0 = tile_ids(t_begin);
+        if (nt > 1) ids1 = tile_ids(t_begin + kKeyTile);
+        issue(t_begin, 0, ids0, KT{});
+        issue(t_begin, 0, ids0, VT{});
+        if (nt > 1) issue(t_begin + kKeyTile, 1, ids1, KT{});
+        if (nt > 2) ids2 = tile_ids(t_begin + 2 * kKeyTile);
+    }
+    wait_dma();
+    asm volatile("" : "+v"(ids2));
+    __syncthreads();
+    floatx16_t sacc[2];
+    qk_plain(0, sacc);
+    __syncthreads();                       // every wave is done with K buffer 0
+
+    // step j: tile t0 = t_begin + 64 j, K of tile j + 1 in K buffer kn, V of tile j in
+    // V buffer vc (kn = vc ^ 1 = (j + 1) % 2)
+    auto step = [&](int t0, int kn, int vc) {
+        const bool more1 = t0 + kKeyTile < t_end, more2 = t0 + 2 * kKeyTile < t_end;
+        int ids3 = 0;
+        if (more1) issue(t0 + kKeyTile, vc ^ 1, ids1, VT{});
+        if (more2) {
+            issue(t0 + 2 * kKeyTile, vc, ids2, KT{});
+            if (t0 + 3 * kKeyTile < t_end) ids3 = tile_ids(t0 + 3 * kKeyTile);
         }
 
-        // ---- online softmax (as in attend)
+        // ---- online softmax of tile j: the maximum first (mask on the tiles that hide keys)
         const bool scaled = t0 + kKeyTile > full_end || !(sl2 > 0.f);
         const float mul = scaled ? 1.f : sl2;
         if (scaled) {
@@ -366,21 +386,61 @@ __device__ __forceinline__ void dma_attend_tiles(PfLdsDma& lds, const int32_t* t
             m = mx;
         }
         const float mn = m;
-        u32x4 pk[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int mt = u >> 1, e0 = (u & 1) * 8;
-            float p[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) p[j] = fast_exp2(__builtin_fmaf(sacc[mt][e0 + j], mul, -mn));
-            pk[u] = u32x4{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
-                          pack_bf16(p[6], p[7])};
-            l = sum_bf16x8(pk[u], l);
-        }
 
-        // ---- O^T += V^T P^T: operand (dt, u) from two transposing reads of key rows
-        // 16 u + 4 (g / 2) + 0..3 and + 8, read two operands ahead
+        // ---- S^T of tile j + 1 (K buffer kn; past the last tile its stale contents give
+        // products nothing reads) beside the probabilities of tile j: one product, six
+        // vector instructions and one operand read at a time
+        floatx16_t snx[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) snx[mt][e] = 0.f;
+        u32x4 pk[4];
         {
+            const char* tk = lds.k[kn];
+            constexpr int NK = 2 * P::KSTEPS, AH = 3;
+            auto kop = [&](int i) {
+                return *reinterpret_cast<const u32x4*>(tk + (i / P::KSTEPS) * 32 * RB +
+                                                       koff[i % P::KSTEPS]);
+            };
+            u32x4 kbf[AH];
+#pragma unroll
+            for (int i = 0; i < AH; ++i) kbf[i] = kop(i);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int mt = u >> 1, e0 = (u & 1) * 8;
+                float p[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    p[j] = fast_exp2(__builtin_fmaf(sacc[mt][e0 + j], mul, -mn));
+                pk[u] = u32x4{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
+                              pack_bf16(p[6], p[7])};
+                l = sum_bf16x8(pk[u], l);
+#pragma unroll
+                for (int i = 4 * u; i < 4 * u + 4; ++i) {
+                    const u32x4 ka = kbf[i % AH];
+                    if (i + AH < NK) kbf[i % AH] = kop(i + AH);
+                    snx[i / P::KSTEPS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8_t, ka),
+                        __builtin_bit_cast(bf16x8_t, qreg[i % P::KSTEPS]), snx[i / P::KSTEPS], 0, 0,
+                        0);
+                }
+            }
+            // issue order: the first AH operand reads, then per product: the product, six
+            // vector instructions and the read of the operand AH products ahead
+            __builtin_amdgcn_sched_group_barrier(0x100, AH, 0);
+#pragma unroll
+            for (int i = 0; i < NK; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+                if (i + AH < NK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- O^T += V^T P^T of tile j (V buffer vc), operands read two ahead
+        {
+            const char* tv = lds.v[vc];
             constexpr int NV = P::DT * 4, AH = 2;
             auto vop = [&](int i) {
                 const int dt = i >> 2, u = i & 3;
@@ -391,31 +451,34 @@ __device__ __forceinline__ void dma_attend_tiles(PfLdsDma& lds, const int32_t* t
                 const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
                 return u32x4{l2.x, l2.y, h2.x, h2.y};
             };
-            u32x4 vbuf[AH];
+            u32x4 vbf[AH];
 #pragma unroll
-            for (int i = 0; i < AH; ++i) vbuf[i] = vop(i);
+            for (int i = 0; i < AH; ++i) vbf[i] = vop(i);
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
-                const u32x4 va = vbuf[i % AH];
-                if (i + AH < NV) vbuf[i % AH] = vop(i + AH);
+                const u32x4 va = vbf[i % AH];
+                if (i + AH < NV) vbf[i % AH] = vop(i + AH);
                 oacc[i >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     __builtin_bit_cast(bf16x8_t, va), __builtin_bit_cast(bf16x8_t, pk[i & 3]),
                     oacc[i >> 2], 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        // this wave's loads of the next tile are in LDS; the barrier publishes them and
-        // frees this buffer
+        // this wave's loads (V of tile j + 1, K of tile j + 2) are in LDS; the barrier
+        // publishes them and frees the buffers tile j used
         wait_dma();
-        asm volatile("" : "+v"(ids_next));   // its load is back too: no wait in the next step
+        asm volatile("" : "+v"(ids3));
         __syncthreads();
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) sacc[mt] = snx[mt];
+        ids1 = ids2;
+        ids2 = ids3;
     };
     for (int t0 = t_begin; t0 < t_end; t0 += 2 * kKeyTile) {
-        step(t0, 0);
+        step(t0, 1, 0);
         if (t0 + kKeyTile >= t_end) break;
-        step(t0 + kKeyTile, 1);
+        step(t0 + kKeyTile, 0, 1);
     }
-
 }
 
 }  // namespace pkv
