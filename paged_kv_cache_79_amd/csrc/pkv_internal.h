@@ -105,9 +105,10 @@ struct DecodeArgs {
 // Share of the tiles (in 1/1024) that the balanced split gives the first half of its
 // waves when two waves share each SIMD: the first-dispatched wave of a SIMD wins
 // issue arbitration and streams faster while its partner is active, so an even
-// split leaves the second half as the critical path.  Measured on MI355X (sweep of
-// 512..704): 624 is best for both the long-context and the GQA decode.
-constexpr int kLeadShareQ10 = 624;
+// split leaves the second half as the critical path.  Measured on MI355X with the
+// matrix-core Q.K and P.V (608..688, alternated on one machine): 656 is best for both
+// the long-context and the GQA decode.
+constexpr int kLeadShareQ10 = 656;
 
 // Persistent waves the balanced decode launches on the current device.
 int decode_balanced_waves(bool is_bf16, int head_dim, int group);

@@ -145,26 +145,26 @@ def test_balanced_split_covers_and_merges(seed):
     else:
         ctx = rng.integers(60, 70, S)                    # around one tile
     W = int(rng.choice([1, 3, 7, 16, 64, 1024, 2048]))
-    lead = int(rng.choice([512, 584, 624, 700, 1000]))
+    lead = int(rng.choice([512, 584, 624, 656, 700, 1000]))
     nt, T, Weff, sp, written, finished, seen = plan(ctx, hkv, W, lead)
     check(ctx, hkv, nt, T, Weff, sp, written, finished, seen)
 
 
 @pytest.mark.parametrize("shape", ["gqa", "long"])
 def test_skewed_split_at_benchmark_shapes(shape):
-    """The split the bf16 kernels take on a 256-CU device: 2048 waves, lead share 624."""
+    """The split the bf16 kernels take on a 256-CU device: 2048 waves, lead share 656."""
     rng = np.random.Generator(np.random.PCG64(7))
     if shape == "gqa":
         ctx, hkv = rng.integers(128, 4096, 64, endpoint=True), 8
     else:
         ctx, hkv = rng.integers(32768, 200000, 8, endpoint=True), 4
-    nt, T, Weff, sp, written, finished, seen = plan(ctx, hkv, 2048, 624)
+    nt, T, Weff, sp, written, finished, seen = plan(ctx, hkv, 2048, 656)
     assert sp[0] == 1024                                 # the weighted path is taken
     check(ctx, hkv, nt, T, Weff, sp, written, finished, seen)
     sizes = np.diff([begin(T, Weff, sp, w) for w in range(Weff + 1)])
-    # lead waves hold ~1.56x the tiles of the others; within a class, even XCDs more
+    # lead waves hold ~656/368 = 1.78x the tiles of the others; within a class, even XCDs more
     lead, lag = sizes[:1024].mean(), sizes[1024:].mean()
-    assert 1.53 < lead / lag < 1.59
+    assert 1.75 < lead / lag < 1.81
     even, odd = sizes[0::2].mean(), sizes[1::2].mean()
     assert 1.02 < even / odd < 1.06
     assert sizes.min() >= 1
@@ -173,7 +173,7 @@ def test_skewed_split_at_benchmark_shapes(shape):
 def test_weighted_split_never_leaves_a_range_empty():
     """From the smallest T the weighted split takes, for uneven lead shares."""
     for W in (16, 1024, 2048):
-        for lead in (512, 624, 1000):
+        for lead in (512, 656, 1000):
             for T in range(W, 40 * W, max(1, W // 3)):
                 sp = split(T, W, W, lead)
                 if sp[0] == 0:
@@ -181,4 +181,4 @@ def test_weighted_split_never_leaves_a_range_empty():
                 b = [begin(T, W, sp, w) for w in range(W + 1)] if W <= 16 or T % 7 == 0 else \
                     [begin(T, W, sp, w) for w in (0, W // 2 - 1, W // 2, W // 2 + 1, W - 1, W)]
                 assert b[0] == 0 and b[-1] == T and min(np.diff(b)) >= 1, (W, lead, T)
-    assert split(2 * 2048, 2048, 2048, 624)[0] == 1024   # the benchmark grids are weighted
+    assert split(2 * 2048, 2048, 2048, 656)[0] == 1024   # the benchmark grids are weighted
