@@ -171,9 +171,9 @@ __device__ __forceinline__ float sum_bf16x8(u32x4 p, float acc) {
 
 // ---- D = 128: K/V tiles straight from the pool into LDS --------------------------
 //
-// The tile loop above (load_tile / store_tile) stages every K/V tile through 64 registers per lane and writes V
-// transposed into LDS with byte permutes.  For D = 128 the tiles instead go from the pool
-// into LDS with the gfx950 direct loads (global_load_lds_dwordx4: lane t's 16 bytes land
+// The tile loop above (load_tile / store_tile) stages every K/V tile through 64 registers
+// per lane and writes V transposed into LDS with byte permutes.  For D = 128 the tiles
+// instead go from the pool into LDS with the gfx950 direct loads (global_load_lds_dwordx4: lane t's 16 bytes land
 // at the wave's LDS base + 16 t), K and V both row-major with 256-byte rows, and the
 // V^T operand of the P.V product is read with the transposing ds_read_b64_tr_b16.  No
 // registers hold a tile in flight, and no vector instruction touches it on its way.
@@ -209,7 +209,6 @@ __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" :
 typedef short pf_v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) pf_v4i16 pf_lds_v4i16;
 
-
 // Attend this wave's 32 rows (the lane's query row: column n = lane % 32 of the 32x32
 // products; q of the row in qreg, the B operand of each k-step) to keys [t_begin,
 // t_end) of one (sequence, kv head), online softmax into (oacc, m, l) as the prefill
@@ -218,9 +217,10 @@ typedef __attribute__((address_space(3))) pf_v4i16 pf_lds_v4i16;
 //             that a zero probability then removes)
 //   full_end  every row of the wave sees every key below it
 //   last_key  the lane's row sees keys <= last_key (-1: none)
-// Per tile: the direct loads of the next tile go out first (block ids read one tile
-// ahead), then S^T = K Q^T, the softmax, O^T += V^T P^T, one wait for this wave's
-// loads and one barrier.
+// Per tile: the direct loads go out first (V of the next tile, K of the one after; their
+// block ids were read a tile earlier), then the S^T = K Q^T products of the next tile
+// beside the softmax of this one, O^T += V^T P^T, one wait for this wave's loads and one
+// barrier.
 __device__ __forceinline__ void dma_attend_tiles(PfLdsDma& lds, const int32_t* table,
                                                  const PoolGeom& geom, const char* kb,
                                                  const char* vb, int ctx, int t_begin, int t_end,
@@ -246,7 +246,7 @@ __device__ __forceinline__ void dma_attend_tiles(PfLdsDma& lds, const int32_t* t
     for (int i = 0; i < 4; ++i) kvo[i] = (uint32_t)(16 * (dp ^ ((4 * i + dr) & 15)));
     const uint32_t vvo = (uint32_t)(16 * (dp ^ (4 * dr)));
     const uint32_t drow = (uint32_t)dr * RB;
-    // block ids of a tile's four loads (lane i < 4: load i), read a tile ahead
+    // block ids of a tile's four loads (lane i < 4: load i), read ahead of the loads
     auto tile_ids = [&](int t0) {
         const int tb = min(t0 + 16 * w + 4 * min(lane, 3), ctx - 1);
         return table[(uint32_t)tb >> geom.log2_bs];

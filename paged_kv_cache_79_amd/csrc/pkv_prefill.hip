@@ -15,18 +15,17 @@
 //                     held in registers; the C layout gives each lane one query
 //                     row (column) and 16 keys per 32-key block, so the row-wise
 //                     softmax is lane-local plus one permlane32 swap;
-//   O^T += V^T P^T    A = V^T from LDS (stored transposed, keys in the order in
-//                     which the C registers of S^T hold them), B = bf16 P^T
-//                     straight from those registers.
-// Software pipeline: while the matrix cores work on tile j from LDS, the K/V
-// global loads of tiles j+1 and j+2 are in flight in two register stages (tile
-// j+2's issued at the top of tile j, after the table reads of tile j+3: the
-// in-order load counter then lets each wait cover only what it needs); tile j+1
-// goes into the second LDS buffer after tile j's products, with one barrier per
-// tile.  V is written transposed with a 16-byte XOR swizzle that keeps both the
-// transposing writes and the operand reads free of bank conflicts.  Workgroups are
-// ordered so that all query tiles of one (chunk, kv head) run on the same XCD and
-// share its L2.
+//   O^T += V^T P^T    A = V^T from LDS in the key order in which the C registers
+//                     of S^T hold them, B = bf16 P^T straight from those registers.
+// Head dim 128 (dma_attend_tiles, pkv_attn_tiles.h): K/V tiles go from the pool
+// straight into LDS with direct loads, both row-major with XOR-permuted chunks, and
+// V^T is read with the transposing LDS read; step j loads V of tile j+1 and K of
+// tile j+2 and runs the S^T products of tile j+1 beside the softmax of tile j, with
+// one barrier per tile.  Head dim 64 (attend below): two register stages hold the
+// K/V of tiles j+1 and j+2 while tile j's products run, and V is written transposed
+// with a 16-byte XOR swizzle that keeps the transposing writes and the operand reads
+// free of bank conflicts.  Workgroups are ordered so that all query tiles of one
+// (chunk, kv head) run on the same XCD and share its L2.
 // Keys past the context get -inf scores by selection (whatever stale data their K
 // rows hold) and their V rows repeat the last token's row, so stale or NaN slots
 // never reach the output.
