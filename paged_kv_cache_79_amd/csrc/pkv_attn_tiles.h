@@ -217,16 +217,20 @@ typedef __attribute__((address_space(3))) pf_v4i16 pf_lds_v4i16;
 //             that a zero probability then removes)
 //   full_end  every row of the wave sees every key below it
 //   last_key  the lane's row sees keys <= last_key (-1: none)
+//   load_q    fills qreg (plain loads); called once the first tiles' block ids are on
+//             their way, so that the q rows and those ids travel together (the ids' wait
+//             then does not also wait for the rows, which the first full wait covers)
 // Per tile: the direct loads go out first (V of the next tile, K of the one after; their
 // block ids were read a tile earlier), then the S^T = K Q^T products of the next tile
 // beside the softmax of this one, O^T += V^T P^T, one wait for this wave's loads and one
 // barrier.
+template <class LoadQ>
 __device__ __forceinline__ void dma_attend_tiles(PfLdsDma& lds, const int32_t* table,
                                                  const PoolGeom& geom, const char* kb,
                                                  const char* vb, int ctx, int t_begin, int t_end,
                                                  int full_end, int last_key, float sl2,
-                                                 const u32x4 (&qreg)[8], floatx16_t (&oacc)[4],
-                                                 float& m, float& l) {
+                                                 LoadQ&& load_q, u32x4 (&qreg)[8],
+                                                 floatx16_t (&oacc)[4], float& m, float& l) {
     constexpr int D = 128, RB = 256;
     using P = PrefillShape<D>;
     int tid = threadIdx.x;
@@ -335,13 +339,19 @@ __device__ __forceinline__ void dma_attend_tiles(PfLdsDma& lds, const int32_t* t
     {
         const int ids0 = tile_ids(t_begin);
         if (nt > 1) ids1 = tile_ids(t_begin + kKeyTile);
+        __builtin_amdgcn_sched_barrier(0);
+        load_q(qreg);
+        __builtin_amdgcn_sched_barrier(0);
         issue(t_begin, 0, ids0, KT{});
         issue(t_begin, 0, ids0, VT{});
         if (nt > 1) issue(t_begin + kKeyTile, 1, ids1, KT{});
         if (nt > 2) ids2 = tile_ids(t_begin + 2 * kKeyTile);
     }
     wait_dma();
+    // the ids and q rows are back: the compiler places no wait for them in the loop
     asm volatile("" : "+v"(ids2));
+#pragma unroll
+    for (int ks = 0; ks < P::KSTEPS; ++ks) asm volatile("" : "+v"(qreg[ks]));
     __syncthreads();
     floatx16_t sacc[2];
     qk_plain(0, sacc);

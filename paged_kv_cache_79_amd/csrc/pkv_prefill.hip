@@ -401,18 +401,16 @@ __device__ __forceinline__ void attend_dma(const PrefillArgs& a, const PfChunk& 
     const int last_key = row_valid ? ctx - nq + qpos_local : -1;
 
     u32x4 qreg[P::KSTEPS];
-    {
-        const char* qp = reinterpret_cast<const char*>(a.q) +
-                         (qidx * Hq + (int64_t)h * G + hh) * RB + half * 16;
+    // the tile loop loads the rows beside the first tiles' block ids; a row past the
+    // chunk (or past the packed rows) reads the chunk's last query row, with no branch
+    // (whose waits would also wait for those ids): every key is masked for it
+    const char* qp = reinterpret_cast<const char*>(a.q) +
+                     (((int64_t)q0 + min(qpos_local, nq - 1)) * Hq + (int64_t)h * G + hh) * RB +
+                     half * 16;
+    auto load_q = [&](u32x4 (&qr)[P::KSTEPS]) {
 #pragma unroll
-        for (int ks = 0; ks < P::KSTEPS; ++ks)
-            qreg[ks] = row_valid ? *reinterpret_cast<const u32x4*>(qp + ks * 32)
-                                 : u32x4{0u, 0u, 0u, 0u};
-        // wait for the rows here: a wait the compiler placed inside the tile loop would
-        // also wait for the direct loads in flight there
-#pragma unroll
-        for (int ks = 0; ks < P::KSTEPS; ++ks) asm volatile("" : "+v"(qreg[ks]));
-    }
+        for (int ks = 0; ks < P::KSTEPS; ++ks) qr[ks] = *reinterpret_cast<const u32x4*>(qp + ks * 32);
+    };
     const int full_end = min(ctx - nq + qt * QP + (w * 32) / G + 1, ctx);
 
     floatx16_t oacc[P::DT];
@@ -426,8 +424,8 @@ __device__ __forceinline__ void attend_dma(const PrefillArgs& a, const PfChunk& 
     const int t_begin = k0 * kKeyTile;
     const int t_end = min(k1 * kKeyTile, ctx - nq + min(nq, (qt + 1) * QP));
 
-    dma_attend_tiles(lds, table, a.g, kb, vb, ctx, t_begin, t_end, full_end, last_key, sl2, qreg,
-                     oacc, m, l);
+    dma_attend_tiles(lds, table, a.g, kb, vb, ctx, t_begin, t_end, full_end, last_key, sl2, load_q,
+                     qreg, oacc, m, l);
 
     const float lt = swap32_sum(l);
     if (!row_valid) return;

@@ -65,20 +65,19 @@ __global__ __launch_bounds__(256, 2) void prefix_kernel(PrefixArgs a, int num_ro
     const int64_t seq = (int64_t)first + member;
 
     u32x4 qreg[P::KSTEPS];
-    {
-        const char* qp = reinterpret_cast<const char*>(a.q) +
-                         (seq * Hq + (int64_t)h * G + hh) * P::RB + half * 16;
+    // A row past the group (or past the packed rows) reads the group's last member's row:
+    // its scores stay finite and nothing of it is written, and the loads need no branch
+    // (whose waits would also wait for the block ids loaded beside them).
+    const char* qp = reinterpret_cast<const char*>(a.q) +
+                     (((int64_t)first + min(member, members - 1)) * Hq + (int64_t)h * G + hh) *
+                         P::RB +
+                     half * 16;
+    auto load_q = [&](u32x4 (&qr)[P::KSTEPS]) {
 #pragma unroll
-        for (int ks = 0; ks < P::KSTEPS; ++ks)
-            qreg[ks] = row_valid ? *reinterpret_cast<const u32x4*>(qp + ks * 32)
-                                 : u32x4{0u, 0u, 0u, 0u};
-        if constexpr (D == 128) {
-            // the rows are back before the tile loop, whose direct loads a wait inside it
-            // would also wait for
-#pragma unroll
-            for (int ks = 0; ks < P::KSTEPS; ++ks) asm volatile("" : "+v"(qreg[ks]));
-        }
-    }
+        for (int ks = 0; ks < P::KSTEPS; ++ks) qr[ks] = *reinterpret_cast<const u32x4*>(qp + ks * 32);
+    };
+    // head dim 128: the tile loop loads the rows beside the first tiles' block ids
+    if constexpr (D != 128) load_q(qreg);
 
     floatx16_t oacc[P::DT];
 #pragma unroll
@@ -92,7 +91,55 @@ __global__ __launch_bounds__(256, 2) void prefix_kernel(PrefixArgs a, int num_ro
         // K/V straight into LDS (dma_attend_tiles); every row sees every key of [k0, k1),
         // and rows past k1 in the last tile read key k1 - 1
         __shared__ __attribute__((aligned(16))) PfLdsDma lds;
-        dma_attend_tiles(lds, table, a.g, kb, vb, k1, k0, k1, k1, k1 - 1, sl2, qreg, oacc, m, l);
+        dma_attend_tiles(lds, table, a.g, kb, vb, k1, k0, k1, k1, k1 - 1, sl2, load_q, qreg, oacc,
+                         m, l);
+
+        // The partial state.  o goes through LDS, half a row at a time, so that each store
+        // writes whole rows: lane 16 i' + j then holds floats 4j .. 4j + 3 of one row
+        // (a row's 64 floats at a pitch of 68, which keeps both the writes of the matrix
+        // layout and the row reads on distinct banks).
+        const float lt = swap32_sum(l);
+        if (row_valid && half == 0) {
+            const int64_t prow = (seq * Hq + (int64_t)h * G + hh) * a.state_stride + split;
+            *reinterpret_cast<float2*>(a.pre_ml + prow * 2) = make_float2(m, lt);
+        }
+        constexpr int kPitch = 68;
+        static_assert(4 * 32 * kPitch * 4 <= (int)sizeof(PfLdsDma), "staging fits the tile buffers");
+        __syncthreads();                   // every wave is done with the tile buffers
+        float* stage = reinterpret_cast<float*>(reinterpret_cast<char*>(&lds) + w * 32 * kPitch * 4);
+        const int j4 = 4 * (lane & 15);
+#pragma unroll
+        for (int ph = 0; ph < 2; ++ph) {
+            // lane (n, half) holds d = 32 dt + 8 g4 + 4 half + e (e < 4) of row n
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const floatx16_t& acc = oacc[2 * ph + u];
+                    *reinterpret_cast<float4*>(stage + n * kPitch + 32 * u + 8 * g4 + 4 * half) =
+                        make_float4(acc[4 * g4 + 0], acc[4 * g4 + 1], acc[4 * g4 + 2],
+                                    acc[4 * g4 + 3]);
+                }
+            float4 v8[8];                  // all reads first, then the stores
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                v8[i] = *reinterpret_cast<const float4*>(stage + (4 * i + (lane >> 4)) * kPitch + j4);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int rr = 4 * i + (lane >> 4);              // row of the wave
+                const float4 v = v8[i];
+                const int r2 = w * 32 + rr;
+                const int mi2 = r2 / G;
+                const int member2 = rb * QP + mi2;
+                if (r2 < QP * G && member2 < members) {
+                    const int64_t prow2 =
+                        (((int64_t)first + member2) * Hq + (int64_t)h * G + (r2 - mi2 * G)) *
+                            a.state_stride + split;
+                    *reinterpret_cast<float4*>(a.pre_o + prow2 * D + 64 * ph + j4) = v;
+                }
+            }
+        }
+        return;
     } else {
     __shared__ __attribute__((aligned(16))) char lds_k[2][kKeyTile * P::KPITCH];
     __shared__ __attribute__((aligned(16))) char lds_vt[2][D * P::VPITCH];
