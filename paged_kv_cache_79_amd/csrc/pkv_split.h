@@ -37,14 +37,17 @@ __device__ __forceinline__ int wave_sum_int(int x) {
 }
 
 // First token of sequence s that the decode attends: in the shared-prefix mode the
-// tokens before it (whole blocks) were attended by the prefix pass.
+// tokens before it (whole blocks) were attended by the prefix pass.  seq_start_of takes
+// the sequence's prefix length as loaded.
+__device__ __forceinline__ int seq_start_of(const DecodeArgs& a, int prefix_len, int ctx) {
+    return min(max(prefix_len, 0) & ~(a.g.block_size - 1), ctx);
+}
 template <bool PREFIX>
 __device__ __forceinline__ int seq_start(const DecodeArgs& a, int s, int ctx) {
     if constexpr (!PREFIX) {
         return 0;
     } else {
-        const int p = max(a.seq_prefix[s], 0) & ~(a.g.block_size - 1);
-        return min(p, ctx);
+        return seq_start_of(a, a.seq_prefix[s], ctx);
     }
 }
 // Tiles of sequence s (per kv head).
@@ -55,9 +58,11 @@ __device__ __forceinline__ int unit_tiles(const DecodeArgs& a, int s) {
 }
 
 // Tiles of the whole batch (all sequences, one kv head) and tiles before sequence `upto`.
-// Four chunks of 64 sequences per pass, their loads issued together; the tile counts
-// and clamped lengths of the first 256 sequences stay in first[q] and first_ctx[q]
-// (sequence 64q + lane) for locate_unit and the wave's first unit.
+// Four chunks of 64 sequences per pass, their loads issued together (a lane past the
+// batch reads the last sequence and discards it: loads under a branch would each wait
+// for their value in turn); the tile counts and clamped lengths of the first 256
+// sequences stay in first[q] and first_ctx[q] (sequence 64q + lane) for locate_unit and
+// the wave's first unit.
 template <bool PREFIX = false>
 __device__ __forceinline__ void count_tiles(const DecodeArgs& a, int upto, int64_t& total,
                                             int64_t& before, int (&first)[4],
@@ -66,12 +71,18 @@ __device__ __forceinline__ void count_tiles(const DecodeArgs& a, int upto, int64
     total = 0;
     before = 0;
     for (int c0 = 0; c0 < a.num_seqs; c0 += 256) {
-        int nt[4], cl[4];
+        int nt[4], cl[4], craw[4], praw[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int sl = c0 + q * 64 + lane;
-            cl[q] = sl < a.num_seqs ? clamp_ctx(a, a.context_lens[sl]) : 0;
-            nt[q] = sl < a.num_seqs ? ntiles_of(cl[q] - seq_start<PREFIX>(a, sl, cl[q])) : 0;
+            const int sl = min(c0 + q * 64 + lane, a.num_seqs - 1);
+            craw[q] = a.context_lens[sl];
+            praw[q] = PREFIX ? a.seq_prefix[sl] : 0;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const bool in = c0 + q * 64 + lane < a.num_seqs;
+            cl[q] = in ? clamp_ctx(a, craw[q]) : 0;
+            nt[q] = in ? ntiles_of(cl[q] - (PREFIX ? seq_start_of(a, praw[q], cl[q]) : 0)) : 0;
         }
         if (c0 == 0) {
 #pragma unroll
@@ -221,7 +232,8 @@ __device__ __forceinline__ void locate_unit(const DecodeArgs& a, int64_t b, int 
             const int q = c0 >> 6;                 // uniform
             nt = q == 0 ? first[0] : q == 1 ? first[1] : q == 2 ? first[2] : first[3];
         } else {
-            nt = sl < a.num_seqs ? unit_tiles<PREFIX>(a, sl) : 0;
+            const int t = unit_tiles<PREFIX>(a, min(sl, a.num_seqs - 1));
+            nt = sl < a.num_seqs ? t : 0;
         }
         int incl = nt;
 #pragma unroll
