@@ -575,8 +575,8 @@ def gpu_leg(prep, args, ceiling):
         "kv_bytes_per_step": byts,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(b.name) if pt == 0 and not contig
-                                and args.block_size == 16 and shared is None else None,
+                     "traffic": (recorded_traffic(("shared_prefix_" if shared else "") + b.name)
+                                 if pt == 0 and not contig and args.block_size == 16 else None),
                      "kernel": ("contiguous_attention_decode" if contig else
                                 "paged_attention_decode_shared_prefix (prefix pass + "
                                 "attention kernel + merge kernel)" if shared else
