@@ -602,9 +602,11 @@ __global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(PrefillArg
     const int qt = item % num_q_tiles;
     const int h = (item / num_q_tiles) % Hkv;
     const int c = item / (num_q_tiles * Hkv);
+    // the descriptor slot exists for every item of the grid (item < num_wgs), so it is
+    // read beside the chunk's bounds and discarded when the item has no work
+    const int2 desc = *reinterpret_cast<const int2*>(a.item_desc + 2 * item);
     const PfChunk k = pf_chunk<QP>(a, c, num_q_tiles);
     if (qt >= k.nqt) return;                   // no work item, no descriptor
-    const int2 desc = *reinterpret_cast<const int2*>(a.item_desc + 2 * item);
     const int w0 = __builtin_amdgcn_readfirstlane(desc.x);
     int np = __builtin_amdgcn_readfirstlane(desc.y);
     if (np <= 0) return;                       // finished in place
