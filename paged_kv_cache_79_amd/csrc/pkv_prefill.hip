@@ -397,7 +397,6 @@ __device__ __forceinline__ void attend_dma(const PrefillArgs& a, const PfChunk& 
     const int hh = r - qi * G;
     const int qpos_local = qt * QP + qi;
     const bool row_valid = (r < QP * G) && (qpos_local < nq);
-    const int64_t qidx = (int64_t)q0 + qpos_local;
     const int last_key = row_valid ? ctx - nq + qpos_local : -1;
 
     u32x4 qreg[P::KSTEPS];
@@ -428,26 +427,45 @@ __device__ __forceinline__ void attend_dma(const PrefillArgs& a, const PfChunk& 
                      qreg, oacc, m, l);
 
     const float lt = swap32_sum(l);
-    if (!row_valid) return;
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    uint16_t* orow;
-    if (slot >= 0) {
-        orow = a.part_o + (slot * kRowsPerWg + r) * D;
-        if (half == 0)
-            *reinterpret_cast<float2*>(a.part_ml + (slot * kRowsPerWg + r) * 2) = make_float2(m, lt);
-    } else {
-        orow = reinterpret_cast<uint16_t*>(a.out) + (qidx * Hq + (int64_t)h * G + hh) * D;
-    }
+    if (slot >= 0 && row_valid && half == 0)
+        *reinterpret_cast<float2*>(a.part_ml + (slot * kRowsPerWg + r) * 2) = make_float2(m, lt);
+    // The rows leave through LDS (the tile loop ends with a barrier after its last reads,
+    // so the buffers are free): lane (n, half) puts its bf16 elements of row n into a
+    // staged copy of the wave's 32 rows, then each store writes 256 contiguous bytes of
+    // one row (lane 16 i' + j: bytes 16 j .. 16 j + 15 of row 4 i + i'), instead of 16
+    // bytes of each of 32 rows.
+    constexpr int kPitch = 272;                // bytes per staged row: 256 + 16
+    static_assert(4 * 32 * kPitch <= (int)sizeof(PfLdsDma), "staging fits the tile buffers");
+    char* stage = reinterpret_cast<char*>(&lds) + w * 32 * kPitch;
 #pragma unroll
     for (int dt = 0; dt < P::DT; ++dt)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-            const int d = dt * 32 + 8 * g4 + 4 * half;
             uint2 wv;
             wv.x = pack_bf16(oacc[dt][4 * g4 + 0] * inv, oacc[dt][4 * g4 + 1] * inv);
             wv.y = pack_bf16(oacc[dt][4 * g4 + 2] * inv, oacc[dt][4 * g4 + 3] * inv);
-            *reinterpret_cast<uint2*>(orow + d) = wv;
+            *reinterpret_cast<uint2*>(stage + n * kPitch + 64 * dt + 16 * g4 + 8 * half) = wv;
         }
+    const int j16 = lane & 15;
+    u32x4 rowv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        rowv[i] = *reinterpret_cast<const u32x4*>(stage + (4 * i + (lane >> 4)) * kPitch + 16 * j16);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r2 = w * 32 + 4 * i + (lane >> 4);
+        const int qi2 = r2 / G;
+        const int hh2 = r2 - qi2 * G;
+        if (r2 < QP * G && qt * QP + qi2 < nq) {
+            uint16_t* dst = slot >= 0
+                                ? a.part_o + (slot * kRowsPerWg + r2) * D
+                                : reinterpret_cast<uint16_t*>(a.out) +
+                                      (((int64_t)q0 + qt * QP + qi2) * Hq + (int64_t)h * G + hh2) * D;
+            *reinterpret_cast<u32x4*>(dst + 8 * j16) = rowv[i];
+        }
+    }
+    __syncthreads();                           // the next piece's loads reuse the buffers
 }
 
 // The workgroup's LDS and its tile loop for head dimension D.
