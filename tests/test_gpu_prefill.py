@@ -67,7 +67,7 @@ def check_small(chunk_lens, contexts, hq, hkv, d=128, bs=16, seed=0, rows=None):
     assert err <= TOL["bf16"], f"row-normalised error {err:.3e}"
 
 
-@pytest.mark.parametrize("g", [1, 2, 4, 7, 8])
+@pytest.mark.parametrize("g", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_groups(g):
     check_small([37, 64], [100, 64], 2 * g, 2, seed=g)
 
