@@ -72,6 +72,21 @@ def test_groups(g):
     check_small([37, 64], [100, 64], 2 * g, 2, seed=g)
 
 
+def test_empty_chunks_between_others():
+    """Chunks with no queries (their contexts still in the table) between chunks with
+    queries, through the call with a workspace (key split when the plan asks for it)
+    and without one."""
+    pre, kp, vp, nb = W.prefill_only(seed=31, chunk_lens=[37, 0, 200, 0, 5],
+                                     contexts=[100, 50, 2600, 300, 900], num_q_heads=8,
+                                     num_kv_heads=2, head_dim=128, block_size=16)
+    print(f"prefill empty chunks, split planned: {expect_split(pre)}", flush=True)
+    want = O.prefill_chunk(pre.q, pre.cu_q_lens, kp, vp, pre.block_tables, pre.context_lens,
+                           pre.scale, "bf16", 2)
+    for split in (True, False):
+        got = run_prefill(pre, dev(kp), dev(vp), split=split)
+        assert rownorm_err(got, want) <= TOL["bf16"], f"split={split}"
+
+
 def test_whole_prompt_and_single_query():
     check_small([1, 130, 5], [1, 130, 300], 8, 2, seed=3)      # n_q == ctx and n_q == 1
 
